@@ -1,0 +1,458 @@
+// Decode attention over the materialised view: split-K flash decode.
+//
+// KVMem runs the model's attention over the bounded view instead of the whole
+// workspace (reproduction README, 'Local reproduction': attention replacement).
+// Query token t of a step sits at view position V + t, is q-RMS-normalised and
+// rotated there, and attends to every view slot.
+//
+// bf16 path (k_attend_bf16): one workgroup of 4 wavefronts per (session, KV
+// head, split of the view).  Each wavefront streams its own run of 32-token
+// blocks straight from HBM into matrix-core operand registers and keeps an
+// online softmax; the 4 wavefronts are merged by log-sum-exp in LDS, the splits
+// by k_attend_combine.  All T*G query rows of a KV head share every K/V element
+// (GQA), so both products are matrix-core contractions with the rows as N:
+//   S^T = K * Q^T   (v_mfma_f32_16x16x32_bf16, A = 16 tokens x 32 dims),
+//   O^T = V^T * P^T (A = 16 dims x 32 tokens from the dimension-major V view).
+// The S^T accumulator layout (lane = query row, 4 tokens per lane per tile) is
+// exactly the P^T operand layout of the second product once the view stores
+// each block's tokens in slot order sigma(u), so no shuffle or LDS transpose is
+// needed between the two products, and every value a lane rescales (row max,
+// row sum, O^T) belongs to that lane's own query row.  The fp32 query and the
+// fp32 probabilities enter the bf16 products as a hi + lo pair of bf16 values
+// (two products into one accumulator), which keeps them to ~2^-16 relative; the
+// bf16 view data are exact operands.  Scores are kept in log2 units.
+//
+// fp32 path (k_attend_f32): a plain vector-ALU kernel with the same split and
+// merge structure (logits and probabilities staged in LDS).
+#include "kvmem_internal.h"
+
+namespace kvmem {
+
+namespace {
+
+constexpr float kLog2eRsqrtD = 0.12751743074480953f;   // log2(e) / sqrt(128)
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+__device__ __forceinline__ void split_hi_lo(float y, uint32_t &hi, uint32_t &lo) {
+  hi = f32_to_bf16(y);
+  lo = f32_to_bf16(y - __uint_as_float(hi << 16));
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void k_attend_bf16(const uint16_t *__restrict__ q, const float *__restrict__ qw,
+                                                     float eps, const uint16_t *__restrict__ kview,
+                                                     const uint16_t *__restrict__ vview, float *__restrict__ part_o,
+                                                     float2 *__restrict__ part_ml, float *__restrict__ out,
+                                                     SessI32 view_tok, int s0, AttendGeom g, double theta) {
+  constexpr int RP = 16 * NT;
+  constexpr int kPitch = kD + 4;
+  __shared__ double inv_freq[kD / 2];
+  __shared__ float sm[4][RP];
+  __shared__ float sls[4][RP];
+  __shared__ float so[4][RP * kPitch];
+
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int split = blockIdx.x;
+  const int V = view_tok.v[sl];
+  const int split_tok = 4 * g.tpw;
+  const int start = split * split_tok;
+  if (start >= V) return;
+  const int n_splits = (V + split_tok - 1) / split_tok;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qq = lane >> 4;
+  const int col = lane & 15;
+  if (tid < kD / 2) inv_freq[tid] = rope_inv_freq(tid, theta);
+  __syncthreads();
+
+  // ---- queries: RMSNorm, RoPE at V + t, log2(e)/sqrt(d), hi/lo bf16 split ----
+  bf16x8 qhi[NT][4], qlo[NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = nt * 16 + col;
+    const bool valid = r < g.rows;
+    const int t = valid ? r / g.G : 0;
+    const int gg = valid ? r % g.G : 0;
+    float x[32];
+    if (valid) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + 32 * qq);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 w = src[c];
+        const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[8 * c + 2 * k] = bf16_lo(e[k]);
+          x[8 * c + 2 * k + 1] = bf16_hi(e[k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) ss += x[e] * x[e];
+    ss += shfl_xor_f(ss, 16);
+    ss += shfl_xor_f(ss, 32);
+    const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = x[e] * rs * qw[32 * qq + e];
+    float px[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) px[e] = shfl_xor_f(x[e], 32);   // RoPE partner: dim +- 64
+    const double pos = (double)(V + t);
+    uint32_t hw[16], lw[16];
+#pragma unroll
+    for (int e = 0; e < 32; e += 2) {
+      uint32_t h2[2], l2[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float c, sn;
+        rope_cos_sin(pos, inv_freq[(32 * qq + e + k) & 63], c, sn);
+        const float y = (qq < 2 ? (x[e + k] * c - px[e + k] * sn) : (x[e + k] * c + px[e + k] * sn)) * kLog2eRsqrtD;
+        split_hi_lo(valid ? y : 0.f, h2[k], l2[k]);
+      }
+      hw[e / 2] = h2[0] | (h2[1] << 16);
+      lw[e / 2] = l2[0] | (l2[1] << 16);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qhi[nt][c] = as_bf16x8(make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]));
+      qlo[nt][c] = as_bf16x8(make_uint4(lw[4 * c], lw[4 * c + 1], lw[4 * c + 2], lw[4 * c + 3]));
+    }
+  }
+
+  // ---- stream this wavefront's blocks ----
+  floatx4 o[NT][8];
+  float mrun[NT], lrun[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    mrun[nt] = -INFINITY;
+    lrun[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const size_t head = (size_t)s * g.Hkv + h;
+  const uint16_t *kbase = kview + head * (size_t)g.max_view * kD;
+  const uint16_t *vbase = vview + head * (size_t)g.max_view * kD;
+  const int tok0 = start + wave * g.tpw;
+  const int tok1 = min(V, tok0 + g.tpw);
+  for (int tb = tok0; tb < tok1; tb += kBT) {
+    uint4 kr[2][4], vr[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        kr[tt][c] = *reinterpret_cast<const uint4 *>(kbase + (size_t)(tb + 16 * tt + col) * kD + 32 * qq + 8 * c);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      vr[dt] = *reinterpret_cast<const uint4 *>(vbase + ((size_t)(tb >> 5) * kD + 16 * dt + col) * kBT + 8 * qq);
+
+    floatx4 sc[2][NT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[tt][c]), qhi[nt][c], a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[tt][c]), qlo[nt][c], a, 0, 0, 0);
+        }
+        sc[tt][nt] = a;
+      }
+    if (tb + kBT > V) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tb + 16 * tt + 4 * qq + i >= V)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) sc[tt][nt][i] = -INFINITY;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float bm = fmaxf(fmaxf(fmaxf(sc[0][nt][0], sc[0][nt][1]), fmaxf(sc[0][nt][2], sc[0][nt][3])),
+                       fmaxf(fmaxf(sc[1][nt][0], sc[1][nt][1]), fmaxf(sc[1][nt][2], sc[1][nt][3])));
+      bm = fmaxf(bm, shfl_xor_f(bm, 16));
+      bm = fmaxf(bm, shfl_xor_f(bm, 32));
+      const float mn = fmaxf(mrun[nt], bm);
+      const float alpha = exp2f(mrun[nt] - mn);
+      mrun[nt] = mn;
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = exp2f(sc[0][nt][i] - mn);
+        p[4 + i] = exp2f(sc[1][nt][i] - mn);
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) psum += p[i];
+      lrun[nt] = lrun[nt] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t h0, l0, h1, l1;
+        split_hi_lo(p[2 * k], h0, l0);
+        split_hi_lo(p[2 * k + 1], h1, l1);
+        ph[k] = h0 | (h1 << 16);
+        pl[k] = l0 | (l1 << 16);
+      }
+      const bf16x8 phi = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      const bf16x8 plo = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), phi, o[nt][dt], 0, 0, 0);
+        o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), plo, o[nt][dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- merge the 4 wavefronts (log-sum-exp) ----
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    lrun[nt] += shfl_xor_f(lrun[nt], 16);
+    lrun[nt] += shfl_xor_f(lrun[nt], 32);
+    const int row = nt * 16 + col;
+    if (qq == 0) {
+      sm[wave][row] = mrun[nt];
+      sls[wave][row] = lrun[nt];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) so[wave][row * kPitch + 16 * dt + 4 * qq + i] = o[nt][dt][i];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < g.rows * kD; idx += 256) {
+    const int row = idx >> 7;
+    const int dim = idx & (kD - 1);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][row]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm[w][row];
+      if (mw != -INFINITY) {
+        const float f = exp2f(mw - M);
+        num += f * so[w][row * kPitch + dim];
+        den += f * sls[w][row];
+      }
+    }
+    if (n_splits == 1) {
+      const int t = row / g.G, gg = row % g.G;
+      out[(((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + dim] = num / den;
+    } else {
+      const size_t pidx = (head * g.max_splits + split) * g.rows + row;
+      part_o[pidx * kD + dim] = num;
+      if (dim == 0) part_ml[pidx] = make_float2(M, den);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path
+// ---------------------------------------------------------------------------
+constexpr int kF32MaxRows = 64;
+constexpr int kF32Tile = 64;
+
+__global__ __launch_bounds__(256) void k_attend_f32(const float *__restrict__ q, const float *__restrict__ qw, float eps,
+                                                    const float *__restrict__ kview, const float *__restrict__ vview,
+                                                    float *__restrict__ part_o, float2 *__restrict__ part_ml,
+                                                    float *__restrict__ out, SessI32 view_tok, int s0, AttendGeom g,
+                                                    double theta) {
+  __shared__ double inv_freq[kD / 2];
+  __shared__ float qs[kF32MaxRows][kD + 1];
+  __shared__ float lg[kF32MaxRows][kF32Tile + 1];
+  __shared__ float srs[kF32MaxRows], smx[kF32MaxRows], slsum[kF32MaxRows], salpha[kF32MaxRows];
+
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int split = blockIdx.x;
+  const int V = view_tok.v[sl];
+  const int split_tok = 4 * g.tpw;
+  const int start = split * split_tok;
+  if (start >= V) return;
+  const int end = min(V, start + split_tok);
+  const int n_splits = (V + split_tok - 1) / split_tok;
+  const int tid = threadIdx.x;
+  const int R = g.rows;
+  if (tid < kD / 2) inv_freq[tid] = rope_inv_freq(tid, theta);
+  if (tid < R) {
+    const int t = tid / g.G, gg = tid % g.G;
+    const float *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
+    float ss = 0.f;
+    for (int e = 0; e < kD; ++e) ss += src[e] * src[e];
+    srs[tid] = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+    smx[tid] = -INFINITY;
+    slsum[tid] = 0.f;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < R * kD; idx += 256) {
+    const int r = idx >> 7, dim = idx & (kD - 1);
+    const int t = r / g.G, gg = r % g.G;
+    const float *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
+    const int i = dim & 63;
+    const int pd = dim < 64 ? dim + 64 : dim - 64;
+    const float x = src[dim] * srs[r] * qw[dim];
+    const float px = src[pd] * srs[r] * qw[pd];
+    float c, sn;
+    rope_cos_sin((double)(V + t), inv_freq[i], c, sn);
+    qs[r][dim] = (dim < 64 ? x * c - px * sn : x * c + px * sn) * kLog2eRsqrtD;
+  }
+  __syncthreads();
+
+  const size_t head = (size_t)s * g.Hkv + h;
+  const float *kbase = kview + head * (size_t)g.max_view * kD;
+  const float *vbase = vview + head * (size_t)g.max_view * kD;
+  const int dim = tid & (kD - 1);
+  const int rh = tid >> 7;                       // rows rh, rh + 2, ...
+  float acc[kF32MaxRows / 2];
+#pragma unroll
+  for (int k = 0; k < kF32MaxRows / 2; ++k) acc[k] = 0.f;
+
+  for (int tb = start; tb < end; tb += kF32Tile) {
+    const int jt = tid & (kF32Tile - 1);
+    const int tok = tb + jt;
+    for (int r = tid >> 6; r < R; r += 4) {
+      float a = -INFINITY;
+      if (tok < end) {
+        const float *kr = kbase + (size_t)tok * kD;
+        a = 0.f;
+        for (int e = 0; e < kD; ++e) a = fmaf(qs[r][e], kr[e], a);
+      }
+      lg[r][jt] = a;
+    }
+    __syncthreads();
+    if (tid < R) {
+      float bm = -INFINITY;
+      for (int j = 0; j < kF32Tile; ++j) bm = fmaxf(bm, lg[tid][j]);
+      const float mn = fmaxf(smx[tid], bm);
+      const float alpha = exp2f(smx[tid] - mn);
+      float ps = 0.f;
+      for (int j = 0; j < kF32Tile; ++j) {
+        const float p = exp2f(lg[tid][j] - mn);
+        lg[tid][j] = p;
+        ps += p;
+      }
+      slsum[tid] = slsum[tid] * alpha + ps;
+      smx[tid] = mn;
+      salpha[tid] = alpha;
+    }
+    __syncthreads();
+    const int nt = min(kF32Tile, end - tb);
+    for (int k = 0; k < kF32MaxRows / 2; ++k) {
+      const int r = rh + 2 * k;
+      if (r >= R) break;
+      float a = acc[k] * salpha[r];
+      for (int j = 0; j < nt; ++j) {
+        const int tk = tb + j;
+        a = fmaf(lg[r][j], vbase[((size_t)(tk >> 5) * kD + dim) * kBT + v_slot(tk & 31)], a);
+      }
+      acc[k] = a;
+    }
+    __syncthreads();
+  }
+  for (int k = 0; k < kF32MaxRows / 2; ++k) {
+    const int r = rh + 2 * k;
+    if (r >= R) break;
+    if (n_splits == 1) {
+      const int t = r / g.G, gg = r % g.G;
+      out[(((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + dim] = acc[k] / slsum[r];
+    } else {
+      const size_t pidx = (head * g.max_splits + split) * g.rows + r;
+      part_o[pidx * kD + dim] = acc[k];
+      if (dim == 0) part_ml[pidx] = make_float2(smx[r], slsum[r]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of the splits (fixed order -> deterministic)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kD) void k_attend_combine(const float *__restrict__ part_o,
+                                                       const float2 *__restrict__ part_ml, float *__restrict__ out,
+                                                       SessI32 view_tok, int s0, AttendGeom g) {
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int row = blockIdx.x;
+  const int dim = threadIdx.x;
+  const int V = view_tok.v[sl];
+  const int split_tok = 4 * g.tpw;
+  const int n = (V + split_tok - 1) / split_tok;
+  if (n == 1) return;                     // written by the attention kernel itself
+  const int t = row / g.G, gg = row % g.G;
+  float *dst = out + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + dim;
+  if (n == 0) {
+    *dst = 0.f;
+    return;
+  }
+  const size_t head = (size_t)s * g.Hkv + h;
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, part_ml[(head * g.max_splits + i) * g.rows + row].x);
+  float num = 0.f, den = 0.f;
+  for (int i = 0; i < n; ++i) {
+    const size_t pidx = (head * g.max_splits + i) * g.rows + row;
+    const float2 ml = part_ml[pidx];
+    const float f = exp2f(ml.x - M);
+    num += f * part_o[pidx * kD + dim];
+    den += f * ml.y;
+  }
+  *dst = num / den;
+}
+
+}  // namespace
+
+int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view) {
+  // Aim for >= 2048 workgroups (8 per CU) at the largest view; 32..512 tokens
+  // per wavefront.
+  const long work = (long)max_view * n_sessions * Hkv;
+  long tpw_blocks = (work + 2048L * 4 * kBT - 1) / (2048L * 4 * kBT);
+  if (tpw_blocks < 1) tpw_blocks = 1;
+  if (tpw_blocks > 16) tpw_blocks = 16;
+  return (int)tpw_blocks * kBT;
+}
+
+int attend_max_splits(int max_view, int tpw) { return (max_view + 4 * tpw - 1) / (4 * tpw); }
+
+hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
+                         const void *v_view, float *part_o, float2 *part_ml, float *out,
+                         const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
+                         hipStream_t st) {
+  int max_v = 0;
+  for (int i = 0; i < n_sess; ++i) max_v = view_tok.v[i] > max_v ? view_tok.v[i] : max_v;
+  const int splits = max_v > 0 ? (max_v + 4 * g.tpw - 1) / (4 * g.tpw) : 0;
+  if (splits > 0) {
+    dim3 grid((unsigned)splits, (unsigned)g.Hkv, (unsigned)n_sess);
+    if (!bf16) {
+      hipLaunchKernelGGL(k_attend_f32, grid, dim3(256), 0, st, (const float *)q, qw, eps, (const float *)k_view,
+                         (const float *)v_view, part_o, part_ml, out, view_tok, s0, g, theta);
+    } else if (g.rows <= 16) {
+      hipLaunchKernelGGL(k_attend_bf16<1>, grid, dim3(256), 0, st, (const uint16_t *)q, qw, eps,
+                         (const uint16_t *)k_view, (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g,
+                         theta);
+    } else {
+      hipLaunchKernelGGL(k_attend_bf16<2>, grid, dim3(256), 0, st, (const uint16_t *)q, qw, eps,
+                         (const uint16_t *)k_view, (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g,
+                         theta);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 cgrid((unsigned)g.rows, (unsigned)g.Hkv, (unsigned)n_sess);
+  hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(kD), 0, st, part_o, part_ml, out, view_tok, s0, g);
+  return hipGetLastError();
+}
+
+}  // namespace kvmem

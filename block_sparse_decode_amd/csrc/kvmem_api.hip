@@ -1,0 +1,267 @@
+// Host side of the C ABI declared in include/kvmem.h: argument validation,
+// scratch layout, launch geometry and the per-session launch loop.  No call
+// allocates, synchronises or keeps state; every invalid argument is rejected
+// before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/kvmem.h"
+#include "kvmem_internal.h"
+
+using namespace kvmem;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+kvmem_status check_geom(const kvmem_geom *g) {
+  if (!g) return KVMEM_E_ARG;
+  if (g->n_q_heads <= 0 || g->n_kv_heads <= 0 || g->n_q_heads % g->n_kv_heads != 0) return KVMEM_E_ARG;
+  if (g->head_dim != kD || g->block_tokens != kBT) return KVMEM_E_UNSUPPORTED;
+  if (g->kv_dtype != KVMEM_F32 && g->kv_dtype != KVMEM_BF16) return KVMEM_E_UNSUPPORTED;
+  return KVMEM_OK;
+}
+
+kvmem_status check_ws(const kvmem_workspace *w, bool need_v) {
+  if (!w) return KVMEM_E_ARG;
+  if (w->n_sessions <= 0 || w->max_blocks <= 0 || w->n_pages <= 0) return KVMEM_E_ARG;
+  if (!w->k_pool || !w->block_table || !w->n_tokens_host) return KVMEM_E_ARG;
+  if (need_v && !w->v_pool) return KVMEM_E_ARG;
+  const long cap = (long)w->max_blocks * kBT;
+  for (int s = 0; s < w->n_sessions; ++s)
+    if (w->n_tokens_host[s] < 0 || (long)w->n_tokens_host[s] > cap) return KVMEM_E_ARG;
+  return KVMEM_OK;
+}
+
+kvmem_status hip_status(hipError_t e) { return e == hipSuccess ? KVMEM_OK : KVMEM_E_HIP; }
+
+struct Split {
+  int n_cand, r_start, n_all, n_full;
+};
+Split recent_split(int n_tok, int n_recent) {
+  Split r;
+  r.n_full = n_tok / kBT;
+  r.n_all = (n_tok + kBT - 1) / kBT;
+  r.r_start = r.n_all - n_recent > 0 ? r.n_all - n_recent : 0;
+  r.n_cand = r.n_full < r.r_start ? r.n_full : r.r_start;
+  return r;
+}
+
+// score_select scratch: per-head scores, per-(row, chunk) softmax statistics, A.
+struct ScoreScratch {
+  size_t scores, part, agg, total;
+};
+ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
+  ScoreScratch r;
+  const size_t rows = (size_t)S * T * g->n_q_heads;
+  const size_t n_chunks = ((size_t)max_blocks + kScoreChunk - 1) / kScoreChunk;
+  r.scores = 0;
+  r.part = align_up(rows * max_blocks * sizeof(float));
+  r.agg = r.part + align_up(rows * n_chunks * sizeof(float2));
+  r.total = r.agg + align_up((size_t)S * g->n_kv_heads * max_blocks * sizeof(float));
+  return r;
+}
+
+struct AttendScratch {
+  size_t part_o, part_ml, total;
+  int tpw, max_splits;
+};
+AttendScratch attend_scratch(const kvmem_geom *g, int S, int T, int max_view) {
+  AttendScratch r;
+  r.tpw = attend_tokens_per_wave(S, g->n_kv_heads, max_view);
+  r.max_splits = attend_max_splits(max_view, r.tpw);
+  const size_t rows = (size_t)T * (g->n_q_heads / g->n_kv_heads);
+  const size_t n = (size_t)S * g->n_kv_heads * r.max_splits * rows;
+  r.part_o = 0;
+  r.part_ml = align_up(n * kD * sizeof(float));
+  r.total = r.part_ml + align_up(n * sizeof(float2));
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvmem_status_string(kvmem_status st) {
+  switch (st) {
+    case KVMEM_OK: return "ok";
+    case KVMEM_E_ARG: return "invalid argument";
+    case KVMEM_E_UNSUPPORTED: return "unsupported geometry or dtype";
+    case KVMEM_E_WORKSPACE: return "scratch buffer too small";
+    case KVMEM_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t kvmem_version(void) { return 100; }
+
+kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws, void *index, void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if ((st = check_ws(ws, false)) != KVMEM_OK) return st;
+  if (!index) return KVMEM_E_ARG;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  for (int s0 = 0; s0 < ws->n_sessions; s0 += kMaxSess) {
+    const int n = ws->n_sessions - s0 < kMaxSess ? ws->n_sessions - s0 : kMaxSess;
+    SessI32 nb;
+    memset(&nb, 0, sizeof(nb));
+    for (int i = 0; i < n; ++i) nb.v[i] = ws->n_tokens_host[s0 + i] / kBT;
+    st = hip_status(launch_build_index(bf16, ws->k_pool, ws->block_table, index, ws->dev_error, nb, s0, n,
+                                       geom->n_kv_heads, ws->max_blocks, ws->n_pages, (hipStream_t)stream));
+    if (st != KVMEM_OK) return st;
+  }
+  return KVMEM_OK;
+}
+
+size_t kvmem_score_select_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t max_blocks, int32_t T) {
+  if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || max_blocks <= 0 || T <= 0) return 0;
+  return score_scratch(geom, n_sessions, max_blocks, T).total;
+}
+
+kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *ws, const void *index,
+                                const void *q, int32_t T, const float *q_norm_w, float eps, int32_t k_select,
+                                int32_t n_recent, int32_t *view_blocks, int32_t *view_tokens_host,
+                                float *scores_opt, float *agg_opt, void *scratch, size_t scratch_bytes,
+                                void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if ((st = check_ws(ws, false)) != KVMEM_OK) return st;
+  if (!index || !q || !q_norm_w || !view_tokens_host || T <= 0 || k_select < 0 || n_recent < 0) return KVMEM_E_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return KVMEM_E_ARG;
+  const long n_list_l = (long)k_select + n_recent;
+  if (n_list_l > (1L << 30)) return KVMEM_E_ARG;
+  const int n_list = (int)n_list_l;
+  if (n_list > 0 && !view_blocks) return KVMEM_E_ARG;
+  const int S = ws->n_sessions;
+  const ScoreScratch sc = score_scratch(geom, S, ws->max_blocks, T);
+  if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
+
+  for (int s = 0; s < S; ++s) {
+    const Split sp = recent_split(ws->n_tokens_host[s], n_recent);
+    const int k_eff = k_select < sp.n_cand ? k_select : sp.n_cand;
+    const long tail = (long)ws->n_tokens_host[s] - (long)kBT * sp.r_start;
+    view_tokens_host[s] = kBT * k_eff + (int)(tail > 0 ? tail : 0);
+  }
+
+  char *base = (char *)scratch;
+  float *scores = scores_opt ? scores_opt : (float *)(base + sc.scores);
+  float2 *part = (float2 *)(base + sc.part);
+  float *A = agg_opt ? agg_opt : (float *)(base + sc.agg);
+  ScoreGeom g;
+  g.Tq = T;
+  g.Hq = geom->n_q_heads;
+  g.Hkv = geom->n_kv_heads;
+  g.G = g.Hq / g.Hkv;
+  g.max_blocks = ws->max_blocks;
+  g.n_chunks = (ws->max_blocks + kScoreChunk - 1) / kScoreChunk;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  const hipStream_t hs = (hipStream_t)stream;
+
+  for (int s0 = 0; s0 < S; s0 += kMaxSess) {
+    const int n = S - s0 < kMaxSess ? S - s0 : kMaxSess;
+    SessI32 nb;
+    TopkMeta tm;
+    memset(&nb, 0, sizeof(nb));
+    memset(&tm, 0, sizeof(tm));
+    for (int i = 0; i < n; ++i) {
+      const Split sp = recent_split(ws->n_tokens_host[s0 + i], n_recent);
+      nb.v[i] = sp.n_full;
+      tm.n_cand.v[i] = sp.n_cand;
+      tm.k_eff.v[i] = k_select < sp.n_cand ? k_select : sp.n_cand;
+      tm.r_start.v[i] = sp.r_start;
+      tm.n_all.v[i] = sp.n_all;
+    }
+    if ((st = hip_status(launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, hs))) !=
+        KVMEM_OK)
+      return st;
+    if ((st = hip_status(launch_aggregate(scores, part, A, nb, s0, n, g, hs))) != KVMEM_OK) return st;
+    if (n_list > 0 &&
+        (st = hip_status(launch_topk(A, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
+      return st;
+  }
+  return KVMEM_OK;
+}
+
+kvmem_status kvmem_materialize(const kvmem_geom *geom, const kvmem_workspace *ws, const int32_t *view_blocks,
+                               int32_t n_list, const int32_t *view_tokens_host, int32_t max_view, float rope_theta,
+                               void *k_view, void *v_view, void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if ((st = check_ws(ws, true)) != KVMEM_OK) return st;
+  if (!view_tokens_host || !k_view || !v_view || n_list < 0) return KVMEM_E_ARG;
+  if (max_view <= 0 || max_view % kBT != 0) return KVMEM_E_ARG;
+  if (!(rope_theta > 1.0f) || !isfinite(rope_theta)) return KVMEM_E_ARG;
+  bool any = false;
+  for (int s = 0; s < ws->n_sessions; ++s) {
+    const int V = view_tokens_host[s];
+    if (V < 0 || V > max_view || (long)V > (long)kBT * n_list) return KVMEM_E_ARG;
+    any = any || V > 0;
+  }
+  if (any && !view_blocks) return KVMEM_E_ARG;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  for (int s0 = 0; s0 < ws->n_sessions; s0 += kMaxSess) {
+    const int n = ws->n_sessions - s0 < kMaxSess ? ws->n_sessions - s0 : kMaxSess;
+    SessI32 vt, na;
+    memset(&vt, 0, sizeof(vt));
+    memset(&na, 0, sizeof(na));
+    for (int i = 0; i < n; ++i) {
+      vt.v[i] = view_tokens_host[s0 + i];
+      na.v[i] = (ws->n_tokens_host[s0 + i] + kBT - 1) / kBT;
+    }
+    st = hip_status(launch_materialize(bf16, ws->k_pool, ws->v_pool, ws->block_table, view_blocks, k_view, v_view,
+                                       ws->dev_error, vt, na, s0, n, geom->n_kv_heads, ws->max_blocks, ws->n_pages,
+                                       n_list, max_view, (double)rope_theta, (hipStream_t)stream));
+    if (st != KVMEM_OK) return st;
+  }
+  return KVMEM_OK;
+}
+
+size_t kvmem_attend_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T, int32_t max_view) {
+  if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || T <= 0 || max_view <= 0 || max_view % kBT) return 0;
+  return attend_scratch(geom, n_sessions, T, max_view).total;
+}
+
+kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,
+                          const float *q_norm_w, float eps, const void *k_view, const void *v_view,
+                          const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
+                          void *scratch, size_t scratch_bytes, void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if (n_sessions <= 0 || !q || !q_norm_w || !k_view || !v_view || !view_tokens_host || !out || T <= 0)
+    return KVMEM_E_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return KVMEM_E_ARG;
+  if (max_view <= 0 || max_view % kBT != 0) return KVMEM_E_ARG;
+  if (!(rope_theta > 1.0f) || !isfinite(rope_theta)) return KVMEM_E_ARG;
+  for (int s = 0; s < n_sessions; ++s)
+    if (view_tokens_host[s] < 0 || view_tokens_host[s] > max_view) return KVMEM_E_ARG;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  const int G = geom->n_q_heads / geom->n_kv_heads;
+  const long rows = (long)T * G;
+  if ((bf16 && rows > 32) || (!bf16 && rows > 64)) return KVMEM_E_UNSUPPORTED;
+  const AttendScratch sc = attend_scratch(geom, n_sessions, T, max_view);
+  if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
+  AttendGeom g;
+  g.Tq = T;
+  g.Hq = geom->n_q_heads;
+  g.Hkv = geom->n_kv_heads;
+  g.G = G;
+  g.rows = (int)rows;
+  g.max_view = max_view;
+  g.max_splits = sc.max_splits;
+  g.tpw = sc.tpw;
+  char *base = (char *)scratch;
+  for (int s0 = 0; s0 < n_sessions; s0 += kMaxSess) {
+    const int n = n_sessions - s0 < kMaxSess ? n_sessions - s0 : kMaxSess;
+    SessI32 vt;
+    memset(&vt, 0, sizeof(vt));
+    for (int i = 0; i < n; ++i) vt.v[i] = view_tokens_host[s0 + i];
+    st = hip_status(launch_attend(bf16, q, q_norm_w, eps, k_view, v_view, (float *)(base + sc.part_o),
+                                  (float2 *)(base + sc.part_ml), out, vt, s0, n, g, (double)rope_theta,
+                                  (hipStream_t)stream));
+    if (st != KVMEM_OK) return st;
+  }
+  return KVMEM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Device-side helpers shared by the KVMem kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvmem {
+
+constexpr int kD = 128;        // head dim
+constexpr int kBT = 32;        // tokens per block
+constexpr int kMaxSess = 64;   // sessions handled by one launch
+
+// Per-session scalars passed by value in the kernel arguments (the lengths
+// live on the host, so no device copy or synchronisation is needed).
+struct SessI32 {
+  int32_t v[kMaxSess];
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal hint: data read once).
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_nt16f(const void *p) {
+  const uint4 v = load_nt16(p);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 / fp64
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, nearest with ties to even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | (u >> 16);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// fp64 -> bf16 bits with a single rounding (nearest, ties to even).  The
+// significand is rounded directly on the fp64 bit pattern to the 8 bits bf16
+// keeps, so no intermediate fp32 rounding can double-round.  Magnitudes below
+// the bf16 normal range use the fixed 2^-133 quantum of its subnormals.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  if (!(fabs(x) >= 0x1p-126)) {
+    if (x != x) return 0x7fc0u;
+    const double y = rint(x * 0x1p133) * 0x1p-133;  // exact multiple of 2^-133
+    return __float_as_uint((float)y) >> 16;
+  }
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t half = 1ull << 44;
+  const uint64_t rem = b & ((1ull << 45) - 1);
+  uint64_t keep = b >> 45;
+  if (rem > half || (rem == half && (keep & 1))) keep += 1;   // carry may bump the exponent
+  const double r = __longlong_as_double((long long)(keep << 45));
+  return __float_as_uint((float)r) >> 16;                      // exact, or +-inf
+}
+
+// ---------------------------------------------------------------------------
+// RoPE angle: phi = pos * theta^(-2i/d) formed in fp64, reduced modulo 2*pi
+// in fp64 with a two-term 2*pi (Cody-Waite), then sin/cos in fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double rope_inv_freq(int i, double theta) {
+  return pow(theta, -(double)(2 * i) / (double)kD);
+}
+
+__device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float &c, float &s) {
+  const double kTwoPiHi = 6.283185307179586232;      // fp64 nearest to 2*pi
+  const double kTwoPiLo = 2.4492935982947064e-16;    // 2*pi - kTwoPiHi
+  const double kInvTwoPi = 0.15915494309189535;
+  const double phi = pos * inv_freq;
+  const double n = rint(phi * kInvTwoPi);
+  double r = fma(-n, kTwoPiHi, phi);
+  r = fma(-n, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
+}
+
+// Slot of token u inside a dimension-major 32-token V view block.
+__host__ __device__ __forceinline__ int v_slot(int u) {
+  return 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppMirror8 = 0x141;    // row_half_mirror: lane i <-> 7 - i within 8
+constexpr int kDppMirror16 = 0x140;   // row_mirror: lane i <-> 15 - i within 16
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ void dev_flag(int32_t *err, int bits) {
+  if (err) atomicOr(err, bits);
+}
+
+}  // namespace kvmem

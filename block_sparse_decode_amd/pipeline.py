@@ -1,0 +1,107 @@
+"""Device buffers for one KV workspace and the four library calls in order.
+
+Plumbing only: torch allocates device memory; every computation is a call
+into libkvmem.so.  Used by the tests, the benchmark and the smoke check.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+BLOCK = 32
+
+
+def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Host array (bf16 as raw uint16 bits, or fp32) -> device tensor."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def view_length(n_tok: int, k_select: int, n_recent: int) -> int:
+    """View tokens of a session (what kvmem_score_select reports), used to size buffers."""
+    nb_full, nb_all = n_tok // BLOCK, -(-n_tok // BLOCK)
+    r0 = max(0, nb_all - n_recent)
+    nc = min(nb_full, r0)
+    return BLOCK * min(k_select, nc) + max(0, n_tok - BLOCK * r0)
+
+
+def v_view_token_major(v_view: torch.Tensor) -> torch.Tensor:
+    """[S][Hkv][nblk][d][32 slots] dimension-major V view -> [S][Hkv][nblk*32][d]
+    token-major (inverse of the slot order documented in kvmem.h)."""
+    sigma = [8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3) for u in range(BLOCK)]
+    idx = torch.tensor(sigma, device=v_view.device)
+    x = v_view.index_select(-1, idx).transpose(-1, -2)          # [..][nblk][32][d]
+    S, H, nb = x.shape[:3]
+    return x.reshape(S, H, nb * BLOCK, x.shape[-1])
+
+
+class DeviceWorkspace:
+    """Inputs of a workload on the GPU plus every buffer the four calls use."""
+
+    def __init__(self, wl, device="cuda", k_select=None, n_recent=None, max_view=None, with_v=True):
+        cfg = wl.cfg
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.dtype = cfg.dtype
+        self.tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.k_select = cfg.k_select if k_select is None else k_select
+        self.n_recent = cfg.n_recent if n_recent is None else n_recent
+        self.T = cfg.T
+        S, H, d = cfg.n_sessions, cfg.n_kv_heads, cfg.head_dim
+        self.S, self.H, self.d = S, H, d
+        self.k_pool = to_device(wl.k_pool, cfg.dtype, self.device)
+        self.v_pool = to_device(wl.v_pool, cfg.dtype, self.device) if with_v else None
+        self.block_table = torch.from_numpy(np.ascontiguousarray(wl.block_table, dtype=np.int32)).to(self.device)
+        self.n_tokens = np.ascontiguousarray(wl.n_tokens, dtype=np.int32)
+        self.dev_error = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self.max_blocks = int(wl.block_table.shape[1])
+        self.q = to_device(wl.q, cfg.dtype, self.device)
+        self.q_norm_w = torch.from_numpy(np.ascontiguousarray(wl.q_norm_w, dtype=np.float32)).to(self.device)
+        self.geom = L.make_geom(cfg.n_q_heads, H, cfg.dtype, d)
+        self.ws = L.make_workspace(self.k_pool, self.v_pool, self.block_table, self.n_tokens, self.dev_error)
+
+        self.index = torch.empty((S, H, self.max_blocks, d), dtype=self.tdtype, device=self.device)
+        self.n_list = self.k_select + self.n_recent
+        self.view_blocks = torch.empty((S, H, max(1, self.n_list)), dtype=torch.int32, device=self.device)
+        self.view_tokens = np.zeros(S, np.int32)
+        need = max(view_length(int(n), self.k_select, self.n_recent) for n in self.n_tokens)
+        mv = max(BLOCK, -(-need // BLOCK) * BLOCK)
+        self.max_view = mv if max_view is None else max_view
+        self.k_view = torch.empty((S, H, self.max_view, d), dtype=self.tdtype, device=self.device)
+        self.v_view = torch.empty((S, H, self.max_view // BLOCK, d, BLOCK), dtype=self.tdtype, device=self.device)
+        self.out = torch.empty((S, self.T, cfg.n_q_heads, d), dtype=torch.float32, device=self.device)
+        nb = L.kvmem_score_select_scratch_bytes(self.geom, S, self.max_blocks, self.T)
+        na = L.kvmem_attend_scratch_bytes(self.geom, S, self.T, self.max_view)
+        self.score_scratch = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.device)
+        self.attend_scratch = torch.empty(max(na, 1), dtype=torch.uint8, device=self.device)
+        self.eps = cfg.eps
+        self.theta = cfg.rope_theta
+
+    # --- the four calls ---------------------------------------------------
+    def build_index(self, stream=None):
+        L.kvmem_build_index(self.geom, self.ws, self.index, stream)
+
+    def score_select(self, stream=None, scores=None, agg=None):
+        L.kvmem_score_select(self.geom, self.ws, self.index, self.q, self.T, self.q_norm_w, self.eps,
+                             self.k_select, self.n_recent, self.view_blocks, self.view_tokens,
+                             scores=scores, agg=agg, scratch=self.score_scratch, stream=stream)
+
+    def materialize(self, stream=None):
+        L.kvmem_materialize(self.geom, self.ws, self.view_blocks, self.n_list, self.view_tokens,
+                            self.max_view, self.theta, self.k_view, self.v_view, stream)
+
+    def attend(self, stream=None):
+        L.kvmem_attend(self.geom, self.S, self.q, self.T, self.q_norm_w, self.eps, self.k_view, self.v_view,
+                       self.view_tokens, self.max_view, self.theta, self.out, scratch=self.attend_scratch,
+                       stream=stream)
+
+    def run(self, stream=None):
+        self.build_index(stream)
+        self.score_select(stream)
+        self.materialize(stream)
+        self.attend(stream)

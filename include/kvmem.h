@@ -1,0 +1,228 @@
+/*
+ * kvmem.h -- C ABI of the KVMem hot path on MI355X (gfx950).
+ *
+ * KVMem keeps a long agent history as paged KV and runs each step over a
+ * bounded, query-selected execution view.  The library implements the
+ * data-parallel path of that method as four calls:
+ *
+ *   kvmem_build_index    Mean-K index: mean of each 32-token block's pre-RoPE
+ *                        keys, per KV head.
+ *   kvmem_score_select   q-RMSNorm, block scores s_b = <q, k_bar_b>/sqrt(d),
+ *                        per-query-head softmax over blocks, sum per KV head,
+ *                        top-k under the block budget plus the recent blocks.
+ *   kvmem_materialize    gather of the selected blocks in their original
+ *                        order, re-RoPE'd to contiguous view positions.
+ *   kvmem_attend         decode attention of the step's queries over the view.
+ *
+ * Sources, cited by page title and section:
+ *   [README] "KVMEM: Virtualizing a million-token agent workspace with paged
+ *            KV" (reproduction README): 'Background and main changes',
+ *            'Core equation', '2026-09-08 validation correction',
+ *            'Local reproduction'.
+ *   [REVIEW] "KVMem: Virtualizing Million-Token Agent Workspaces on a Consumer
+ *            GPU" (evolve.pub review): 'Summary', 'Key claims under review',
+ *            'Scope & Claims'.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller unless the name ends in
+ *    _host.  The library allocates nothing and keeps no state between calls.
+ *  - Every call validates its arguments on the host first; on any invalid
+ *    argument it returns an error status and enqueues nothing.  Otherwise it
+ *    enqueues its kernels on `stream` (a hipStream_t; NULL = the default
+ *    stream) and returns KVMEM_OK without synchronising.  Faults inside a
+ *    kernel surface at the caller's next synchronisation, as usual in HIP.
+ *  - A failed kernel launch returns KVMEM_E_HIP (work enqueued before it in
+ *    the same call may already be running).
+ *  - Geometry: head_dim must be 128 and block_tokens 32; n_q_heads must be a
+ *    multiple of n_kv_heads (query head g belongs to KV head g / G with
+ *    G = n_q_heads / n_kv_heads).  kv_dtype is KVMEM_F32 or KVMEM_BF16 and
+ *    applies to the K/V pools, the index, the queries and the view.
+ *  - Calls on the same stream are ordered; concurrent calls on different
+ *    streams that write the same buffers race.  The library itself is
+ *    thread-safe (no global state).
+ */
+#ifndef KVMEM_H_
+#define KVMEM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVMEM_OK = 0,
+  KVMEM_E_ARG = 1,          /* null pointer, negative size, inconsistent sizes  */
+  KVMEM_E_UNSUPPORTED = 2,  /* geometry or dtype the kernels do not implement   */
+  KVMEM_E_WORKSPACE = 3,    /* scratch buffer smaller than the queried size     */
+  KVMEM_E_HIP = 4           /* a HIP launch failed                              */
+} kvmem_status;
+
+typedef enum { KVMEM_F32 = 0, KVMEM_BF16 = 1 } kvmem_dtype;
+
+/* Bits a kernel ORs into kvmem_workspace.dev_error when it meets a bad table
+ * entry.  The offending block is not read; its outputs are written as zeros. */
+#define KVMEM_DEVERR_PAGE  1   /* block_table entry outside [0, n_pages)            */
+#define KVMEM_DEVERR_BLOCK 2   /* view_blocks entry outside the session's history   */
+
+typedef struct {
+  int32_t n_q_heads;     /* Hq                                  */
+  int32_t n_kv_heads;    /* Hkv                                 */
+  int32_t head_dim;      /* d, must be 128                      */
+  int32_t block_tokens;  /* tokens per block, must be 32        */
+  int32_t kv_dtype;      /* kvmem_dtype                         */
+} kvmem_geom;
+
+/* The paged workspace ([README 'Background and main changes']: the history is
+ * kept as paged KV; [README 'Core equation']: address space and execution
+ * window are separate).
+ *
+ * k_pool, v_pool : [n_pages][Hkv][32][d] in kv_dtype.  A page holds one
+ *                  32-token block of one session for all KV heads; keys are
+ *                  stored BEFORE RoPE.  Tokens of a partial last block beyond
+ *                  the history are never read.
+ * block_table    : [n_sessions][max_blocks] int32, logical block -> page.
+ *                  Entries past a session's history are never read.
+ * n_tokens_host  : HOST array [n_sessions] of history lengths, each in
+ *                  [0, 32 * max_blocks].
+ * dev_error      : optional device int32 (may be NULL) that kernels OR
+ *                  KVMEM_DEVERR_* bits into.                                 */
+typedef struct {
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *block_table;
+  const int32_t *n_tokens_host;
+  int32_t n_sessions;
+  int32_t max_blocks;
+  int32_t n_pages;
+  int32_t *dev_error;
+} kvmem_workspace;
+
+/* ---------------------------------------------------------------------------
+ * Mean-K index ([README 'Core equation']: each block b has an index vector
+ * k_bar_b; [REVIEW 'Summary']: a position-independent Mean-K index over
+ * 32-token blocks, i.e. the mean of the block's pre-RoPE keys).
+ *
+ * For every session s, KV head h and complete block beta < n_tokens[s] / 32:
+ *   index[s][h][beta][:] = round( (1/32) * sum_{u<32} K[page(s,beta)][h][u][:] )
+ * The sum is accumulated in fp64 and rounded once (to nearest, ties to even)
+ * to kv_dtype.  Rows for beta >= n_tokens[s] / 32 are not written.  v_pool
+ * is not used and may be NULL.
+ *
+ * index : [n_sessions][Hkv][max_blocks][d] in kv_dtype.
+ * ------------------------------------------------------------------------- */
+kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws,
+                               void *index, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Query-conditioned block selection ([README 'Core equation']:
+ * s_b = <q, k_bar_b>/sqrt(d), selected KV within the block budget;
+ * [README '2026-09-08 validation correction']: the query is RMS-normalised
+ * and GQA query heads are softmaxed per head, not averaged before the
+ * softmax; [README 'Local reproduction']: recent blocks share the budget).
+ *
+ * For session s, with N = n_tokens[s], Nb = N / 32 complete blocks,
+ * Nall = ceil(N / 32) blocks, recent range [r0, Nall) with
+ * r0 = max(0, Nall - n_recent), candidates beta < nc = min(Nb, r0), and
+ * k_eff = min(k_select, nc):
+ *   q~[t][g]   = w * q[t][g] / sqrt(mean_i q[t][g][i]^2 + eps)      (fp32)
+ *   s[t][g][b] = <q~[t][g], index[h(g)][b]> / sqrt(d),  b < Nb       (fp32)
+ *   p[t][g][b] = softmax over b < Nb of s[t][g][:]
+ *   A[h][b]    = sum_t sum_{g in group h} p[t][g][b]
+ * The k_eff candidates with the largest A (ties: lower block index) are
+ * listed in ascending order, followed by the recent blocks ascending, then
+ * -1 padding:
+ *   view_blocks[s][h][0 .. k_select + n_recent)
+ * view_tokens_host[s] receives the view length
+ *   V = 32 * k_eff + max(0, N - 32 * r0)
+ * (computed on the host: it depends on the lengths only).
+ *
+ * q            : [n_sessions][T][Hq][d] in kv_dtype.
+ * q_norm_w     : [d] fp32.
+ * scores_opt   : optional [n_sessions][T][Hq][max_blocks] fp32, receives s.
+ * agg_opt      : optional [n_sessions][Hkv][max_blocks] fp32, receives A.
+ * scratch      : device buffer of at least kvmem_score_select_scratch_bytes().
+ * Requires T >= 1, k_select >= 0, n_recent >= 0.
+ * ------------------------------------------------------------------------- */
+size_t kvmem_score_select_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions,
+                                        int32_t max_blocks, int32_t T);
+kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *ws,
+                                const void *index, const void *q, int32_t T,
+                                const float *q_norm_w, float eps,
+                                int32_t k_select, int32_t n_recent,
+                                int32_t *view_blocks, int32_t *view_tokens_host,
+                                float *scores_opt, float *agg_opt,
+                                void *scratch, size_t scratch_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Materialisation of the bounded execution view ([REVIEW 'Summary' and
+ * 'Scope & Claims']: selected blocks are restored with position-consistent
+ * re-RoPE into a bounded view; [README 'Background and main changes']: the
+ * view is materialised within the native window).
+ *
+ * View slot j = 32*m + u (m < ceil(V/32), u < 32, j < V) holds token u of
+ * block beta = view_blocks[s][h][m]:
+ *   K_view[j] = round( RoPE(K[page(s,beta)][h][u], position j) )
+ *   V_view[j] = V[page(s,beta)][h][u]        (bit copy)
+ * RoPE rotates pairs (i, i + d/2) by angle j * theta^(-2i/d); the angle is
+ * formed in fp64, the rotation in fp32, the result rounded to nearest even.
+ * Slots j in [V, 32 * ceil(V/32)) are written as zeros; later slots are not
+ * written.
+ *
+ * view_blocks      : as written by kvmem_score_select, row stride n_list.
+ * view_tokens_host : HOST [n_sessions] view lengths V (<= 32 * n_list and
+ *                    <= max_view).
+ * k_view           : [n_sessions][Hkv][max_view][d] in kv_dtype, token-major.
+ * v_view           : [n_sessions][Hkv][max_view/32][d][32] in kv_dtype: each
+ *                    32-token view block is stored dimension-major, and token
+ *                    u of the block sits at slot
+ *                      sigma(u) = 8*((u & 15) >> 2) + 4*(u >> 4) + (u & 3).
+ *                    (This is the operand order of the attention kernel's
+ *                    matrix-core tiles, so kvmem_attend reads it directly.)
+ * max_view must be a positive multiple of 32.
+ * ------------------------------------------------------------------------- */
+kvmem_status kvmem_materialize(const kvmem_geom *geom, const kvmem_workspace *ws,
+                               const int32_t *view_blocks, int32_t n_list,
+                               const int32_t *view_tokens_host, int32_t max_view,
+                               float rope_theta, void *k_view, void *v_view, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode attention over the view ([README 'Local reproduction']: attention
+ * over the selected view replaces full attention).
+ *
+ * For session s with view length V, query token t < T and query head g:
+ *   q_r       = RoPE(q~[t][g], position V + t)       (q~ as in score_select)
+ *   l_j       = <q_r, K_view[h(g)][j]> / sqrt(d),  j < V
+ *   out[t][g] = sum_j softmax_j(l) * V_view[h(g)][j]
+ * The step's own tokens attend to the view only (no mask among them).  An
+ * empty view (V = 0) gives a zero output.  Accumulation is fp32; the
+ * split-K partials are merged by log-sum-exp in a fixed order, so results are
+ * deterministic run to run.
+ *
+ * q, q_norm_w, eps : as for kvmem_score_select.
+ * k_view, v_view   : as written by kvmem_materialize.
+ * out              : [n_sessions][T][Hq][d] fp32.
+ * scratch          : at least kvmem_attend_scratch_bytes() bytes.
+ * ------------------------------------------------------------------------- */
+size_t kvmem_attend_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T,
+                                  int32_t max_view);
+kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions,
+                          const void *q, int32_t T, const float *q_norm_w, float eps,
+                          const void *k_view, const void *v_view,
+                          const int32_t *view_tokens_host, int32_t max_view,
+                          float rope_theta, float *out,
+                          void *scratch, size_t scratch_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *kvmem_status_string(kvmem_status status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t kvmem_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVMEM_H_ */

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes scratch buffers, and rejects every invalid argument
+before it enqueues anything (so these calls never reach the device)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import __graft_entry__  # noqa: F401  (puts the repo root on sys.path)
+from block_sparse_decode_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvmem.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        __graft_entry__.build()
+    return L.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kvmem_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_match_header(lib):
+    decl = _declared()
+    assert set(decl) == set(L.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in decl:
+        assert name in syms, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    assert L.status_string(0) == "ok"
+    assert "scratch" in L.status_string(3)
+    assert L.kvmem_version() >= 100
+
+
+def _geom(dtype="bf16", Hq=64, Hkv=8, d=128, bt=32):
+    return L.make_geom(Hq, Hkv, dtype, d, bt)
+
+
+def _ws(S=2, max_blocks=64, n_tok=(100, 2048), n_pages=70):
+    n = np.asarray(n_tok, np.int32)
+    ws = L.Workspace(0x1000, 0x2000, 0x3000, n.ctypes.data, S, max_blocks, n_pages, None)
+    return ws, n
+
+
+def test_scratch_sizes(lib):
+    g = _geom()
+    a = L.kvmem_score_select_scratch_bytes(g, 1, 32768, 1)
+    # per-head scores + per-chunk stats + aggregated scores
+    assert a >= 64 * 32768 * 4 + 8 * 32768 * 4
+    assert L.kvmem_score_select_scratch_bytes(g, 0, 32768, 1) == 0
+    assert L.kvmem_score_select_scratch_bytes(_geom(d=64), 1, 32768, 1) == 0
+    b = L.kvmem_attend_scratch_bytes(g, 1, 1, 262144)
+    assert b > 0 and b % 256 == 0
+    assert L.kvmem_attend_scratch_bytes(g, 1, 1, 100) == 0          # not a multiple of 32
+
+
+def test_build_index_rejects(lib):
+    ws, n = _ws()
+    assert L.kvmem_build_index(_geom(), ws, None, check=False) == L.KVMEM_E_ARG
+    assert L.kvmem_build_index(_geom(d=64), ws, 0x10, check=False) == L.KVMEM_E_UNSUPPORTED
+    assert L.kvmem_build_index(_geom(bt=16), ws, 0x10, check=False) == L.KVMEM_E_UNSUPPORTED
+    assert L.kvmem_build_index(_geom(Hq=63), ws, 0x10, check=False) == L.KVMEM_E_ARG
+    g = _geom()
+    g.kv_dtype = 7
+    assert L.kvmem_build_index(g, ws, 0x10, check=False) == L.KVMEM_E_UNSUPPORTED
+    ws2, n2 = _ws(n_tok=(100, 64 * 32 + 1))                           # longer than the table
+    assert L.kvmem_build_index(_geom(), ws2, 0x10, check=False) == L.KVMEM_E_ARG
+    ws3, n3 = _ws(n_tok=(-1, 5))
+    assert L.kvmem_build_index(_geom(), ws3, 0x10, check=False) == L.KVMEM_E_ARG
+    st = L.load().kvmem_build_index(None, ctypes.byref(ws), 0x10, None)
+    assert st == L.KVMEM_E_ARG
+    st = L.load().kvmem_build_index(ctypes.byref(_geom()), None, 0x10, None)
+    assert st == L.KVMEM_E_ARG
+
+
+def test_score_select_rejects(lib):
+    ws, n = _ws()
+    vt = np.zeros(2, np.int32)
+    g = _geom()
+    need = L.kvmem_score_select_scratch_bytes(g, 2, 64, 1)
+    common = dict(view_tokens_host=vt, scratch=0x4000, scratch_bytes=need, check=False)
+    call = lambda **kw: L.kvmem_score_select(**{**dict(geom=g, ws=ws, index=0x10, q=0x20, T=1, q_norm_w=0x30,
+                                                      eps=1e-6, k_select=8, n_recent=4, view_blocks=0x40),
+                                              **common, **kw})
+    assert call(T=0) == L.KVMEM_E_ARG
+    assert call(k_select=-1) == L.KVMEM_E_ARG
+    assert call(n_recent=-2) == L.KVMEM_E_ARG
+    assert call(index=None) == L.KVMEM_E_ARG
+    assert call(q=None) == L.KVMEM_E_ARG
+    assert call(q_norm_w=None) == L.KVMEM_E_ARG
+    assert call(view_blocks=None) == L.KVMEM_E_ARG
+    assert call(eps=float("nan")) == L.KVMEM_E_ARG
+    assert call(eps=-1.0) == L.KVMEM_E_ARG
+    assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
+    assert call(scratch=None) == L.KVMEM_E_WORKSPACE
+    assert call(geom=_geom(d=256)) == L.KVMEM_E_UNSUPPORTED
+
+
+def test_materialize_rejects(lib):
+    ws, n = _ws()
+    g = _geom()
+    vt = np.array([64, 96], np.int32)
+    call = lambda **kw: L.kvmem_materialize(**{**dict(geom=g, ws=ws, view_blocks=0x10, n_list=4,
+                                                     view_tokens_host=vt, max_view=128, rope_theta=1e6,
+                                                     k_view=0x20, v_view=0x30, check=False), **kw})
+    assert call(max_view=100) == L.KVMEM_E_ARG             # not a multiple of 32
+    assert call(max_view=64) == L.KVMEM_E_ARG              # shorter than a view
+    assert call(n_list=2) == L.KVMEM_E_ARG                 # view longer than the list allows
+    assert call(view_blocks=None) == L.KVMEM_E_ARG
+    assert call(k_view=None) == L.KVMEM_E_ARG
+    assert call(rope_theta=0.5) == L.KVMEM_E_ARG
+    assert call(rope_theta=float("inf")) == L.KVMEM_E_ARG
+    ws_nov = L.Workspace(0x1000, None, 0x3000, n.ctypes.data, 2, 64, 70, None)
+    assert call(ws=ws_nov) == L.KVMEM_E_ARG                # V pool needed
+    assert call(view_tokens_host=np.array([-1, 0], np.int32)) == L.KVMEM_E_ARG
+
+
+def test_attend_rejects(lib):
+    g = _geom()
+    vt = np.array([64, 96], np.int32)
+    need = L.kvmem_attend_scratch_bytes(g, 2, 1, 128)
+    call = lambda **kw: L.kvmem_attend(**{**dict(geom=g, n_sessions=2, q=0x10, T=1, q_norm_w=0x20, eps=1e-6,
+                                                k_view=0x30, v_view=0x40, view_tokens_host=vt, max_view=128,
+                                                rope_theta=1e6, out=0x50, scratch=0x60, scratch_bytes=need,
+                                                check=False), **kw})
+    assert call(T=0) == L.KVMEM_E_ARG
+    assert call(n_sessions=0) == L.KVMEM_E_ARG
+    assert call(out=None) == L.KVMEM_E_ARG
+    assert call(view_tokens_host=np.array([64, 160], np.int32)) == L.KVMEM_E_ARG
+    assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
+    assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head in bf16
+    assert call(geom=_geom(bt=64)) == L.KVMEM_E_UNSUPPORTED

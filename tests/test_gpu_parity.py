@@ -1,0 +1,278 @@
+"""GPU parity of every step against the CPU oracle, through the C ABI.
+
+Bars (from the scope of the hot path):
+  * Mean-K index            : bit-exact (fp64 sums, one rounding on both sides)
+  * raw block scores s      : |d| <= 1e-3 * max(|s_ref|, rms of the row)
+  * aggregated scores A     : |d| <= 1e-3 * A_ref
+  * selected blocks, view   : bit-exact (inputs certified with a 1e-3 cut margin)
+  * V view                  : bit-exact;  K view: <= 1 bf16 ulp / 2e-6 relative fp32
+  * attention output        : <= 2e-2 max-abs for bf16, <= 1e-4 for fp32
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvmem_oracle as O
+from tests.certify import certify
+from tests.helpers import make_workload, oracle_ws, small_cfg
+from workloads import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+ATT_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _bits_to_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
+    with np.errstate(invalid="ignore"):          # buffers hold unwritten slots past the views
+        if dtype == "bf16":
+            b = t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << np.uint32(16)
+            return b.view(np.float32).astype(np.float64)
+        return t.cpu().numpy().astype(np.float64)
+
+
+def run_gpu(wl, scores=True):
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace, v_view_token_major
+    cfg = wl.cfg
+    print(f"[gpu] {cfg.name} S={cfg.n_sessions} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} T={cfg.T} "
+          f"N={list(wl.n_tokens)[:4]} k={cfg.k_select} R={cfg.n_recent}", flush=True)
+    dw = DeviceWorkspace(wl, "cuda")
+    S, H, T, Hq = cfg.n_sessions, cfg.n_kv_heads, cfg.T, cfg.n_q_heads
+    sc = torch.full((S, T, Hq, dw.max_blocks), float("nan"), device="cuda") if scores else None
+    ag = torch.full((S, H, dw.max_blocks), float("nan"), device="cuda")
+    dw.build_index()
+    dw.score_select(scores=sc, agg=ag)
+    dw.materialize()
+    dw.attend()
+    torch.cuda.synchronize()
+    res = dict(dw=dw, index=_bits_to_f64(dw.index, cfg.dtype), agg=ag.cpu().numpy().astype(np.float64),
+               scores=None if sc is None else sc.cpu().numpy().astype(np.float64),
+               vb=dw.view_blocks.cpu().numpy(), vt=dw.view_tokens.copy(),
+               kview=_bits_to_f64(dw.k_view, cfg.dtype),
+               vview=_bits_to_f64(v_view_token_major(dw.v_view).contiguous(), cfg.dtype),
+               out=dw.out.cpu().numpy().astype(np.float64), err=int(dw.dev_error.item()))
+    return res
+
+
+def check_session(wl, res, s, heads=None, att_heads=None, check_scores=True, tag=""):
+    cfg = wl.cfg
+    ws = oracle_ws(wl)
+    G = cfg.group
+    heads = range(cfg.n_kv_heads) if heads is None else heads
+    att_heads = heads if att_heads is None else att_heads
+    n_tok = int(wl.n_tokens[s])
+    nb = n_tok // 32
+    index = [O.mean_k_index(ws, s, h) for h in range(cfg.n_kv_heads)]
+    S_all, A_all, qn = O.session_scores(ws, s, wl.q[s], wl.q_norm_w, cfg.eps, index,
+                                        keep_scores=check_scores)
+    V_ref = O.view_tokens(n_tok, cfg.k_select, cfg.n_recent)
+    assert int(res["vt"][s]) == V_ref, (tag, s)
+    worst_att = 0.0
+    for h in heads:
+        # index: bit-exact
+        assert np.array_equal(res["index"][s, h, :nb], index[h]), (tag, s, h, "index")
+        # aggregated scores
+        A_ref = A_all[h]
+        A_gpu = res["agg"][s, h, :nb]
+        assert np.all(np.abs(A_gpu - A_ref) <= 1e-3 * A_ref + 1e-30), (tag, s, h, "A")
+        if check_scores and nb > 0:
+            s_ref = S_all[h]                                      # [T][G][nb]
+            s_gpu = res["scores"][s, :, h * G:(h + 1) * G, :nb]
+            scale = np.maximum(np.abs(s_ref), np.sqrt(np.mean(s_ref ** 2, axis=-1, keepdims=True)))
+            assert np.all(np.abs(s_gpu - s_ref) <= 1e-3 * scale), (tag, s, h, "scores")
+        # selection: bit-exact list incl. recent and padding
+        lst, V = O.view_list(A_ref, n_tok, cfg.k_select, cfg.n_recent)
+        n_list = cfg.k_select + cfg.n_recent
+        want = np.full(n_list, -1, np.int64)
+        want[:len(lst)] = lst
+        assert np.array_equal(res["vb"][s, h, :n_list], want), (tag, s, h, "view_blocks")
+        if h not in att_heads:
+            continue
+        kv, vv = O.materialize(ws, s, h, lst, V, cfg.rope_theta)
+        assert np.array_equal(res["vview"][s, h, :V], vv), (tag, s, h, "V view")
+        kg = res["kview"][s, h, :V]
+        # one storage rounding plus the fp32 rotation error, which is relative to
+        # the rotated pair's magnitude (cancellation can make a result tiny)
+        rot = 1e-6 * np.abs(kv).max(axis=-1, keepdims=True)
+        if cfg.dtype == "bf16":
+            ulp = np.ldexp(1.0, np.frexp(np.abs(kv))[1] - 8)
+            assert np.all(np.abs(kg - kv) <= ulp + rot), (tag, s, h, "K view")
+        else:
+            assert np.all(np.abs(kg - kv) <= 2e-7 * np.abs(kv) + rot), (tag, s, h, "K view")
+        # the padded tail of the last view block is zero
+        if V % 32:
+            end = -(-V // 32) * 32
+            assert np.all(res["kview"][s, h, V:end] == 0) and np.all(res["vview"][s, h, V:end] == 0)
+        o_ref = O.attend(qn[:, h * G:(h + 1) * G], kv, vv, cfg.rope_theta)
+        o_gpu = res["out"][s, :, h * G:(h + 1) * G]
+        err = float(np.abs(o_gpu - o_ref).max()) if V else float(np.abs(o_gpu).max())
+        worst_att = max(worst_att, err)
+        assert err <= ATT_TOL[cfg.dtype], (tag, s, h, "attend", err)
+    return worst_att
+
+
+def _full_check(wl, **kw):
+    res = run_gpu(wl)
+    assert res["err"] == 0
+    worst = 0.0
+    for s in range(wl.cfg.n_sessions):
+        worst = max(worst, check_session(wl, res, s, tag=wl.cfg.name, **kw))
+    print(f"[gpu] {wl.cfg.name}: worst attention |err| = {worst:.3e}", flush=True)
+    return res
+
+
+# ---------------------------------------------------------------------------
+# small and edge-case workloads (several tiles, ragged tails)
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    "bf16_ragged": small_cfg("bf16_ragged", "bf16", S=3, Hq=16, Hkv=2, n_tokens=(32 * 300 + 5, 32 * 64, 7),
+                             k=24, R=3, n_planted=6, spare_pages=5, seed=31),
+    "f32_ragged": small_cfg("f32_ragged", "f32", S=2, Hq=8, Hkv=2, n_tokens=(32 * 513 + 31, 32 * 40),
+                            k=17, R=2, n_planted=5, spare_pages=2, seed=32),
+    "bf16_t2_g8": small_cfg("bf16_t2_g8", "bf16", S=2, Hq=16, Hkv=2, T=2, n_tokens=(32 * 700, 32 * 257 + 1),
+                            k=50, R=5, n_planted=8, seed=33),
+    "bf16_t4_g8": small_cfg("bf16_t4_g8", "bf16", S=3, Hq=16, Hkv=2, T=4, n_tokens=(32 * 1100, 32 * 600, 32 * 90),
+                            k=40, R=8, n_planted=10, seed=34),
+    "bf16_g4": small_cfg("bf16_g4", "bf16", S=1, Hq=8, Hkv=2, n_tokens=(32 * 1000,), k=64, R=4, seed=35),
+    "bf16_g1": small_cfg("bf16_g1", "bf16", S=1, Hq=4, Hkv=4, n_tokens=(32 * 777 + 3,), k=32, R=2, seed=36),
+    "f32_t3_g4": small_cfg("f32_t3_g4", "f32", S=2, Hq=8, Hkv=2, T=3, n_tokens=(32 * 200 + 9, 32 * 33),
+                           k=12, R=2, seed=37),
+    "recent_only": small_cfg("recent_only", "bf16", S=2, Hq=16, Hkv=2, n_tokens=(32 * 50 + 3, 32 * 8),
+                             k=0, R=6, seed=38),
+    "budget_covers_all": small_cfg("budget_covers_all", "bf16", S=2, Hq=16, Hkv=2, n_tokens=(32 * 60 + 3, 32 * 11),
+                             k=10_000, R=2, seed=39),
+    "r0_partial": small_cfg("r0_partial", "bf16", S=2, Hq=16, Hkv=2, n_tokens=(32 * 90 + 17, 32 * 33),
+                            k=20, R=0, seed=40),
+    "empty_and_tiny": small_cfg("empty_and_tiny", "bf16", S=4, Hq=16, Hkv=2, n_tokens=(0, 5, 32, 32 * 40),
+                                k=8, R=2, n_planted=2, seed=41),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    _need_gpu()
+    wl = make_workload(SMALL[name])
+    certify(wl)
+    _full_check(wl)
+
+
+def test_c1_parity():
+    _need_gpu()
+    wl = make_workload(CONFIGS["c1"])
+    certify(wl)
+    res = _full_check(wl)
+    # the planted blocks are the selected ones
+    planted = set(np.nonzero(wl.plant_mag[0, 0])[0].tolist())
+    assert set(res["vb"][0, 0, :8].tolist()) == planted
+
+
+def test_random_qnorm_weight():
+    _need_gpu()
+    cfg = small_cfg("w_random", "bf16", S=1, Hq=16, Hkv=2, n_tokens=(32 * 400,), k=30, R=4, seed=42,
+                    w_mode="random")
+    wl = make_workload(cfg)
+    certify(wl)
+    _full_check(wl)
+
+
+# ---------------------------------------------------------------------------
+# properties
+# ---------------------------------------------------------------------------
+
+def _defined(wl, res):
+    """The parts of every output the library defines (buffers also hold
+    never-written slots past each session's blocks and view)."""
+    out = {"out": res["out"], "vb": res["vb"]}
+    for s in range(wl.cfg.n_sessions):
+        nb = int(wl.n_tokens[s]) // 32
+        V = int(res["vt"][s])
+        out[f"index{s}"] = res["index"][s, :, :nb]
+        out[f"agg{s}"] = res["agg"][s, :, :nb]
+        out[f"kview{s}"] = res["kview"][s, :, :V]
+        out[f"vview{s}"] = res["vview"][s, :, :V]
+    return out
+
+
+def test_deterministic_and_page_permutation_invariant():
+    _need_gpu()
+    cfg = small_cfg("perm", "bf16", S=2, Hq=16, Hkv=2, n_tokens=(32 * 500 + 7, 32 * 100), k=40, R=3, seed=43,
+                    spare_pages=3)
+    wl = make_workload(cfg)
+    a = _defined(wl, run_gpu(wl))
+    b = _defined(wl, run_gpu(wl))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k                       # run-to-run bitwise
+    perm = np.random.default_rng(5).permutation(wl.n_pages)
+    wl2 = make_workload(cfg)
+    wl2.k_pool = np.empty_like(wl.k_pool)
+    wl2.v_pool = np.empty_like(wl.v_pool)
+    wl2.k_pool[perm] = wl.k_pool
+    wl2.v_pool[perm] = wl.v_pool
+    wl2.block_table = np.where(wl.block_table >= 0, perm[np.maximum(wl.block_table, 0)], -1).astype(np.int32)
+    c = _defined(wl2, run_gpu(wl2))
+    for k in a:
+        assert np.array_equal(a[k], c[k]), k
+
+
+def test_split_count_invariance():
+    # a larger view buffer changes the split-K partition; the merge must agree
+    _need_gpu()
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace
+    cfg = small_cfg("splits", "bf16", S=1, Hq=64, Hkv=8, n_tokens=(32 * 4000,), k=1000, R=8, seed=44)
+    wl = make_workload(cfg)
+    outs = []
+    for mv in (None, 32 * 1008 * 8, 32 * 1008 * 64):
+        dw = DeviceWorkspace(wl, "cuda", max_view=mv)
+        dw.run()
+        torch.cuda.synchronize()
+        outs.append(dw.out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() < 1e-5
+
+
+def test_bad_page_is_flagged_not_read():
+    _need_gpu()
+    cfg = small_cfg("badpage", "bf16", S=1, Hq=16, Hkv=2, n_tokens=(32 * 64,), k=8, R=2, seed=45)
+    wl = make_workload(cfg)
+    wl.block_table[0, 5] = wl.n_pages + 100          # outside the pool: kernels must skip it
+    res = run_gpu(wl, scores=False)
+    assert res["err"] & 1
+    assert np.all(res["index"][0, :, 5] == 0)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_c2_full():
+    _need_gpu()
+    wl = make_workload(CONFIGS["c2"])
+    certify(wl)
+    _full_check(wl, check_scores=True)
+
+
+def test_c3_full():
+    _need_gpu()
+    wl = make_workload(CONFIGS["c3"])
+    certify(wl)
+    res = run_gpu(wl, scores=False)
+    assert res["err"] == 0
+    # selection for every head; materialise + attention on two heads
+    check_session(wl, res, 0, att_heads=(0, 5), check_scores=False, tag="c3")
+
+
+def test_c4_full():
+    _need_gpu()
+    wl = make_workload(CONFIGS["c4"])
+    certify(wl)
+    res = run_gpu(wl)
+    assert res["err"] == 0
+    for s in range(16):
+        check_session(wl, res, s, att_heads=(s % 8,), tag=f"c4 s={s}")
