@@ -1,0 +1,228 @@
+"""Benchmark of the KVMem hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+One step is one pass of the whole path over the 1M-token workspace
+(1,048,576 tokens = 32,768 blocks; 64 query / 8 KV heads; d = 128; bf16):
+    kvmem_score_select -> kvmem_materialize -> kvmem_attend -> kvmem_build_index.
+Two independent copies of the workspace are used in turn; a step scores,
+materialises and attends one copy and rebuilds the Mean-K index of the other,
+so each stage reads what the previous step wrote long before (the index a
+scorer reads was written one step earlier, with >3 GB of other traffic in
+between), as an incrementally maintained index would be.  Inputs are
+resident in HBM before the timed region.
+
+Prints ONE JSON line.  `value` is blocks scored per second over whole steps
+(32,768 blocks per step / step time).  Per-stage times come from HIP events
+recorded on the stream the library launches on; `roofline` reports the
+dominant stage against the 8 TB/s HBM peak using the algorithmic bytes of the
+method; `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "blocks scored/s + view decode-step latency (µs) at 1M-token workspace; % HBM peak"
+HBM_PEAK = 8.0e12   # B/s, MI355X HBM3E
+
+# HBM bytes per launch of each stage's main kernel at the 1M-token workspace,
+# from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB device
+# copy (fetch x2.0, write x1.0); the summary and commands are in
+# profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
+# taken on (sha256 over block_sparse_decode_amd/csrc/*); otherwise reported null.
+COUNTER_SOURCES_SHA = "83307936011cc99a57a266a5c758e0a3f8f27126b82930a684dee9798023e347"
+MEASURED_TRAFFIC = {"build_index": 2.216e9, "materialize": 2.163e9, "attend": 1.086e9,
+                    "score_select": 7.598e7}
+
+
+def kernel_sources_sha() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "block_sparse_decode_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def alg_bytes(cfg, n_blocks: int, view_tokens: int) -> dict:
+    """Algorithmic bytes per call: what the method must move."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    H, d = cfg.n_kv_heads, cfg.head_dim
+    return {
+        # read 32 keys, write one index row, per (block, KV head)
+        "build_index": (32 + 1) * H * d * b * n_blocks,
+        # read the index row of every (block, KV head), write A
+        "score_select": (H * d * b + H * 4) * n_blocks,
+        # read K and V of the selected tokens, write both into the view
+        "materialize": 4 * H * d * b * view_tokens,
+        # read K and V of the view once
+        "attend": 2 * H * d * b * view_tokens,
+    }
+
+
+def cpu_baseline(wl, heads=(0, 1, 2, 3)) -> dict:
+    """The oracle as it stands, timed on a sample: the whole path for a few of
+    the 8 KV heads of the workspace, scaled to the full workload."""
+    from oracle import kvmem_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = wl.cfg
+    ws = O.Workspace(wl.k_pool, wl.v_pool, wl.block_table, wl.n_tokens, cfg.dtype, cfg.n_q_heads,
+                     cfg.n_kv_heads, cfg.head_dim)
+    G = cfg.group
+    t0 = time.perf_counter()
+    qn = O.q_rmsnorm(O.decode(wl.q[0], cfg.dtype), wl.q_norm_w, cfg.eps)
+    n_tok = int(wl.n_tokens[0])
+    for h in heads:
+        idx = O.mean_k_index(ws, 0, h)
+        A = O.head_aggregate(qn[:, h * G:(h + 1) * G], idx)
+        lst, V = O.view_list(A, n_tok, cfg.k_select, cfg.n_recent)
+        kv, vv = O.materialize(ws, 0, h, lst, V, cfg.rope_theta)
+        O.attend(qn[:, h * G:(h + 1) * G], kv, vv, cfg.rope_theta)
+    dt = time.perf_counter() - t0
+    per_step = dt * cfg.n_kv_heads / len(heads)
+    nb = n_tok // 32
+    return {"value": nb / per_step, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole path (index, scores, selection, view, attention) for KV heads {list(heads)} of "
+                      f"{cfg.n_kv_heads} on the same workspace, {dt:.1f} s, scaled x{cfg.n_kv_heads / len(heads):.2f} "
+                      f"to one step; numpy float64, BLAS threads as 'cores', elementwise work single-threaded",
+            "seconds_per_step": per_step}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run one plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X here "
+              "(sharding by KV head is a design note, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace
+    from workloads import CONFIGS, make_workload
+
+    cfg = CONFIGS[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    wl = make_workload(cfg)
+    print(f"[bench] workload {cfg.name} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    wss = [DeviceWorkspace(wl, dev), DeviceWorkspace(wl, dev)]
+    stream = torch.cuda.current_stream(dev)
+    for w in wss:
+        w.build_index(stream)
+    torch.cuda.synchronize()
+
+    stages = ["score_select", "materialize", "attend", "build_index"]
+
+    def step(i, evs=None):
+        a, b = wss[i % 2], wss[(i + 1) % 2]
+        if evs is not None:
+            evs[0].record(stream)
+        a.score_select(stream)
+        if evs is not None:
+            evs[1].record(stream)
+        a.materialize(stream)
+        if evs is not None:
+            evs[2].record(stream)
+        a.attend(stream)
+        if evs is not None:
+            evs[3].record(stream)
+        b.build_index(stream)
+        if evs is not None:
+            evs[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    per = {s: [] for s in stages}
+    for ev in events:
+        for j, s in enumerate(stages):
+            per[s].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    mean = {s: float(np.mean(v)) for s, v in per.items()}
+
+    nb = int(wl.n_tokens[0]) // 32
+    V = int(wss[0].view_tokens[0])
+    ab = alg_bytes(cfg, nb, V)
+    stage_rep = {}
+    for s in stages:
+        gbs = ab[s] / mean[s] / 1e9
+        stage_rep[s] = {"us": round(mean[s] * 1e6, 2), "us_p10": round(float(np.percentile(per[s], 10)) * 1e6, 2),
+                        "us_p90": round(float(np.percentile(per[s], 90)) * 1e6, 2), "alg_bytes": int(ab[s]),
+                        "GB/s": round(gbs, 1), "hbm_frac": round(gbs * 1e9 / HBM_PEAK, 4)}
+    dom = max(stages, key=lambda s: mean[s])
+    ms_per_step = wall / args.steps * 1e3
+    res = {
+        "metric": METRIC,
+        "value": nb / (wall / args.steps),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_sessions} session, {int(wl.n_tokens[0]):,} tokens "
+                               f"({nb:,} blocks of 32), {cfg.n_q_heads} q heads / {cfg.n_kv_heads} KV heads, "
+                               f"d={cfg.head_dim}, {cfg.dtype}, top-{cfg.k_select} + {cfg.n_recent} recent blocks "
+                               f"-> {V:,}-token view, T={cfg.T}",
+                   "blocks": nb, "view_tokens": V, "query_tokens": cfg.T},
+        "decode_step_latency_us": stage_rep["attend"]["us"],
+        "blocks_scored_per_s_score_select": nb / mean["score_select"],
+        "stages": stage_rep,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ab[dom] / mean[dom] / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(ab[dom] / mean[dom] / HBM_PEAK, 4),
+                     "traffic": (MEASURED_TRAFFIC.get(dom) if args.workload == "c3"
+                                 and kernel_sources_sha() == COUNTER_SOURCES_SHA else None)},
+    }
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

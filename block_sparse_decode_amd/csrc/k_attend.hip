@@ -31,6 +31,7 @@ namespace kvmem {
 namespace {
 
 constexpr float kLog2eRsqrtD = 0.12751743074480953f;   // log2(e) / sqrt(128)
+constexpr int kQprepMaxT = 32;                          // query tokens per step in the bf16 path
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
@@ -39,15 +40,185 @@ __device__ __forceinline__ void split_hi_lo(float y, uint32_t &hi, uint32_t &lo)
   lo = f32_to_bf16(y - __uint_as_float(hi << 16));
 }
 
+// Query operands of the matrix-core products, prepared once per (session, KV
+// head): q~ (RMSNorm, weight), RoPE at V + t, scaled by log2(e)/sqrt(d), split
+// into bf16 hi + lo, stored in the B-operand lane layout
+// qop[s][h][nt][c*2 + {hi,lo}][lane] (uint4 = 8 bf16).  Lane (qq, col) holds row
+// 16*nt + col; its chunk c holds dims 32c + 8qq .. +7, so the RoPE partner of a
+// dim (+-64) sits in chunk c ^ 2 of the same lane.
 template <int NT>
-__global__ __launch_bounds__(256) void k_attend_bf16(const uint16_t *__restrict__ q, const float *__restrict__ qw,
-                                                     float eps, const uint16_t *__restrict__ kview,
+__global__ __launch_bounds__(64) void k_attend_qprep(const uint16_t *__restrict__ q, const float *__restrict__ qw,
+                                                     float eps, uint4 *__restrict__ qop, SessI32 view_tok, int s0,
+                                                     AttendGeom g, double theta) {
+  __shared__ float cs_tab[kQprepMaxT][kD / 2][2];
+  const int sl = blockIdx.y;
+  const int s = s0 + sl;
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int qq = lane >> 4;
+  const int col = lane & 15;
+  const int V = view_tok.v[sl];
+  // (cos, sin) of every (query token, frequency) once: lane = frequency index
+  {
+    const double inv_freq = rope_inv_freq(lane, theta);
+    const int n_t = (g.rows + g.G - 1) / g.G;
+    for (int t = 0; t < n_t; ++t) rope_cos_sin((double)(V + t), inv_freq, cs_tab[t][lane][0], cs_tab[t][lane][1]);
+  }
+  __syncthreads();
+  uint4 *dst = qop + ((size_t)(s * g.Hkv + h) * NT) * 8 * 64;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = nt * 16 + col;
+    const bool valid = r < g.rows;
+    const int t = valid ? r / g.G : 0;
+    const int gg = valid ? r % g.G : 0;
+    float x[4][8];                                    // [chunk c][j] = dim 32c + 8qq + j
+    if (valid) {
+      const uint16_t *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + 8 * qq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(src + 32 * c);
+        const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[c][2 * k] = bf16_lo(e[k]);
+          x[c][2 * k + 1] = bf16_hi(e[k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[c][j] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += x[c][j] * x[c][j];
+    ss += shfl_xor_f(ss, 16);
+    ss += shfl_xor_f(ss, 32);
+    const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[c][j] = x[c][j] * rs * qw[32 * c + 8 * qq + j];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        uint32_t h2[2], l2[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int ip = 32 * (c & 1) + 8 * qq + j + k;          // pair index (dim mod 64)
+          const float cs = cs_tab[t][ip][0], sn = cs_tab[t][ip][1];
+          const float xo = x[c][j + k], xp = x[c ^ 2][j + k];
+          const float y = (c < 2 ? xo * cs - xp * sn : xo * cs + xp * sn) * kLog2eRsqrtD;
+          split_hi_lo(valid ? y : 0.f, h2[k], l2[k]);
+        }
+        hw[j / 2] = h2[0] | (h2[1] << 16);
+        lw[j / 2] = l2[0] | (l2[1] << 16);
+      }
+      dst[((size_t)nt * 8 + 2 * c) * 64 + lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      dst[((size_t)nt * 8 + 2 * c + 1) * 64 + lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+  }
+}
+
+// K and V operands of one 32-token view block for lane (qq, col).  Chunk c of
+// the K operand holds dims 32c + 8qq .. +7 of token 16tt + col, so the four
+// lane groups of one load instruction read one contiguous 64-byte run per row.
+struct KVTile {
+  uint4 k[2][4];
+  uint4 v[8];
+};
+
+__device__ __forceinline__ void load_kv_tile(KVTile &t, const uint16_t *kbase, const uint16_t *vbase, int tb,
+                                             int qq, int col) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      t.k[tt][c] = load_nt16(kbase + (size_t)(tb + 16 * tt + col) * kD + 32 * c + 8 * qq);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) t.v[dt] = load_nt16(vbase + ((size_t)(tb >> 5) * kD + 16 * dt + col) * kBT + 8 * qq);
+}
+
+// One 32-token block: S^T = K Q^T, online softmax, O^T += V^T P^T.
+template <int NT>
+__device__ __forceinline__ void attend_tile(const KVTile &t, const bf16x8 (&qhi)[NT][4], const bf16x8 (&qlo)[NT][4],
+                                            floatx4 (&o)[NT][8], float (&mrun)[NT], float (&lrun)[NT], int tb, int V,
+                                            int qq) {
+  floatx4 sc[2][NT];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[tt][c]), qhi[nt][c], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[tt][c]), qlo[nt][c], a, 0, 0, 0);
+      }
+      sc[tt][nt] = a;
+    }
+  if (tb + kBT > V) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tb + 16 * tt + 4 * qq + i >= V)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sc[tt][nt][i] = -INFINITY;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float bm = fmaxf(fmaxf(fmaxf(sc[0][nt][0], sc[0][nt][1]), fmaxf(sc[0][nt][2], sc[0][nt][3])),
+                     fmaxf(fmaxf(sc[1][nt][0], sc[1][nt][1]), fmaxf(sc[1][nt][2], sc[1][nt][3])));
+    bm = fmaxf(bm, shfl_xor_f(bm, 16));
+    bm = fmaxf(bm, shfl_xor_f(bm, 32));
+    const float mn = fmaxf(mrun[nt], bm);
+    const float alpha = exp2f(mrun[nt] - mn);
+    mrun[nt] = mn;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2f(sc[0][nt][i] - mn);
+      p[4 + i] = exp2f(sc[1][nt][i] - mn);
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) psum += p[i];
+    lrun[nt] = lrun[nt] * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t h0, l0, h1, l1;
+      split_hi_lo(p[2 * k], h0, l0);
+      split_hi_lo(p[2 * k + 1], h1, l1);
+      ph[k] = h0 | (h1 << 16);
+      pl[k] = l0 | (l1 << 16);
+    }
+    const bf16x8 phi = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8 plo = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.v[dt]), phi, o[nt][dt], 0, 0, 0);
+      o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.v[dt]), plo, o[nt][dt], 0, 0, 0);
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void k_attend_bf16(const uint4 *__restrict__ qop, const uint16_t *__restrict__ kview,
                                                      const uint16_t *__restrict__ vview, float *__restrict__ part_o,
                                                      float2 *__restrict__ part_ml, float *__restrict__ out,
-                                                     SessI32 view_tok, int s0, AttendGeom g, double theta) {
+                                                     SessI32 view_tok, int s0, AttendGeom g) {
   constexpr int RP = 16 * NT;
   constexpr int kPitch = kD + 4;
-  __shared__ double inv_freq[kD / 2];
   __shared__ float sm[4][RP];
   __shared__ float sls[4][RP];
   __shared__ float so[4][RP * kPitch];
@@ -66,69 +237,24 @@ __global__ __launch_bounds__(256) void k_attend_bf16(const uint16_t *__restrict_
   const int wave = tid >> 6;
   const int qq = lane >> 4;
   const int col = lane & 15;
-  if (tid < kD / 2) inv_freq[tid] = rope_inv_freq(tid, theta);
-  __syncthreads();
+  const size_t head = (size_t)s * g.Hkv + h;
 
-  // ---- queries: RMSNorm, RoPE at V + t, log2(e)/sqrt(d), hi/lo bf16 split ----
   bf16x8 qhi[NT][4], qlo[NT][4];
+  {
+    const uint4 *src = qop + head * NT * 8 * 64;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = nt * 16 + col;
-    const bool valid = r < g.rows;
-    const int t = valid ? r / g.G : 0;
-    const int gg = valid ? r % g.G : 0;
-    float x[32];
-    if (valid) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(
-          q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + 32 * qq);
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 w = src[c];
-        const uint32_t e[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[8 * c + 2 * k] = bf16_lo(e[k]);
-          x[8 * c + 2 * k + 1] = bf16_hi(e[k]);
-        }
+        qhi[nt][c] = as_bf16x8(src[((size_t)nt * 8 + 2 * c) * 64 + lane]);
+        qlo[nt][c] = as_bf16x8(src[((size_t)nt * 8 + 2 * c + 1) * 64 + lane]);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = 0.f;
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) ss += x[e] * x[e];
-    ss += shfl_xor_f(ss, 16);
-    ss += shfl_xor_f(ss, 32);
-    const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-#pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = x[e] * rs * qw[32 * qq + e];
-    float px[32];
-#pragma unroll
-    for (int e = 0; e < 32; ++e) px[e] = shfl_xor_f(x[e], 32);   // RoPE partner: dim +- 64
-    const double pos = (double)(V + t);
-    uint32_t hw[16], lw[16];
-#pragma unroll
-    for (int e = 0; e < 32; e += 2) {
-      uint32_t h2[2], l2[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        float c, sn;
-        rope_cos_sin(pos, inv_freq[(32 * qq + e + k) & 63], c, sn);
-        const float y = (qq < 2 ? (x[e + k] * c - px[e + k] * sn) : (x[e + k] * c + px[e + k] * sn)) * kLog2eRsqrtD;
-        split_hi_lo(valid ? y : 0.f, h2[k], l2[k]);
-      }
-      hw[e / 2] = h2[0] | (h2[1] << 16);
-      lw[e / 2] = l2[0] | (l2[1] << 16);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      qhi[nt][c] = as_bf16x8(make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]));
-      qlo[nt][c] = as_bf16x8(make_uint4(lw[4 * c], lw[4 * c + 1], lw[4 * c + 2], lw[4 * c + 3]));
-    }
+    // Complete these loads here: otherwise the wait-count insertion treats them as
+    // still outstanding inside the streaming loop and waits for the prefetched
+    // tile before every block.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
-  // ---- stream this wavefront's blocks ----
   floatx4 o[NT][8];
   float mrun[NT], lrun[NT];
 #pragma unroll
@@ -138,82 +264,21 @@ __global__ __launch_bounds__(256) void k_attend_bf16(const uint16_t *__restrict_
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  const size_t head = (size_t)s * g.Hkv + h;
   const uint16_t *kbase = kview + head * (size_t)g.max_view * kD;
   const uint16_t *vbase = vview + head * (size_t)g.max_view * kD;
+  // One 32-token tile at a time: load, then compute.  (Holding a second tile in
+  // flight per wavefront measured markedly slower on this part: the stream
+  // runs best with each wavefront walking its run one tile deep.)
   const int tok0 = start + wave * g.tpw;
   const int tok1 = min(V, tok0 + g.tpw);
   for (int tb = tok0; tb < tok1; tb += kBT) {
-    uint4 kr[2][4], vr[8];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        kr[tt][c] = *reinterpret_cast<const uint4 *>(kbase + (size_t)(tb + 16 * tt + col) * kD + 32 * qq + 8 * c);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      vr[dt] = *reinterpret_cast<const uint4 *>(vbase + ((size_t)(tb >> 5) * kD + 16 * dt + col) * kBT + 8 * qq);
-
-    floatx4 sc[2][NT];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        floatx4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[tt][c]), qhi[nt][c], a, 0, 0, 0);
-          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[tt][c]), qlo[nt][c], a, 0, 0, 0);
-        }
-        sc[tt][nt] = a;
-      }
-    if (tb + kBT > V) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tb + 16 * tt + 4 * qq + i >= V)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) sc[tt][nt][i] = -INFINITY;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float bm = fmaxf(fmaxf(fmaxf(sc[0][nt][0], sc[0][nt][1]), fmaxf(sc[0][nt][2], sc[0][nt][3])),
-                       fmaxf(fmaxf(sc[1][nt][0], sc[1][nt][1]), fmaxf(sc[1][nt][2], sc[1][nt][3])));
-      bm = fmaxf(bm, shfl_xor_f(bm, 16));
-      bm = fmaxf(bm, shfl_xor_f(bm, 32));
-      const float mn = fmaxf(mrun[nt], bm);
-      const float alpha = exp2f(mrun[nt] - mn);
-      mrun[nt] = mn;
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = exp2f(sc[0][nt][i] - mn);
-        p[4 + i] = exp2f(sc[1][nt][i] - mn);
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) psum += p[i];
-      lrun[nt] = lrun[nt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[nt][dt] *= alpha;
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t h0, l0, h1, l1;
-        split_hi_lo(p[2 * k], h0, l0);
-        split_hi_lo(p[2 * k + 1], h1, l1);
-        ph[k] = h0 | (h1 << 16);
-        pl[k] = l0 | (l1 << 16);
-      }
-      const bf16x8 phi = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
-      const bf16x8 plo = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), phi, o[nt][dt], 0, 0, 0);
-        o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), plo, o[nt][dt], 0, 0, 0);
-      }
-    }
+    KVTile t;
+    load_kv_tile(t, kbase, vbase, tb, qq, col);
+    // keep all 16 K and V loads of the tile together at its start (the
+    // scheduler would otherwise sink the V loads below the first product and
+    // expose a second memory latency per tile)
+    __builtin_amdgcn_sched_barrier(0);
+    attend_tile<NT>(t, qhi, qlo, o, mrun, lrun, tb, V, qq);
   }
 
   // ---- merge the 4 wavefronts (log-sum-exp) ----
@@ -378,56 +443,93 @@ __global__ __launch_bounds__(256) void k_attend_f32(const float *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// merge of the splits (fixed order -> deterministic)
+// merge of the splits (fixed order -> deterministic): one workgroup per
+// (session, KV head, query row); 8 groups of 32 threads each take every 8th
+// split for 4 dimensions, then the groups are added in order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kD) void k_attend_combine(const float *__restrict__ part_o,
-                                                       const float2 *__restrict__ part_ml, float *__restrict__ out,
-                                                       SessI32 view_tok, int s0, AttendGeom g) {
+__device__ __forceinline__ float block_reduce_256(float v, float *red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float o = shfl_xor_f(v, m);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float r = is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict__ part_o,
+                                                        const float2 *__restrict__ part_ml, float *__restrict__ out,
+                                                        SessI32 view_tok, int s0, AttendGeom g) {
+  __shared__ float red[4];
+  __shared__ float4 acc_s[8][32];
   const int sl = blockIdx.z;
   const int s = s0 + sl;
   const int h = blockIdx.y;
   const int row = blockIdx.x;
-  const int dim = threadIdx.x;
+  const int tid = threadIdx.x;
   const int V = view_tok.v[sl];
   const int split_tok = 4 * g.tpw;
   const int n = (V + split_tok - 1) / split_tok;
   if (n == 1) return;                     // written by the attention kernel itself
   const int t = row / g.G, gg = row % g.G;
-  float *dst = out + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + dim;
+  float *dst = out + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
   if (n == 0) {
-    *dst = 0.f;
+    if (tid < kD) dst[tid] = 0.f;
     return;
   }
   const size_t head = (size_t)s * g.Hkv + h;
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, part_ml[(head * g.max_splits + i) * g.rows + row].x);
-  float num = 0.f, den = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const size_t pidx = (head * g.max_splits + i) * g.rows + row;
-    const float2 ml = part_ml[pidx];
-    const float f = exp2f(ml.x - M);
-    num += f * part_o[pidx * kD + dim];
-    den += f * ml.y;
+  const size_t base = head * g.max_splits * g.rows + row;     // + i * rows
+  float m = -INFINITY;
+  for (int i = tid; i < n; i += 256) m = fmaxf(m, part_ml[base + (size_t)i * g.rows].x);
+  const float M = block_reduce_256(m, red, true);
+  float d = 0.f;
+  for (int i = tid; i < n; i += 256) {
+    const float2 ml = part_ml[base + (size_t)i * g.rows];
+    d += exp2f(ml.x - M) * ml.y;
   }
-  *dst = num / den;
+  const float den = block_reduce_256(d, red, false);
+  const int sg = tid >> 5, q4 = tid & 31;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = sg; i < n; i += 8) {
+    const size_t pidx = base + (size_t)i * g.rows;
+    const float w = exp2f(part_ml[pidx].x - M);
+    const float4 v = reinterpret_cast<const float4 *>(part_o + pidx * kD)[q4];
+    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+  }
+  acc_s[sg][q4] = acc;
+  __syncthreads();
+  if (tid < 32) {
+    float4 r = acc_s[0][tid];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      const float4 v = acc_s[j][tid];
+      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+    }
+    const float inv = 1.0f / den;
+    reinterpret_cast<float4 *>(dst)[tid] = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+  }
 }
 
 }  // namespace
 
 int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view) {
-  // Aim for >= 2048 workgroups (8 per CU) at the largest view; 32..512 tokens
+  // Aim for >= 2048 workgroups (8 per CU) at the largest view; 32..256 tokens
   // per wavefront.
   const long work = (long)max_view * n_sessions * Hkv;
   long tpw_blocks = (work + 2048L * 4 * kBT - 1) / (2048L * 4 * kBT);
   if (tpw_blocks < 1) tpw_blocks = 1;
-  if (tpw_blocks > 16) tpw_blocks = 16;
+  if (tpw_blocks > 8) tpw_blocks = 8;
   return (int)tpw_blocks * kBT;
 }
 
 int attend_max_splits(int max_view, int tpw) { return (max_view + 4 * tpw - 1) / (4 * tpw); }
 
 hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
-                         const void *v_view, float *part_o, float2 *part_ml, float *out,
+                         const void *v_view, float *part_o, float2 *part_ml, uint4 *qop, float *out,
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
                          hipStream_t st) {
   int max_v = 0;
@@ -439,19 +541,21 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
       hipLaunchKernelGGL(k_attend_f32, grid, dim3(256), 0, st, (const float *)q, qw, eps, (const float *)k_view,
                          (const float *)v_view, part_o, part_ml, out, view_tok, s0, g, theta);
     } else if (g.rows <= 16) {
-      hipLaunchKernelGGL(k_attend_bf16<1>, grid, dim3(256), 0, st, (const uint16_t *)q, qw, eps,
-                         (const uint16_t *)k_view, (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g,
-                         theta);
+      hipLaunchKernelGGL(k_attend_qprep<1>, dim3(g.Hkv, n_sess), dim3(64), 0, st, (const uint16_t *)q, qw, eps, qop,
+                         view_tok, s0, g, theta);
+      hipLaunchKernelGGL(k_attend_bf16<1>, grid, dim3(256), 0, st, (const uint4 *)qop, (const uint16_t *)k_view,
+                         (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g);
     } else {
-      hipLaunchKernelGGL(k_attend_bf16<2>, grid, dim3(256), 0, st, (const uint16_t *)q, qw, eps,
-                         (const uint16_t *)k_view, (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g,
-                         theta);
+      hipLaunchKernelGGL(k_attend_qprep<2>, dim3(g.Hkv, n_sess), dim3(64), 0, st, (const uint16_t *)q, qw, eps, qop,
+                         view_tok, s0, g, theta);
+      hipLaunchKernelGGL(k_attend_bf16<2>, grid, dim3(256), 0, st, (const uint4 *)qop, (const uint16_t *)k_view,
+                         (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   dim3 cgrid((unsigned)g.rows, (unsigned)g.Hkv, (unsigned)n_sess);
-  hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(kD), 0, st, part_o, part_ml, out, view_tok, s0, g);
+  hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
   return hipGetLastError();
 }
 

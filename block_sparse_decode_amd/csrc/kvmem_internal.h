@@ -15,8 +15,8 @@ hipError_t launch_build_index(int bf16, const void *k_pool, const int32_t *table
                               int Hkv, int max_blocks, int n_pages, hipStream_t st);
 
 // --- scoring ------------------------------------------------------------------
-constexpr int kScoreChunk = 256;     // index rows per scoring workgroup
-constexpr int kAggChunk = 1024;      // blocks per aggregation workgroup
+constexpr int kScoreChunk = 128;     // index rows per scoring work item
+constexpr int kAggChunk = 256;       // blocks per aggregation workgroup (one per thread)
 
 struct ScoreGeom {
   int Tq, Hq, Hkv, G, max_blocks, n_chunks;
@@ -51,7 +51,7 @@ int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view);
 int attend_max_splits(int max_view, int tpw);
 
 hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
-                         const void *v_view, float *part_o, float2 *part_ml, float *out,
+                         const void *v_view, float *part_o, float2 *part_ml, uint4 *qop, float *out,
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
                          hipStream_t st);
 

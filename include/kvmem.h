@@ -26,7 +26,8 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Pointers are DEVICE pointers owned by the caller unless the name ends in
- *    _host.  The library allocates nothing and keeps no state between calls.
+ *    _host.  The library allocates nothing and keeps no state between calls
+ *    (it only caches the device's compute-unit count to size its grids).
  *  - Every call validates its arguments on the host first; on any invalid
  *    argument it returns an error status and enqueues nothing.  Otherwise it
  *    enqueues its kernels on `stream` (a hipStream_t; NULL = the default
@@ -40,7 +41,7 @@
  *    applies to the K/V pools, the index, the queries and the view.
  *  - Calls on the same stream are ordered; concurrent calls on different
  *    streams that write the same buffers race.  The library itself is
- *    thread-safe (no global state).
+ *    thread-safe (its only cached value is a device property).
  */
 #ifndef KVMEM_H_
 #define KVMEM_H_
