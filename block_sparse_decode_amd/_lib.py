@@ -21,6 +21,7 @@ KVMEM_F32, KVMEM_BF16 = 0, 1
 KVMEM_DEVERR_PAGE, KVMEM_DEVERR_BLOCK = 1, 2
 
 EXPORTED = [
+    "kvmem_index_bytes",
     "kvmem_build_index",
     "kvmem_score_select_scratch_bytes",
     "kvmem_score_select",
@@ -61,6 +62,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with `python -m block_sparse_decode_amd.build`")
     lib = ctypes.CDLL(p)
+    lib.kvmem_index_bytes.argtypes = [POINTER(Geom), c_int32, c_int32]
+    lib.kvmem_index_bytes.restype = c_size_t
     lib.kvmem_build_index.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p]
     lib.kvmem_build_index.restype = c_int32
     lib.kvmem_score_select_scratch_bytes.argtypes = [POINTER(Geom), c_int32, c_int32, c_int32]
@@ -131,6 +134,10 @@ def make_workspace(k_pool, v_pool, block_table, n_tokens_host: np.ndarray, dev_e
 
 
 # --- the four entry points (same names as the C ABI) ------------------------
+
+def kvmem_index_bytes(geom: Geom, n_sessions: int, max_blocks: int) -> int:
+    return int(load().kvmem_index_bytes(ctypes.byref(geom), n_sessions, max_blocks))
+
 
 def kvmem_build_index(geom: Geom, ws: Workspace, index, stream=None, check: bool = True) -> int:
     st = load().kvmem_build_index(ctypes.byref(geom), ctypes.byref(ws), _p(index), _stream(stream))

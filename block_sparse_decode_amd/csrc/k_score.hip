@@ -6,320 +6,450 @@
 // '2026-09-08 validation correction': averaging GQA heads before the softmax was
 // the withdrawn bug).
 //
-// k_score_gemv: a memory-bound GEMV on the vector ALUs.  LPR lanes share one
-// 256-byte index row, each lane holding DPL = 128/LPR of its dimensions and the
-// matching slice of all LPR query rows in registers, so every index element is
-// loaded once and feeds LPR FMAs.  The LPR partial sums are then combined with a
-// DPP reduce-scatter: lane p keeps its partials in a lane-specific row order
-// (row = register ^ x(p)), chosen so that at every step each lane adds the
-// partner's register that holds the same row -- log2(LPR) fused add+DPP moves and
-// no selects.  After the last step lane p owns the full score of row x(p).
-// Scores go through LDS to coalesced stores; per (row, chunk) the kernel also
-// writes the chunk's max and sum of exp, so the softmax needs no second pass over
-// the index.
-//
-// k_aggregate: merges the chunk statistics into each row's max and normaliser,
-// then A[b] = sum_rows exp(s[row][b] - M_row) / Z_row, summed in row order.
+// k_score_qprep: the normalised, weighted query rows q~/sqrt(d) in fp32.
+// k_score_gemv:  a memory-bound GEMV on the vector ALUs, one index row per lane
+//                (details at the kernel).
+// k_aggregate:   merges the softmax statistics into each row's max and
+//                normaliser, then A[b] = sum_rows exp(s[row][b] - M_row) / Z_row,
+//                summed in row order.
 #include "kvmem_internal.h"
 
 namespace kvmem {
 
 namespace {
 
-// Reduce-scatter schedule for LPR lanes per index row.  Step i exchanges with
-// lane p ^ mask_i (DPP pattern) and keeps registers [0, LPR >> (i+1)).  x(p) is
-// the linear map over the bits of p with x(p) ^ x(p ^ mask_i) = LPR >> (i+1).
-template <int LPR>
-struct RS;
-
-template <>
-struct RS<4> {  // masks 2, 1
-  static __device__ __forceinline__ int x(int p) { return p & 3; }
-  template <int N>
-  static __device__ __forceinline__ void reduce(float (&a)[N]) {
-    a[0] += dpp_f32<kDppXor2>(a[2]);
-    a[1] += dpp_f32<kDppXor2>(a[3]);
-    a[0] += dpp_f32<kDppXor1>(a[1]);
-  }
-};
-
-template <>
-struct RS<8> {  // masks 7, 2, 1
-  static __device__ __forceinline__ int x(int p) {
-    return (p & 1) ^ (p & 2) ^ ((p & 4) ? 7 : 0);
-  }
-  template <int N>
-  static __device__ __forceinline__ void reduce(float (&a)[N]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] += dpp_f32<kDppMirror8>(a[k + 4]);
-    a[0] += dpp_f32<kDppXor2>(a[2]);
-    a[1] += dpp_f32<kDppXor2>(a[3]);
-    a[0] += dpp_f32<kDppXor1>(a[1]);
-  }
-};
-
-template <>
-struct RS<16> {  // masks 15, 7, 2, 1
-  static __device__ __forceinline__ int x(int p) {
-    return (p & 1) ^ (p & 2) ^ ((p & 4) ? 7 : 0) ^ ((p & 8) ? 12 : 0);
-  }
-  template <int N>
-  static __device__ __forceinline__ void reduce(float (&a)[N]) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) a[k] += dpp_f32<kDppMirror16>(a[k + 8]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] += dpp_f32<kDppMirror8>(a[k + 4]);
-    a[0] += dpp_f32<kDppXor2>(a[2]);
-    a[1] += dpp_f32<kDppXor2>(a[3]);
-    a[0] += dpp_f32<kDppXor1>(a[1]);
-  }
-};
-
-template <typename T, int N>
-struct LoadRow;
-
-template <int N>
-struct LoadRow<uint16_t, N> {  // N bf16 (N multiple of 8) -> fp32
-  static __device__ __forceinline__ void load(const uint16_t *p, float (&v)[N]) {
-#pragma unroll
-    for (int c = 0; c < N / 8; ++c) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(p + 8 * c);
-      const uint32_t e[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[8 * c + 2 * k] = bf16_lo(e[k]);
-        v[8 * c + 2 * k + 1] = bf16_hi(e[k]);
-      }
-    }
-  }
-};
-
-template <int N>
-struct LoadRow<float, N> {  // N fp32 (N multiple of 4)
-  static __device__ __forceinline__ void load(const float *p, float (&v)[N]) {
-#pragma unroll
-    for (int c = 0; c < N / 4; ++c) {
-      const float4 w = reinterpret_cast<const float4 *>(p)[c];
-      v[4 * c] = w.x; v[4 * c + 1] = w.y; v[4 * c + 2] = w.z; v[4 * c + 3] = w.w;
-    }
-  }
-};
-
 __device__ __forceinline__ float load_elem(const uint16_t *p) { return bf16_lo(*p); }
 __device__ __forceinline__ float load_elem(const float *p) { return *p; }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
-  return v;
+// q~ rows of every (session, query token, query head), normalised, weighted and
+// scaled by 1/sqrt(d), in fp32, in the order the scorer reads them: dimension
+// 16m + i of a row is stored at element 8i + m of the row (i < 16, m < 8), so a
+// lane that needs dimensions i, 16 + i, ..., 112 + i reads 32 contiguous bytes.
+// One wavefront per row.
+template <typename T>
+__global__ __launch_bounds__(64) void k_score_qprep(const T *__restrict__ q, const float *__restrict__ qw, float eps,
+                                                    float *__restrict__ qn) {
+  const size_t row = blockIdx.x;                       // (s, t, g) flattened
+  const int lane = threadIdx.x;
+  const T *src = q + row * kD;
+  const float x0 = load_elem(src + lane), x1 = load_elem(src + 64 + lane);
+  const float ss = wave_sum_dpp(x0 * x0 + x1 * x1);
+  const float rs = (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * 0.08838834764831845f;   // 1/sqrt(128)
+  // dimension lane = 16m + i with m = lane / 16; dimension 64 + lane has m + 4
+  qn[row * kD + (lane & 15) * 8 + (lane >> 4)] = x0 * rs * qw[lane];
+  qn[row * kD + (lane & 15) * 8 + (lane >> 4) + 4] = x1 * rs * qw[64 + lane];
 }
 
-// q~ = w * q / sqrt(mean(q^2) + eps), pre-scaled by 1/sqrt(d), for rows
-// [r0, r0 + NR) of KV head h, into LDS.  Rows past n_rows are zero.
-template <typename T, int NR>
-__device__ __forceinline__ void norm_rows_to_lds(float (*qs)[kD], const T *q, const float *qw, float eps,
-                                                 int s, int h, int r0, int n_rows, int Tq, int Hq, int G) {
-  const int lane16 = threadIdx.x & 15;
-  for (int rr = threadIdx.x >> 4; rr < NR; rr += blockDim.x >> 4) {
-    const int r = r0 + rr;
-    float x[8];
-    float ss = 0.f;
-    if (r < n_rows) {
-      const int t = r / G, g = r % G;
-      const T *src = q + (((size_t)s * Tq + t) * Hq + (size_t)h * G + g) * kD + lane16 * 8;
+// One lane's index row inside a tile, as 16-byte words (16 for bf16, 32 for
+// fp32).  Word w of the 64 rows of a tile is contiguous, so load w of a
+// wavefront is a single coalesced 1 KiB access.
+template <typename T>
+struct RowRaw {
+  static constexpr int kWords = kD * (int)sizeof(T) / 16;
+  uint4 w[kWords];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_row(RowRaw<T> &r, const T *tile, int lane) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        x[k] = load_elem(src + k);
-        ss += x[k] * x[k];
-      }
-    } else {
+  for (int i = 0; i < RowRaw<T>::kWords; ++i) r.w[i] = load_nt16(tile + (i * kIdxTile + lane) * (16 / (int)sizeof(T)));
+}
+
+// 8 consecutive elements of the row, starting at element 8c, as fp32.
+__device__ __forceinline__ void row8(const RowRaw<uint16_t> &r, int c, float (&v)[8]) {
+  const uint32_t e[4] = {r.w[c].x, r.w[c].y, r.w[c].z, r.w[c].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] = 0.f;
-    }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) ss += shfl_xor_f(ss, m);
-    const float rs = (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * 0.08838834764831845f;  // 1/sqrt(128)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qs[rr][lane16 * 8 + k] = (r < n_rows) ? x[k] * rs * qw[lane16 * 8 + k] : 0.f;
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = bf16_lo(e[k]);
+    v[2 * k + 1] = bf16_hi(e[k]);
   }
 }
+__device__ __forceinline__ void row8(const RowRaw<float> &r, int c, float (&v)[8]) {
+  const uint4 a = r.w[2 * c], b = r.w[2 * c + 1];
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
 
-// Raw 16-byte words of the index slice one lane reads for one work item.
-template <typename T, int LPR>
-struct ItemRaw {
-  static constexpr int kWords = (kD / LPR) * (int)sizeof(T) / 16;   // per index row and lane
-  static constexpr int kRows = kScoreChunk / (4 * (64 / LPR));         // rows per lane per item
-  uint4 w[kRows][kWords];
+// acc[r] += sum_j q_j(r) * kv[j] for the eight query values q_j(r) = lane
+// 8H + j of each 16-lane row of q[r] (the query rows are replicated in the four
+// rows of the wavefront, so every lane sees the same q_j(r)).  Each FMA takes
+// q_j(r) through a DPP row broadcast (row_newbcast) of its first operand: the
+// query stays in registers and costs no extra instruction.  The FMAs are
+// ordered dimension-major, so consecutive ones update different rows and do
+// not wait on each other.  A DPP read of q needs two wait states after a VALU
+// write of it, which the compiler does not insert for inline asm, hence the
+// leading s_nop.  (Generated: one block per row count and half.)
+template <int R>
+struct Fma8;
+template <>
+struct Fma8<4> {
+  static __device__ __forceinline__ void fma8_lo(float (&acc)[4], const float (&q)[4], const float (&kv)[8]) {
+    asm("s_nop 1\n\t"
+          "v_fmac_f32_dpp %0, %4, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(kv[0]), "v"(kv[1]), "v"(kv[2]), "v"(kv[3]), "v"(kv[4]), "v"(kv[5]), "v"(kv[6]), "v"(kv[7]));
+  }
+
+  static __device__ __forceinline__ void fma8_hi(float (&acc)[4], const float (&q)[4], const float (&kv)[8]) {
+    asm("s_nop 1\n\t"
+          "v_fmac_f32_dpp %0, %4, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %12 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %12 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %12 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %12 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %14 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %14 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %14 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %14 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %4, %15 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %5, %15 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %6, %15 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %7, %15 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(kv[0]), "v"(kv[1]), "v"(kv[2]), "v"(kv[3]), "v"(kv[4]), "v"(kv[5]), "v"(kv[6]), "v"(kv[7]));
+  }
+};
+template <>
+struct Fma8<8> {
+  static __device__ __forceinline__ void fma8_lo(float (&acc)[8], const float (&q)[8], const float (&kv)[8]) {
+    asm("s_nop 1\n\t"
+          "v_fmac_f32_dpp %0, %8, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %19 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %20 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %21 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %22 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7])
+        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(kv[0]), "v"(kv[1]), "v"(kv[2]), "v"(kv[3]), "v"(kv[4]), "v"(kv[5]), "v"(kv[6]), "v"(kv[7]));
+  }
+
+  static __device__ __forceinline__ void fma8_hi(float (&acc)[8], const float (&q)[8], const float (&kv)[8]) {
+    asm("s_nop 1\n\t"
+          "v_fmac_f32_dpp %0, %8, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %0, %8, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %1, %9, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %2, %10, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %3, %11, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %4, %12, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %5, %13, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %6, %14, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+          "v_fmac_f32_dpp %7, %15, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7])
+        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]), "v"(kv[0]), "v"(kv[1]), "v"(kv[2]), "v"(kv[3]), "v"(kv[4]), "v"(kv[5]), "v"(kv[6]), "v"(kv[7]));
+  }
 };
 
-// Work item = (session, KV head x row group, chunk of kScoreChunk blocks).
+// Work item = (session, row group, KV head, index tile), tile fastest.  The
+// key (session, row group, head) = item / ntl = (sl * n_rg + rg) * Hkv + h.
 struct Item {
-  int sl, h, r0, b0, nb, key;
-  bool valid;
+  int sl, h, r0, t, nb, key;
 };
-
-__device__ __forceinline__ Item decode_item(int item, int n_chunks_launch, int ny, int Hkv, int rows_per_group,
-                                            int n_rows, const SessI32 &n_blocks) {
+__device__ __forceinline__ Item decode_item(int item, const ScoreSplit &sp, int Hkv, const SessI32 &n_blocks) {
   Item it;
-  const int chunk = item % n_chunks_launch;
-  it.key = item / n_chunks_launch;
-  const int y = it.key % ny;
-  it.sl = it.key / ny;
-  it.h = y % Hkv;
-  it.r0 = (y / Hkv) * rows_per_group;
+  it.t = item % sp.ntl;
+  it.key = item / sp.ntl;
+  it.h = it.key % Hkv;
+  const int y = it.key / Hkv;
+  it.r0 = (y % sp.n_rg) * sp.rpg;
+  it.sl = y / sp.n_rg;
   it.nb = n_blocks.v[it.sl];
-  it.b0 = chunk * kScoreChunk;
-  it.valid = it.b0 < it.nb && it.r0 < n_rows;
   return it;
 }
 
-template <typename T, int LPR>
-__device__ __forceinline__ void load_item(ItemRaw<T, LPR> &raw, const T *index, const Item &it, int s0,
-                                          const ScoreGeom &g, int lane, int wave) {
-  constexpr int DPL = kD / LPR;
-  constexpr int RPW = 64 / LPR;
-  constexpr int RPI = 4 * RPW;
-  const T *base = index + ((size_t)((s0 + it.sl) * g.Hkv + it.h) * g.max_blocks) * kD + (lane % LPR) * DPL;
-#pragma unroll
-  for (int r = 0; r < ItemRaw<T, LPR>::kRows; ++r) {
-    // rows past the history re-read the last row (their scores are never
-    // stored): no branch around the loads, so they all stay in flight
-    const int b = min(it.b0 + r * RPI + wave * RPW + lane / LPR, it.nb - 1);
-    const T *src = base + (size_t)b * kD;
-#pragma unroll
-    for (int w = 0; w < ItemRaw<T, LPR>::kWords; ++w) raw.w[r][w] = load_nt16(src + w * (16 / sizeof(T)));
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void unpack_row(const uint4 *w, float (&v)[N], uint16_t) {
-#pragma unroll
-  for (int c = 0; c < N / 8; ++c) {
-    const uint32_t e[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[8 * c + 2 * k] = bf16_lo(e[k]);
-      v[8 * c + 2 * k + 1] = bf16_hi(e[k]);
-    }
-  }
-}
-template <int N>
-__device__ __forceinline__ void unpack_row(const uint4 *w, float (&v)[N], float) {
-#pragma unroll
-  for (int c = 0; c < N / 4; ++c) {
-    v[4 * c] = __uint_as_float(w[c].x);
-    v[4 * c + 1] = __uint_as_float(w[c].y);
-    v[4 * c + 2] = __uint_as_float(w[c].z);
-    v[4 * c + 3] = __uint_as_float(w[c].w);
-  }
-}
-
-// Persistent over work items, chunk fastest.  Workgroup b takes the contiguous
-// items [b * per, (b + 1) * per), so the grid is one round of resident
-// workgroups and the query rows are normalised again only when (session, head)
-// changes.  The next item's index rows are requested before the current item's
-// scores are written out.
-template <typename T, int LPR>
-__global__ __launch_bounds__(256) void k_score_gemv(const T *__restrict__ index, const T *__restrict__ q,
-                                                    const float *__restrict__ qw, float eps,
-                                                    float *__restrict__ scores, float2 *__restrict__ part,
-                                                    SessI32 n_blocks, int s0, ScoreGeom g, int n_sess,
-                                                    int n_rg, int n_chunks_launch, int per) {
-  constexpr int ROWS = LPR;
-  constexpr int DPL = kD / LPR;
-  constexpr int RPW = 64 / LPR;
-  constexpr int RPI = 4 * RPW;
-  constexpr int NIT = kScoreChunk / RPI;
-  __shared__ float qs[ROWS][kD];
-  __shared__ float st[ROWS][kScoreChunk];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int p = lane % LPR;
-  const int xl = RS<LPR>::x(p);
+// Block-scoring GEMV, one index row per lane.  A wavefront owns a contiguous
+// range of items; for each it streams the 64 rows of one index tile (lane b
+// holds row b whole, 16 coalesced loads), and accumulates the R query rows of
+// its group against it.  The query rows sit in registers, replicated per
+// 16-lane row, and reach the FMAs through DPP broadcasts: no LDS, no scalar
+// loads and no cross-lane reduction in the inner loop.
+//
+// Softmax statistics: each lane keeps a running max m and sum l of exp(s - m)
+// per query row over the blocks it has scored in the current key; when the key
+// changes (and at the end) the wavefront reduces them once and writes one
+// (max, sum) slot per row.  Scores are stored coalesced per row.
+//
+// bf16: the next item's rows are requested before the current item is
+// computed (two register buffers).  fp32 rows are twice as large and are
+// loaded one item at a time.
+template <typename T, int R>
+__global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, const float *__restrict__ qn,
+                                                   float *__restrict__ scores, float2 *__restrict__ part,
+                                                   SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
+  constexpr bool kPrefetch = sizeof(T) == 2;
+  const int lane = threadIdx.x;
   const int n_rows = g.Tq * g.G;
-  const int ny = g.Hkv * n_rg;
-  const int total = n_sess * ny * n_chunks_launch;
-  const int item0 = blockIdx.x * per;
-  const int item1 = min(total, item0 + per);
-  int loaded = -1;
-  float qr[ROWS][DPL];
-  ItemRaw<T, LPR> raw;
+  const int total = sp.n_sess * g.Hkv * sp.n_rg * sp.ntl;
+  const int i0 = blockIdx.x * sp.per;                   // < total (grid = ceil(total / per))
+  const int i1 = min(total, i0 + sp.per);
 
-  int item = item0;
-  Item cur;
-  for (; item < item1; ++item) {                       // first valid item
-    cur = decode_item(item, n_chunks_launch, ny, g.Hkv, ROWS, n_rows, n_blocks);
-    if (cur.valid) break;
-  }
-  if (item < item1) load_item<T, LPR>(raw, index, cur, s0, g, lane, wave);
+  int key, key_r0;
+  float qv[R][kD / 16];                                 // q[r][16 m + lane % 16] (see fma8)
+  size_t row_id[R];                                     // (s, t, query head) rows of the key
+  float m[R], l[R];
 
-  while (item < item1) {
-    const int s = s0 + cur.sl;
-    if (cur.key != loaded) {
-      __syncthreads();
-      norm_rows_to_lds<T, ROWS>(qs, q, qw, eps, s, cur.h, cur.r0, n_rows, g.Tq, g.Hq, g.G);
-      __syncthreads();
+  auto tile_of = [&](int item) {
+    const Item it = decode_item(item, sp, g.Hkv, n_blocks);
+    return index + ((size_t)((s0 + it.sl) * g.Hkv + it.h) * g.n_tiles + it.t) * (size_t)(kIdxTile * kD);
+  };
+
+  // one (max, sum) slot per row of the current key
+  auto flush = [&]() {
+    const int slot = blockIdx.x - (key * sp.ntl) / sp.per;
 #pragma unroll
-      for (int k = 0; k < ROWS; ++k)
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) qr[k][j] = qs[k ^ xl][p * DPL + j];
-      loaded = cur.key;
+    for (int r = 0; r < R; ++r) {
+      if (key_r0 + r >= n_rows) break;
+      const float M = wave_max_dpp(m[r]);
+      const float x = m[r] == -INFINITY ? 0.f : l[r] * __expf(m[r] - M);
+      const float L = wave_sum_dpp(x);
+      if (lane == 0) part[row_id[r] * g.slot_stride + slot] = make_float2(M, L);
     }
+  };
+
+  // query rows and fresh statistics for a new key
+  auto start_key = [&](const Item &c) {
+    key = c.key;
+    key_r0 = c.r0;
+    const int s = s0 + c.sl;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      float kv[DPL];
-      unpack_row(raw.w[it], kv, T());
-      float acc[ROWS];
+    for (int r = 0; r < R; ++r) {
+      // rows past n_rows read row r0 (their results are not stored)
+      const int row = c.r0 + r < n_rows ? c.r0 + r : c.r0;
+      const int t = row / g.G, gg = row % g.G;
+      row_id[r] = ((size_t)s * g.Tq + t) * g.Hq + (size_t)c.h * g.G + gg;
+      const float4 *qp = reinterpret_cast<const float4 *>(qn + row_id[r] * kD + (lane & 15) * 8);
+      const float4 qa = qp[0], qb = qp[1];
+      qv[r][0] = qa.x; qv[r][1] = qa.y; qv[r][2] = qa.z; qv[r][3] = qa.w;
+      qv[r][4] = qb.x; qv[r][5] = qb.y; qv[r][6] = qb.z; qv[r][7] = qb.w;
+      m[r] = -INFINITY;
+      l[r] = 0.f;
+    }
+  };
+
+  auto compute = [&](const RowRaw<T> &raw, int item) {
+    const Item c = decode_item(item, sp, g.Hkv, n_blocks);
+    if (c.key != key) {
+      flush();
+      start_key(c);
+    }
+    if (c.t * kIdxTile >= c.nb) return;                 // tile past this session's history
+
+    float acc[R];
 #pragma unroll
-      for (int k = 0; k < ROWS; ++k) {
-        float a = 0.f;
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) a = fmaf(qr[k][j], kv[j], a);
-        acc[k] = a;
+    for (int cc = 0; cc < kD / 8; cc += 2) {
+      float q[R], kv[8];
+#pragma unroll
+      for (int r = 0; r < R; ++r) q[r] = qv[r][cc / 2];
+      row8(raw, cc, kv);
+      Fma8<R>::fma8_lo(acc, q, kv);
+      row8(raw, cc + 1, kv);
+      Fma8<R>::fma8_hi(acc, q, kv);
+    }
+
+    const int b = c.t * kIdxTile + lane;
+    if (b < c.nb) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (c.r0 + r >= n_rows) break;
+        scores[row_id[r] * g.max_blocks + b] = acc[r];
+        // running softmax statistics: one exp per score
+        const float d = acc[r] - m[r];
+        const float e = __expf(-fabsf(d));
+        l[r] = d > 0.f ? fmaf(l[r], e, 1.f) : l[r] + e;
+        m[r] = fmaxf(m[r], acc[r]);
       }
-      RS<LPR>::reduce(acc);
-      st[xl][it * RPI + wave * RPW + lane / LPR] = acc[0];
     }
-    // next valid item: request its rows now
-    int nxt = item + 1;
-    Item next = cur;
-    for (; nxt < item1; ++nxt) {
-      next = decode_item(nxt, n_chunks_launch, ny, g.Hkv, ROWS, n_rows, n_blocks);
-      if (next.valid) break;
-    }
-    if (nxt < item1) load_item<T, LPR>(raw, index, next, s0, g, lane, wave);
-    __syncthreads();
+  };
 
-    const int nvalid = min(kScoreChunk, cur.nb - cur.b0);
-    const int chunk = cur.b0 / kScoreChunk;
-    for (int rr = wave; rr < ROWS; rr += 4) {
-      const int r = cur.r0 + rr;
-      if (r >= n_rows) break;
-      const int t = r / g.G, gg = r % g.G;
-      const size_t row_id = ((size_t)s * g.Tq + t) * g.Hq + (size_t)cur.h * g.G + gg;
-      float *dst = scores + row_id * g.max_blocks + cur.b0;
-      float m = -INFINITY;
-      for (int j = lane; j < nvalid; j += 64) {
-        const float v = st[rr][j];
-        dst[j] = v;
-        m = fmaxf(m, v);
-      }
-      m = wave_max(m);
-      float l = 0.f;
-      for (int j = lane; j < nvalid; j += 64) l += expf(st[rr][j] - m);
-      l = wave_sum(l);
-      if (lane == 0) part[row_id * g.n_chunks + chunk] = make_float2(m, l);
+  // The first key's query loads go out before any tile load: vector loads
+  // complete in order, so loading them later would make the first FMA wait for
+  // every tile load in flight.
+  start_key(decode_item(i0, sp, g.Hkv, n_blocks));
+  if constexpr (kPrefetch) {
+    RowRaw<T> ra, rb;
+    load_row(ra, tile_of(i0), lane);
+    int it = i0;
+    while (true) {
+      // the last item re-reads its own tile (an L2 hit) so the loads stay unconditional
+      load_row(rb, tile_of(min(it + 1, i1 - 1)), lane);
+      compute(ra, it);
+      if (++it >= i1) break;
+      load_row(ra, tile_of(min(it + 1, i1 - 1)), lane);
+      compute(rb, it);
+      if (++it >= i1) break;
     }
-    __syncthreads();
-    item = nxt;
-    cur = next;
+  } else {
+    RowRaw<T> ra;
+    for (int it = i0; it < i1; ++it) {
+      load_row(ra, tile_of(it), lane);
+      compute(ra, it);
+    }
   }
+  flush();
 }
 
 __device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
@@ -331,12 +461,12 @@ __device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
 constexpr int kAggRowsPerPass = 64;
 
 // One workgroup per (session, KV head, 256 blocks).  Each wavefront first
-// merges the chunk statistics of some rows into the row's max M and 1/Z
-// (log-sum-exp merge), then every thread owns one block and sums
-// exp(s - M) / Z over the rows in a fixed order.
+// merges the statistics slots of some rows into the row's max M and 1/Z
+// (log-sum-exp merge, slots in order), then every thread owns one block and
+// sums exp(s - M) / Z over the rows in a fixed order.
 __global__ __launch_bounds__(256) void k_aggregate(const float *__restrict__ scores,
                                                    const float2 *__restrict__ part, float *__restrict__ A,
-                                                   SessI32 n_blocks, int s0, ScoreGeom g) {
+                                                   SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
   __shared__ float sM[kAggRowsPerPass];
   __shared__ float sInvZ[kAggRowsPerPass];
   const int sl = blockIdx.z;
@@ -348,7 +478,6 @@ __global__ __launch_bounds__(256) void k_aggregate(const float *__restrict__ sco
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n_rows = g.Tq * g.G;
-  const int nch = (nb + kScoreChunk - 1) / kScoreChunk;
   const int b = b0 + threadIdx.x;
   const bool valid = b < nb;
   float acc = 0.f;
@@ -359,8 +488,12 @@ __global__ __launch_bounds__(256) void k_aggregate(const float *__restrict__ sco
       const int r = rb + rr;
       const int t = r / g.G, gg = r % g.G;
       const size_t row_id = ((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg;
+      // the wavefronts that met this row's key, in order
+      const int key = (sl * sp.n_rg + r / sp.rpg) * g.Hkv + h;
+      const int w0 = (key * sp.ntl) / sp.per;
+      const int n_slots = ((key + 1) * sp.ntl - 1) / sp.per - w0 + 1;
       float2 ml = make_float2(-INFINITY, 0.f);
-      for (int c = lane; c < nch; c += 64) ml = merge_ml(ml, part[row_id * g.n_chunks + c]);
+      for (int c = lane; c < n_slots; c += 64) ml = merge_ml(ml, part[row_id * g.slot_stride + c]);
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) {
         float2 o;
@@ -387,60 +520,75 @@ __global__ __launch_bounds__(256) void k_aggregate(const float *__restrict__ sco
   if (valid) A[((size_t)s * g.Hkv + h) * g.max_blocks + b] = acc;
 }
 
-template <typename T, int LPR>
-hipError_t launch_gemv_lpr(const void *index, const void *q, const float *qw, float eps, float *scores,
-                           float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
-                           int max_nb, hipStream_t st) {
-  const int n_rows = g.Tq * g.G;
-  const int n_rg = (n_rows + LPR - 1) / LPR;
-  const int n_chunks = (max_nb + kScoreChunk - 1) / kScoreChunk;
-  const long total = (long)n_sess * g.Hkv * n_rg * n_chunks;
-  static int res = 0;                                   // resident workgroups (device property)
-  if (res == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
+// Wavefronts per SIMD that the scorer's grid aims for: each wavefront then
+// gets several items, so its next tile streams in while it computes.
+constexpr int kScoreWavesPerSimd = 2;
+
+template <typename T, int R>
+hipError_t launch_gemv_r(const void *index, const float *qn, float *scores, float2 *part,
+                         const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g, int max_nb,
+                         ScoreSplit *split, hipStream_t st) {
+  static int cus = 0;                                   // compute units (device property)
+  if (cus == 0) {
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_score_gemv<T, LPR>, 256, 0) != hipSuccess) per_cu = 1;
-    res = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
   }
-  const long grid0 = total < res ? total : res;
-  const int per = (int)((total + grid0 - 1) / grid0);
-  const int grid = (int)((total + per - 1) / per);
-  hipLaunchKernelGGL((k_score_gemv<T, LPR>), dim3(grid), dim3(256), 0, st, (const T *)index, (const T *)q, qw, eps,
-                     scores, part, n_blocks, s0, g, n_sess, n_rg, n_chunks, per);
+  ScoreSplit sp;
+  sp.n_sess = n_sess;
+  sp.rpg = R;
+  sp.n_rg = (g.Tq * g.G + R - 1) / R;
+  sp.ntl = idx_tiles(max_nb);
+  const long total = (long)n_sess * g.Hkv * sp.n_rg * sp.ntl;
+  const long target = (long)cus * 4 * kScoreWavesPerSimd;
+  sp.per = (int)((total + target - 1) / target);
+  const int grid = (int)((total + sp.per - 1) / sp.per);
+  *split = sp;
+  hipLaunchKernelGGL((k_score_gemv<T, R>), dim3(grid), dim3(64), 0, st, (const T *)index, qn, scores, part, n_blocks,
+                     s0, g, sp);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_gemv_t(const void *index, const void *q, const float *qw, float eps, float *scores,
+hipError_t launch_gemv_t(const void *index, const void *q, const float *qw, float eps, float *qn, float *scores,
                          float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
-                         hipStream_t st) {
+                         ScoreSplit *split, hipStream_t st) {
   int max_nb = 0;
   for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
+  split->n_sess = n_sess;
+  split->ntl = 0;
   if (max_nb == 0) return hipSuccess;
+  // normalised query rows of the sessions of this launch
+  const size_t row0 = (size_t)s0 * g.Tq * g.Hq;
+  hipLaunchKernelGGL(k_score_qprep<T>, dim3((unsigned)(n_sess * g.Tq * g.Hq)), dim3(64), 0, st,
+                     (const T *)q + row0 * kD, qw, eps, qn + row0 * kD);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int n_rows = g.Tq * g.G;
-  if (n_rows <= 4) return launch_gemv_lpr<T, 4>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, max_nb, st);
-  if (n_rows <= 8) return launch_gemv_lpr<T, 8>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, max_nb, st);
-  return launch_gemv_lpr<T, 16>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, max_nb, st);
+  if (n_rows <= 4)
+    return launch_gemv_r<T, 4>(index, qn, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
+  // more rows: groups of 8 rows, each re-reading the index rows
+  return launch_gemv_r<T, 8>(index, qn, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
 }
 
 }  // namespace
 
-hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps,
+hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *qn,
                              float *scores, float2 *part, const SessI32 &n_blocks, int s0, int n_sess,
-                             const ScoreGeom &g, hipStream_t st) {
-  return bf16 ? launch_gemv_t<uint16_t>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, st)
-              : launch_gemv_t<float>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, st);
+                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st) {
+  return bf16 ? launch_gemv_t<uint16_t>(index, q, qw, eps, qn, scores, part, n_blocks, s0, n_sess, g, split, st)
+              : launch_gemv_t<float>(index, q, qw, eps, qn, scores, part, n_blocks, s0, n_sess, g, split, st);
 }
 
 hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, const SessI32 &n_blocks,
-                            int s0, int n_sess, const ScoreGeom &g, hipStream_t st) {
+                            int s0, const ScoreGeom &g, const ScoreSplit &split, hipStream_t st) {
   int max_nb = 0;
-  for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
-  if (max_nb == 0) return hipSuccess;
-  dim3 grid((unsigned)((max_nb + kAggChunk - 1) / kAggChunk), (unsigned)g.Hkv, (unsigned)n_sess);
-  hipLaunchKernelGGL(k_aggregate, grid, dim3(256), 0, st, scores, part, A, n_blocks, s0, g);
+  for (int i = 0; i < split.n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
+  if (max_nb == 0 || split.ntl == 0) return hipSuccess;
+  dim3 grid((unsigned)((max_nb + kAggChunk - 1) / kAggChunk), (unsigned)g.Hkv, (unsigned)split.n_sess);
+  hipLaunchKernelGGL(k_aggregate, grid, dim3(256), 0, st, scores, part, A, n_blocks, s0, g, split);
   return hipGetLastError();
 }
 

@@ -50,16 +50,17 @@ Split recent_split(int n_tok, int n_recent) {
 
 // score_select scratch: per-head scores, per-(row, chunk) softmax statistics, A.
 struct ScoreScratch {
-  size_t scores, part, agg, total;
+  size_t scores, part, agg, qn, total;
 };
 ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   ScoreScratch r;
   const size_t rows = (size_t)S * T * g->n_q_heads;
-  const size_t n_chunks = ((size_t)max_blocks + kScoreChunk - 1) / kScoreChunk;
+  const size_t n_slots = (size_t)idx_tiles(max_blocks) + 1;   // softmax-statistics slots per row
   r.scores = 0;
   r.part = align_up(rows * max_blocks * sizeof(float));
-  r.agg = r.part + align_up(rows * n_chunks * sizeof(float2));
-  r.total = r.agg + align_up((size_t)S * g->n_kv_heads * max_blocks * sizeof(float));
+  r.agg = r.part + align_up(rows * n_slots * sizeof(float2));
+  r.qn = r.agg + align_up((size_t)S * g->n_kv_heads * max_blocks * sizeof(float));
+  r.total = r.qn + align_up(rows * kD * sizeof(float));   // normalised query rows
   return r;
 }
 
@@ -96,7 +97,13 @@ const char *kvmem_status_string(kvmem_status st) {
   return "unknown status";
 }
 
-int32_t kvmem_version(void) { return 100; }
+int32_t kvmem_version(void) { return 200; }
+
+size_t kvmem_index_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t max_blocks) {
+  if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || max_blocks <= 0) return 0;
+  const size_t elem = geom->kv_dtype == KVMEM_BF16 ? 2 : 4;
+  return (size_t)n_sessions * geom->n_kv_heads * idx_tiles(max_blocks) * kIdxTile * kD * elem;
+}
 
 kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws, void *index, void *stream) {
   kvmem_status st = check_geom(geom);
@@ -136,6 +143,11 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
   const int n_list = (int)n_list_l;
   if (n_list > 0 && !view_blocks) return KVMEM_E_ARG;
   const int S = ws->n_sessions;
+  // 32-bit indexing of the query rows and of the scoring work items
+  const long q_rows = (long)S * T * geom->n_q_heads;
+  const long n_rg = ((long)T * (geom->n_q_heads / geom->n_kv_heads) + 7) / 8;
+  if (q_rows * kD >= (1L << 31) || (long)S * geom->n_kv_heads * n_rg * idx_tiles(ws->max_blocks) >= (1L << 31))
+    return KVMEM_E_UNSUPPORTED;
   const ScoreScratch sc = score_scratch(geom, S, ws->max_blocks, T);
   if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
 
@@ -156,7 +168,8 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
   g.Hkv = geom->n_kv_heads;
   g.G = g.Hq / g.Hkv;
   g.max_blocks = ws->max_blocks;
-  g.n_chunks = (ws->max_blocks + kScoreChunk - 1) / kScoreChunk;
+  g.n_tiles = idx_tiles(ws->max_blocks);
+  g.slot_stride = g.n_tiles + 1;
   const int bf16 = geom->kv_dtype == KVMEM_BF16;
   const hipStream_t hs = (hipStream_t)stream;
 
@@ -174,10 +187,11 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
       tm.r_start.v[i] = sp.r_start;
       tm.n_all.v[i] = sp.n_all;
     }
-    if ((st = hip_status(launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, hs))) !=
-        KVMEM_OK)
+    ScoreSplit split;
+    if ((st = hip_status(launch_score_gemv(bf16, index, q, q_norm_w, eps, (float *)(base + sc.qn), scores, part, nb,
+                                           s0, n, g, &split, hs))) != KVMEM_OK)
       return st;
-    if ((st = hip_status(launch_aggregate(scores, part, A, nb, s0, n, g, hs))) != KVMEM_OK) return st;
+    if ((st = hip_status(launch_aggregate(scores, part, A, nb, s0, g, split, hs))) != KVMEM_OK) return st;
     if (n_list > 0 &&
         (st = hip_status(launch_topk(A, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
       return st;

@@ -111,6 +111,38 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppMirror8 = 0x141;    // row_half_mirror: lane i <-> 7 - i within 8
 constexpr int kDppMirror16 = 0x140;   // row_mirror: lane i <-> 15 - i within 16
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15: lane 15 of each row -> the next row
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31: lane 31 -> rows 2 and 3
+
+// DPP move that writes only the rows in ROW_MASK; other lanes get `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32_rows(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xf, false));
+}
+
+// Whole-wavefront sum / max on the DPP network (no LDS round trips): reduce
+// each 16-lane row (quad swaps, then the half-row and row mirrors), fold row 0
+// into row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1 into rows 2-3
+// (row_bcast:31).  Lane 63 ends with the total, returned to every lane.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppMirror8>(v);
+  v += dpp_f32<kDppMirror16>(v);
+  v += dpp_f32_rows<kDppBcast15, 0xa>(0.f, v);
+  v += dpp_f32_rows<kDppBcast31, 0xc>(0.f, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror8>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror16>(v));
+  v = fmaxf(v, dpp_f32_rows<kDppBcast15, 0xa>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32_rows<kDppBcast31, 0xc>(-INFINITY, v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 

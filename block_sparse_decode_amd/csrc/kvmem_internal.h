@@ -10,24 +10,43 @@
 namespace kvmem {
 
 // --- Mean-K index -----------------------------------------------------------
+// The index is stored in tiles of kIdxTile consecutive blocks of one (session,
+// KV head).  Inside a tile, 16-byte word w (elements [w*E, w*E + E) of a row,
+// E = 16 / sizeof(element)) of all kIdxTile rows is contiguous:
+//   element (row r, dim i) of a tile sits at ((i / E) * kIdxTile + r) * E + i % E.
+// A tile is kIdxTile * kD elements; (session s, head h) owns n_tiles tiles,
+// n_tiles = ceil(max_blocks / kIdxTile).
+constexpr int kIdxTile = 64;
+__host__ __device__ constexpr int idx_tiles(int max_blocks) { return (max_blocks + kIdxTile - 1) / kIdxTile; }
+
 hipError_t launch_build_index(int bf16, const void *k_pool, const int32_t *table, void *index,
                               int32_t *dev_err, const SessI32 &n_blocks, int s0, int n_sess,
                               int Hkv, int max_blocks, int n_pages, hipStream_t st);
 
 // --- scoring ------------------------------------------------------------------
-constexpr int kScoreChunk = 128;     // index rows per scoring work item
 constexpr int kAggChunk = 256;       // blocks per aggregation workgroup (one per thread)
 
 struct ScoreGeom {
-  int Tq, Hq, Hkv, G, max_blocks, n_chunks;
+  int Tq, Hq, Hkv, G, max_blocks;
+  int n_tiles;       // index tiles per (session, head)
+  int slot_stride;   // softmax-statistics slots per query row (n_tiles + 1)
 };
 
-hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps,
+// How one scoring launch split its work: items are (session, row group of
+// rpg query rows, KV head, index tile), tile fastest, and wavefront w owns
+// items [w * per, (w + 1) * per).  The softmax statistics of a (session, row
+// group, head) key are written by every wavefront whose range meets the key,
+// one slot each, in wavefront order.
+struct ScoreSplit {
+  int n_sess, rpg, n_rg, ntl, per;
+};
+
+hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *qn,
                              float *scores, float2 *part, const SessI32 &n_blocks, int s0, int n_sess,
-                             const ScoreGeom &g, hipStream_t st);
+                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st);
 
 hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, const SessI32 &n_blocks,
-                            int s0, int n_sess, const ScoreGeom &g, hipStream_t st);
+                            int s0, const ScoreGeom &g, const ScoreSplit &split, hipStream_t st);
 
 // --- selection ------------------------------------------------------------------
 struct TopkMeta {

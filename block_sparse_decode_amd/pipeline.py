@@ -40,6 +40,23 @@ def v_view_token_major(v_view: torch.Tensor) -> torch.Tensor:
     return x.reshape(S, H, nb * BLOCK, x.shape[-1])
 
 
+INDEX_TILE = 64
+
+
+def index_tile_shape(S: int, H: int, max_blocks: int, d: int, dtype: str) -> tuple:
+    """Shape of the tiled Mean-K index as documented in kvmem.h:
+    [S][H][tiles of 64 blocks][16-byte word][64 rows][elements per word]."""
+    E = 8 if dtype == "bf16" else 4
+    return (S, H, -(-max_blocks // INDEX_TILE), d // E, INDEX_TILE, E)
+
+
+def index_rows(index: torch.Tensor, max_blocks: int) -> torch.Tensor:
+    """Tiled index [S][H][NT][W][64][E] -> row-major [S][H][max_blocks][d]."""
+    S, H, NT, W, T, E = index.shape
+    x = index.permute(0, 1, 2, 4, 3, 5).reshape(S, H, NT * T, W * E)
+    return x[:, :, :max_blocks]
+
+
 class DeviceWorkspace:
     """Inputs of a workload on the GPU plus every buffer the four calls use."""
 
@@ -65,7 +82,10 @@ class DeviceWorkspace:
         self.geom = L.make_geom(cfg.n_q_heads, H, cfg.dtype, d)
         self.ws = L.make_workspace(self.k_pool, self.v_pool, self.block_table, self.n_tokens, self.dev_error)
 
-        self.index = torch.empty((S, H, self.max_blocks, d), dtype=self.tdtype, device=self.device)
+        shape = index_tile_shape(S, H, self.max_blocks, d, cfg.dtype)
+        assert int(np.prod(shape)) * (2 if cfg.dtype == "bf16" else 4) == \
+            L.kvmem_index_bytes(self.geom, S, self.max_blocks)
+        self.index = torch.empty(shape, dtype=self.tdtype, device=self.device)
         self.n_list = self.k_select + self.n_recent
         self.view_blocks = torch.empty((S, H, max(1, self.n_list)), dtype=torch.int32, device=self.device)
         self.view_tokens = np.zeros(S, np.int32)

@@ -107,13 +107,23 @@ typedef struct {
  * 32-token blocks, i.e. the mean of the block's pre-RoPE keys).
  *
  * For every session s, KV head h and complete block beta < n_tokens[s] / 32:
- *   index[s][h][beta][:] = round( (1/32) * sum_{u<32} K[page(s,beta)][h][u][:] )
+ *   row(s, h, beta) = round( (1/32) * sum_{u<32} K[page(s,beta)][h][u][:] )
  * The sum is accumulated in fp64 and rounded once (to nearest, ties to even)
  * to kv_dtype.  Rows for beta >= n_tokens[s] / 32 are not written.  v_pool
  * is not used and may be NULL.
  *
- * index : [n_sessions][Hkv][max_blocks][d] in kv_dtype.
+ * index : kvmem_index_bytes() bytes in kv_dtype, TILED: the rows of each
+ *         (s, h) are grouped in tiles of 64 consecutive blocks, and inside a
+ *         tile the 16-byte word w (elements [E*w, E*w + E) of a row, E = 8 for
+ *         bf16 and 4 for fp32) of all 64 rows is stored contiguously:
+ *           element i of row(s, h, beta) is at element offset
+ *             ((((s * Hkv + h) * NT + beta / 64) * (d / E) + i / E) * 64
+ *               + beta % 64) * E + i % E,        NT = ceil(max_blocks / 64).
+ *         (One load instruction of a 64-lane wavefront then reads one word of
+ *         64 rows as a single contiguous 1 KiB access, with every lane
+ *         holding its own row.)
  * ------------------------------------------------------------------------- */
+size_t kvmem_index_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t max_blocks);
 kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws,
                                void *index, void *stream);
 
@@ -132,6 +142,7 @@ kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws
  *   s[t][g][b] = <q~[t][g], index[h(g)][b]> / sqrt(d),  b < Nb       (fp32)
  *   p[t][g][b] = softmax over b < Nb of s[t][g][:]
  *   A[h][b]    = sum_t sum_{g in group h} p[t][g][b]
+ * with index rows read from the tiled layout of kvmem_build_index.
  * The k_eff candidates with the largest A (ties: lower block index) are
  * listed in ascending order, followed by the recent blocks ascending, then
  * -1 padding:

@@ -43,7 +43,7 @@ def test_exports_match_header(lib):
 def test_status_strings_and_version(lib):
     assert L.status_string(0) == "ok"
     assert "scratch" in L.status_string(3)
-    assert L.kvmem_version() >= 100
+    assert L.kvmem_version() >= 200
 
 
 def _geom(dtype="bf16", Hq=64, Hkv=8, d=128, bt=32):
@@ -63,6 +63,12 @@ def test_scratch_sizes(lib):
     assert a >= 64 * 32768 * 4 + 8 * 32768 * 4
     assert L.kvmem_score_select_scratch_bytes(g, 0, 32768, 1) == 0
     assert L.kvmem_score_select_scratch_bytes(_geom(d=64), 1, 32768, 1) == 0
+    # tiled index: whole tiles of 64 blocks per (session, KV head)
+    assert L.kvmem_index_bytes(g, 1, 32768) == 8 * 32768 * 128 * 2
+    assert L.kvmem_index_bytes(g, 3, 65) == 3 * 8 * 128 * 128 * 2
+    assert L.kvmem_index_bytes(_geom("f32", 4, 1), 2, 1) == 2 * 64 * 128 * 4
+    assert L.kvmem_index_bytes(g, 0, 64) == 0 and L.kvmem_index_bytes(g, 1, 0) == 0
+    assert L.kvmem_index_bytes(_geom(d=64), 1, 64) == 0
     b = L.kvmem_attend_scratch_bytes(g, 1, 1, 262144)
     assert b > 0 and b % 256 == 0
     assert L.kvmem_attend_scratch_bytes(g, 1, 1, 100) == 0          # not a multiple of 32

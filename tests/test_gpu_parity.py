@@ -38,7 +38,7 @@ def _bits_to_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
 
 
 def run_gpu(wl, scores=True):
-    from block_sparse_decode_amd.pipeline import DeviceWorkspace, v_view_token_major
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace, index_rows, v_view_token_major
     cfg = wl.cfg
     print(f"[gpu] {cfg.name} S={cfg.n_sessions} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} T={cfg.T} "
           f"N={list(wl.n_tokens)[:4]} k={cfg.k_select} R={cfg.n_recent}", flush=True)
@@ -51,7 +51,7 @@ def run_gpu(wl, scores=True):
     dw.materialize()
     dw.attend()
     torch.cuda.synchronize()
-    res = dict(dw=dw, index=_bits_to_f64(dw.index, cfg.dtype), agg=ag.cpu().numpy().astype(np.float64),
+    res = dict(dw=dw, index=_bits_to_f64(index_rows(dw.index, dw.max_blocks).contiguous(), cfg.dtype), agg=ag.cpu().numpy().astype(np.float64),
                scores=None if sc is None else sc.cpu().numpy().astype(np.float64),
                vb=dw.view_blocks.cpu().numpy(), vt=dw.view_tokens.copy(),
                kview=_bits_to_f64(dw.k_view, cfg.dtype),
