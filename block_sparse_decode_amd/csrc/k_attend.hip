@@ -35,10 +35,6 @@ constexpr int kQprepMaxT = 32;                          // query tokens per step
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-__device__ __forceinline__ void split_hi_lo(float y, uint32_t &hi, uint32_t &lo) {
-  hi = f32_to_bf16(y);
-  lo = f32_to_bf16(y - __uint_as_float(hi << 16));
-}
 
 // Query operands of the matrix-core products, prepared once per (session, KV
 // head): q~ (RMSNorm, weight), RoPE at V + t, scaled by log2(e)/sqrt(d), split

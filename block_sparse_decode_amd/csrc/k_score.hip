@@ -6,9 +6,8 @@
 // '2026-09-08 validation correction': averaging GQA heads before the softmax was
 // the withdrawn bug).
 //
-// k_score_qprep: the normalised, weighted query rows q~/sqrt(d) in fp32.
-// k_score_gemv:  a memory-bound GEMV on the vector ALUs, one index row per lane
-//                (details at the kernel).
+// k_score_gemv:  a GEMV on the vector ALUs, one index row per lane, for steps
+//                of at most 8 query rows per KV head (details at the kernel).
 // k_aggregate:   merges the softmax statistics into each row's max and
 //                normaliser, then A[b] = sum_rows exp(s[row][b] - M_row) / Z_row,
 //                summed in row order.
@@ -20,25 +19,6 @@ namespace {
 
 __device__ __forceinline__ float load_elem(const uint16_t *p) { return bf16_lo(*p); }
 __device__ __forceinline__ float load_elem(const float *p) { return *p; }
-
-// q~ rows of every (session, query token, query head), normalised, weighted and
-// scaled by 1/sqrt(d), in fp32, in the order the scorer reads them: dimension
-// 16m + i of a row is stored at element 8i + m of the row (i < 16, m < 8), so a
-// lane that needs dimensions i, 16 + i, ..., 112 + i reads 32 contiguous bytes.
-// One wavefront per row.
-template <typename T>
-__global__ __launch_bounds__(64) void k_score_qprep(const T *__restrict__ q, const float *__restrict__ qw, float eps,
-                                                    float *__restrict__ qn) {
-  const size_t row = blockIdx.x;                       // (s, t, g) flattened
-  const int lane = threadIdx.x;
-  const T *src = q + row * kD;
-  const float x0 = load_elem(src + lane), x1 = load_elem(src + 64 + lane);
-  const float ss = wave_sum_dpp(x0 * x0 + x1 * x1);
-  const float rs = (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * 0.08838834764831845f;   // 1/sqrt(128)
-  // dimension lane = 16m + i with m = lane / 16; dimension 64 + lane has m + 4
-  qn[row * kD + (lane & 15) * 8 + (lane >> 4)] = x0 * rs * qw[lane];
-  qn[row * kD + (lane & 15) * 8 + (lane >> 4) + 4] = x1 * rs * qw[64 + lane];
-}
 
 // One lane's index row inside a tile, as 16-byte words (16 for bf16, 32 for
 // fp32).  Word w of the 64 rows of a tile is contiguous, so load w of a
@@ -302,23 +282,6 @@ struct Fma8<8> {
   }
 };
 
-// Work item = (session, row group, KV head, index tile), tile fastest.  The
-// key (session, row group, head) = item / ntl = (sl * n_rg + rg) * Hkv + h.
-struct Item {
-  int sl, h, r0, t, nb, key;
-};
-__device__ __forceinline__ Item decode_item(int item, const ScoreSplit &sp, int Hkv, const SessI32 &n_blocks) {
-  Item it;
-  it.t = item % sp.ntl;
-  it.key = item / sp.ntl;
-  it.h = it.key % Hkv;
-  const int y = it.key / Hkv;
-  it.r0 = (y % sp.n_rg) * sp.rpg;
-  it.sl = y / sp.n_rg;
-  it.nb = n_blocks.v[it.sl];
-  return it;
-}
-
 // Block-scoring GEMV, one index row per lane.  A wavefront owns a contiguous
 // range of items; for each it streams the 64 rows of one index tile (lane b
 // holds row b whole, 16 coalesced loads), and accumulates the R query rows of
@@ -327,15 +290,16 @@ __device__ __forceinline__ Item decode_item(int item, const ScoreSplit &sp, int 
 // loads and no cross-lane reduction in the inner loop.
 //
 // Softmax statistics: each lane keeps a running max m and sum l of exp(s - m)
-// per query row over the blocks it has scored in the current key; when the key
-// changes (and at the end) the wavefront reduces them once and writes one
-// (max, sum) slot per row.  Scores are stored coalesced per row.
+// per query row over the blocks it has scored in the current key; at the end
+// of each key the wavefront reduces them once and writes one (max, sum) slot
+// per row.  Scores are stored coalesced per row.
 //
 // bf16: the next item's rows are requested before the current item is
 // computed (two register buffers).  fp32 rows are twice as large and are
 // loaded one item at a time.
 template <typename T, int R>
-__global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, const float *__restrict__ qn,
+__global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, const T *__restrict__ q,
+                                                   const float *__restrict__ qw, float eps,
                                                    float *__restrict__ scores, float2 *__restrict__ part,
                                                    SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
   constexpr bool kPrefetch = sizeof(T) == 2;
@@ -351,13 +315,13 @@ __global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, 
   float m[R], l[R];
 
   auto tile_of = [&](int item) {
-    const Item it = decode_item(item, sp, g.Hkv, n_blocks);
+    const ScoreItem it = decode_score_item(item, sp, g.Hkv, n_blocks);
     return index + ((size_t)((s0 + it.sl) * g.Hkv + it.h) * g.n_tiles + it.t) * (size_t)(kIdxTile * kD);
   };
 
   // one (max, sum) slot per row of the current key
   auto flush = [&]() {
-    const int slot = blockIdx.x - (key * sp.ntl) / sp.per;
+    const int slot = blockIdx.x - score_slot0(key, sp);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (key_r0 + r >= n_rows) break;
@@ -368,32 +332,45 @@ __global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, 
     }
   };
 
-  // query rows and fresh statistics for a new key
-  auto start_key = [&](const Item &c) {
+  // Query registers and fresh statistics for a new key: lane l holds
+  // q~[r][16 mm + l % 16] / sqrt(d) (l % 16 = the lane's place in its 16-lane
+  // row, so every row of the wavefront carries the whole query row).  The mean
+  // square of a query row is summed over the 16 lanes of a row with DPP.
+  auto start_key = [&](const ScoreItem &c) {
     key = c.key;
     key_r0 = c.r0;
     const int s = s0 + c.sl;
+    const int i = lane & 15;
+    float w[kD / 16];
+#pragma unroll
+    for (int mm = 0; mm < kD / 16; ++mm) w[mm] = qw[16 * mm + i];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       // rows past n_rows read row r0 (their results are not stored)
       const int row = c.r0 + r < n_rows ? c.r0 + r : c.r0;
       const int t = row / g.G, gg = row % g.G;
       row_id[r] = ((size_t)s * g.Tq + t) * g.Hq + (size_t)c.h * g.G + gg;
-      const float4 *qp = reinterpret_cast<const float4 *>(qn + row_id[r] * kD + (lane & 15) * 8);
-      const float4 qa = qp[0], qb = qp[1];
-      qv[r][0] = qa.x; qv[r][1] = qa.y; qv[r][2] = qa.z; qv[r][3] = qa.w;
-      qv[r][4] = qb.x; qv[r][5] = qb.y; qv[r][6] = qb.z; qv[r][7] = qb.w;
+      const T *src = q + row_id[r] * kD + i;
+      float ss = 0.f;
+#pragma unroll
+      for (int mm = 0; mm < kD / 16; ++mm) {
+        qv[r][mm] = load_elem(src + 16 * mm);
+        ss += qv[r][mm] * qv[r][mm];
+      }
+      ss += dpp_f32<kDppXor1>(ss);
+      ss += dpp_f32<kDppXor2>(ss);
+      ss += dpp_f32<kDppMirror8>(ss);
+      ss += dpp_f32<kDppMirror16>(ss);
+      const float rs = (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * 0.08838834764831845f;   // 1/sqrt(128)
+#pragma unroll
+      for (int mm = 0; mm < kD / 16; ++mm) qv[r][mm] *= rs * w[mm];
       m[r] = -INFINITY;
       l[r] = 0.f;
     }
   };
 
   auto compute = [&](const RowRaw<T> &raw, int item) {
-    const Item c = decode_item(item, sp, g.Hkv, n_blocks);
-    if (c.key != key) {
-      flush();
-      start_key(c);
-    }
+    const ScoreItem c = decode_score_item(item, sp, g.Hkv, n_blocks);
     if (c.t * kIdxTile >= c.nb) return;                 // tile past this session's history
 
     float acc[R];
@@ -425,31 +402,34 @@ __global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, 
     }
   };
 
-  // The first key's query loads go out before any tile load: vector loads
-  // complete in order, so loading them later would make the first FMA wait for
-  // every tile load in flight.
-  start_key(decode_item(i0, sp, g.Hkv, n_blocks));
-  if constexpr (kPrefetch) {
-    RowRaw<T> ra, rb;
-    load_row(ra, tile_of(i0), lane);
-    int it = i0;
-    while (true) {
-      // the last item re-reads its own tile (an L2 hit) so the loads stay unconditional
-      load_row(rb, tile_of(min(it + 1, i1 - 1)), lane);
-      compute(ra, it);
-      if (++it >= i1) break;
-      load_row(ra, tile_of(min(it + 1, i1 - 1)), lane);
-      compute(rb, it);
-      if (++it >= i1) break;
-    }
-  } else {
-    RowRaw<T> ra;
-    for (int it = i0; it < i1; ++it) {
+  // One segment per key in the range: the key's query loads go out before its
+  // first tile load (vector loads complete in order), then the tiles stream.
+  // bf16 keeps one tile of look-ahead, and the last item re-reads its own tile
+  // (an L2 hit) so that the loads stay unconditional.
+  for (int it = i0; it < i1;) {
+    const ScoreItem c0 = decode_score_item(it, sp, g.Hkv, n_blocks);
+    const int end = min(i1, (c0.key + 1) * sp.ntl);
+    start_key(c0);
+    if constexpr (kPrefetch) {
+      RowRaw<T> ra, rb;
       load_row(ra, tile_of(it), lane);
-      compute(ra, it);
+      while (true) {
+        load_row(rb, tile_of(min(it + 1, end - 1)), lane);
+        compute(ra, it);
+        if (++it >= end) break;
+        load_row(ra, tile_of(min(it + 1, end - 1)), lane);
+        compute(rb, it);
+        if (++it >= end) break;
+      }
+    } else {
+      RowRaw<T> ra;
+      for (; it < end; ++it) {
+        load_row(ra, tile_of(it), lane);
+        compute(ra, it);
+      }
     }
+    flush();
   }
-  flush();
 }
 
 __device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
@@ -490,8 +470,7 @@ __global__ __launch_bounds__(256) void k_aggregate(const float *__restrict__ sco
       const size_t row_id = ((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg;
       // the wavefronts that met this row's key, in order
       const int key = (sl * sp.n_rg + r / sp.rpg) * g.Hkv + h;
-      const int w0 = (key * sp.ntl) / sp.per;
-      const int n_slots = ((key + 1) * sp.ntl - 1) / sp.per - w0 + 1;
+      const int n_slots = score_n_slots(key, sp);
       float2 ml = make_float2(-INFINITY, 0.f);
       for (int c = lane; c < n_slots; c += 64) ml = merge_ml(ml, part[row_id * g.slot_stride + c]);
 #pragma unroll
@@ -525,7 +504,7 @@ __global__ __launch_bounds__(256) void k_aggregate(const float *__restrict__ sco
 constexpr int kScoreWavesPerSimd = 2;
 
 template <typename T, int R>
-hipError_t launch_gemv_r(const void *index, const float *qn, float *scores, float2 *part,
+hipError_t launch_gemv_r(const void *index, const void *q, const float *qw, float eps, float *scores, float2 *part,
                          const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g, int max_nb,
                          ScoreSplit *split, hipStream_t st) {
   static int cus = 0;                                   // compute units (device property)
@@ -546,40 +525,34 @@ hipError_t launch_gemv_r(const void *index, const float *qn, float *scores, floa
   sp.per = (int)((total + target - 1) / target);
   const int grid = (int)((total + sp.per - 1) / sp.per);
   *split = sp;
-  hipLaunchKernelGGL((k_score_gemv<T, R>), dim3(grid), dim3(64), 0, st, (const T *)index, qn, scores, part, n_blocks,
-                     s0, g, sp);
+  hipLaunchKernelGGL((k_score_gemv<T, R>), dim3(grid), dim3(64), 0, st, (const T *)index, (const T *)q, qw, eps,
+                     scores, part, n_blocks, s0, g, sp);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_gemv_t(const void *index, const void *q, const float *qw, float eps, float *qn, float *scores,
-                         float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
-                         ScoreSplit *split, hipStream_t st) {
+hipError_t launch_gemv_t(const void *index, const void *q, const float *qw, float eps, float *scores, float2 *part,
+                         const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g, ScoreSplit *split,
+                         hipStream_t st) {
   int max_nb = 0;
   for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
   split->n_sess = n_sess;
   split->ntl = 0;
   if (max_nb == 0) return hipSuccess;
-  // normalised query rows of the sessions of this launch
-  const size_t row0 = (size_t)s0 * g.Tq * g.Hq;
-  hipLaunchKernelGGL(k_score_qprep<T>, dim3((unsigned)(n_sess * g.Tq * g.Hq)), dim3(64), 0, st,
-                     (const T *)q + row0 * kD, qw, eps, qn + row0 * kD);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int n_rows = g.Tq * g.G;
   if (n_rows <= 4)
-    return launch_gemv_r<T, 4>(index, qn, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
+    return launch_gemv_r<T, 4>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
   // more rows: groups of 8 rows, each re-reading the index rows
-  return launch_gemv_r<T, 8>(index, qn, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
+  return launch_gemv_r<T, 8>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
 }
 
 }  // namespace
 
-hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *qn,
-                             float *scores, float2 *part, const SessI32 &n_blocks, int s0, int n_sess,
-                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st) {
-  return bf16 ? launch_gemv_t<uint16_t>(index, q, qw, eps, qn, scores, part, n_blocks, s0, n_sess, g, split, st)
-              : launch_gemv_t<float>(index, q, qw, eps, qn, scores, part, n_blocks, s0, n_sess, g, split, st);
+hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *scores,
+                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
+                             ScoreSplit *split, hipStream_t st) {
+  return bf16 ? launch_gemv_t<uint16_t>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, split, st)
+              : launch_gemv_t<float>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, split, st);
 }
 
 hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, const SessI32 &n_blocks,

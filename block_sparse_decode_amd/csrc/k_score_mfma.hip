@@ -1,0 +1,251 @@
+// Block scoring on the matrix cores, for query chunks of several tokens.
+//
+// With T query tokens per step every KV head scores its blocks against T * G
+// query rows (the per-head softmax of the reproduction README,
+// '2026-09-08 validation correction', is taken per query token and head), so
+// scoring is a real dense contraction: S = index_tile (64 blocks x 128) * Q^T.
+// The index tile is the A operand of v_mfma_f32_16x16x32_bf16 as it sits in
+// HBM (bf16, exact); the normalised query rows q~/sqrt(d) (fp32) are split into
+// bf16 hi + lo parts and both are accumulated into the same fp32 result, which
+// keeps ~16 significant bits of the query, the same as an fp32 FMA product
+// with a bf16 index element would need.
+//
+// k_score_mfma: one wavefront per run of (row group, head, index tile) items;
+//               builds the query operands itself when a key starts, and
+//               writes the scores and per-row softmax statistics in the same
+//               form as the vector-ALU scorer, so the same aggregation kernel
+//               follows.
+#include "kvmem_internal.h"
+
+namespace kvmem {
+
+namespace {
+
+constexpr int kMfmaRowGroup = 32;   // query rows per pass over the index: two 16-column operand sets
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+__device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = bf16_lo(e[k]);
+    x[2 * k + 1] = bf16_hi(e[k]);
+  }
+}
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// The 16 A-operand words of a 64-block index tile: a.w[4m + c] is word
+// 4c + qq of block 16m + col (dims 32c + 8qq .. + 7), i.e. A rows = blocks
+// 16m .. 16m + 15 and k = dims 32c .. 32c + 31.  Each load reads four
+// contiguous 256-byte runs of the tiled index.
+struct TileA {
+  uint4 w[16];
+};
+__device__ __forceinline__ void load_tile_a(TileA &a, const uint16_t *tile, int lane) {
+  const int qq = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      a.w[4 * m + c] = load_nt16(tile + ((4 * c + qq) * kIdxTile + 16 * m + col) * 8);
+}
+
+// Scores of the T * G query rows of a row group against every index row, on
+// the matrix cores.  Work items and statistics slots are those of the
+// vector-ALU scorer (ScoreSplit, rows per group = 32).  Per item the wavefront
+// computes D[cs][m] = A(blocks 16m..) * B(rows 16cs..): lane (qq, col) holds
+// the scores of blocks 16m + 4qq + i, i < 4, for row 16cs + col.  Running
+// per-lane softmax statistics of its row are merged over the four lanes of a
+// row at the end of each key.  The next tile is requested before the current
+// one is multiplied (two register buffers).
+template <typename TQ>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_score_mfma(const uint16_t *__restrict__ index, const TQ *__restrict__ q,
+                                                   const float *__restrict__ qw, float eps,
+                                                   float *__restrict__ scores, float2 *__restrict__ part,
+                                                   SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
+  const int lane = threadIdx.x;
+  const int qq = lane >> 4, col = lane & 15;
+  const int n_rows = g.Tq * g.G;
+  const int total = sp.n_sess * g.Hkv * sp.n_rg * sp.ntl;
+  const int i0 = blockIdx.x * sp.per;                   // < total (grid = ceil(total / per))
+  const int i1 = min(total, i0 + sp.per);
+
+  int key, key_r0;
+  bf16x8 b[2][4][2];                                    // [cs][c][hi, lo]
+  size_t row_id[2];
+  bool row_ok[2];
+  float m[2], l[2];
+
+  auto tile_of = [&](int item) {
+    const ScoreItem it = decode_score_item(item, sp, g.Hkv, n_blocks);
+    return index + ((size_t)((s0 + it.sl) * g.Hkv + it.h) * g.n_tiles + it.t) * (size_t)(kIdxTile * kD);
+  };
+
+  auto flush = [&]() {
+    const int slot = blockIdx.x - score_slot0(key, sp);
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      float M = fmaxf(m[cs], shfl_xor_f(m[cs], 16));
+      M = fmaxf(M, shfl_xor_f(M, 32));
+      float x = m[cs] == -INFINITY ? 0.f : l[cs] * __expf(m[cs] - M);
+      x += shfl_xor_f(x, 16);
+      x += shfl_xor_f(x, 32);
+      if (qq == 0 && row_ok[cs]) part[row_id[cs] * g.slot_stride + slot] = make_float2(M, x);
+    }
+  };
+
+  // B operands of a key: lane (qq, col) holds dims 32k + 8qq .. + 7 of query
+  // row r0 + 16cs + col, as q~/sqrt(d) split into bf16 hi and lo (rows past
+  // T * G are zero).  The row's mean square is summed over the four lanes
+  // that share it.
+  auto start_key = [&](const ScoreItem &c) {
+    key = c.key;
+    key_r0 = c.r0;
+    const int s = s0 + c.sl;
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      const int r = c.r0 + cs * 16 + col;
+      row_ok[cs] = r < n_rows;
+      const int rr = row_ok[cs] ? r : 0;
+      row_id[cs] = ((size_t)s * g.Tq + rr / g.G) * g.Hq + (size_t)c.h * g.G + rr % g.G;
+      m[cs] = -INFINITY;
+      l[cs] = 0.f;
+      // two passes over the lane's 32 dims keep few registers live: the
+      // mean square, then the weighted, scaled, split values
+      const TQ *src = q + row_id[cs] * kD + 8 * qq;
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float x[8];
+        load8(src + 32 * k, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+      }
+      ss += shfl_xor_f(ss, 16);
+      ss += shfl_xor_f(ss, 32);
+      const float rs = row_ok[cs] ? (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * 0.08838834764831845f : 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float x[8], w[8];
+        load8(src + 32 * k, x);
+        load8(qw + 32 * k + 8 * qq, w);
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          uint32_t h0, l0, h1, l1;
+          split_hi_lo(x[j] * rs * w[j], h0, l0);
+          split_hi_lo(x[j + 1] * rs * w[j + 1], h1, l1);
+          hw[j / 2] = h0 | (h1 << 16);
+          lw[j / 2] = l0 | (l1 << 16);
+        }
+        b[cs][k][0] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        b[cs][k][1] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      }
+    }
+  };
+
+  auto compute = [&](const TileA &a, int item) {
+    const ScoreItem c = decode_score_item(item, sp, g.Hkv, n_blocks);
+    if (c.t * kIdxTile >= c.nb) return;                 // tile past this session's history
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      if (key_r0 + cs * 16 >= n_rows) break;            // operand set wholly past the rows
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a.w[4 * mm + k]), b[cs][k][0], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a.w[4 * mm + k]), b[cs][k][1], d, 0, 0, 0);
+        }
+        if (row_ok[cs]) {
+          const int bb = c.t * kIdxTile + 16 * mm + 4 * qq;
+          float *dst = scores + row_id[cs] * g.max_blocks + bb;
+          if (bb + 3 < c.nb && (g.max_blocks & 3) == 0) {
+            *reinterpret_cast<float4 *>(dst) = make_float4(d[0], d[1], d[2], d[3]);   // 16-byte aligned
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (bb + i < c.nb) dst[i] = d[i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (bb + i < c.nb) {
+              const float dd = d[i] - m[cs];
+              const float e = __expf(-fabsf(dd));
+              l[cs] = dd > 0.f ? fmaf(l[cs], e, 1.f) : l[cs] + e;
+              m[cs] = fmaxf(m[cs], d[i]);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // One segment per key in the range: the first tile's loads go out, then the
+  // key's query operands are built while they are in flight, then the tiles
+  // stream with one tile of look-ahead; the last item re-reads its own tile
+  // (an L2 hit) so that the loads stay unconditional.
+  for (int it = i0; it < i1;) {
+    const ScoreItem c0 = decode_score_item(it, sp, g.Hkv, n_blocks);
+    const int end = min(i1, (c0.key + 1) * sp.ntl);
+    TileA ta, tb;
+    load_tile_a(ta, tile_of(it), lane);
+    start_key(c0);
+    while (true) {
+      load_tile_a(tb, tile_of(min(it + 1, end - 1)), lane);
+      compute(ta, it);
+      if (++it >= end) break;
+      load_tile_a(ta, tile_of(min(it + 1, end - 1)), lane);
+      compute(tb, it);
+      if (++it >= end) break;
+    }
+    flush();
+  }
+}
+
+constexpr int kMfmaWavesPerSimd = 2;
+
+}  // namespace
+
+hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
+                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
+                             ScoreSplit *split, hipStream_t st) {
+  int max_nb = 0;
+  for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
+  split->n_sess = n_sess;
+  split->ntl = 0;
+  if (max_nb == 0) return hipSuccess;
+  ScoreSplit sp;
+  sp.n_sess = n_sess;
+  sp.rpg = kMfmaRowGroup;
+  sp.n_rg = (g.Tq * g.G + kMfmaRowGroup - 1) / kMfmaRowGroup;
+  sp.ntl = idx_tiles(max_nb);
+  static int cus = 0;                                   // compute units (device property)
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
+  const long total = (long)n_sess * g.Hkv * sp.n_rg * sp.ntl;
+  const long target = (long)cus * 4 * kMfmaWavesPerSimd;
+  sp.per = (int)((total + target - 1) / target);
+  const int grid = (int)((total + sp.per - 1) / sp.per);
+  *split = sp;
+  if (bf16_q)
+    hipLaunchKernelGGL(k_score_mfma<uint16_t>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index,
+                       (const uint16_t *)q, qw, eps, scores, part, n_blocks, s0, g, sp);
+  else
+    hipLaunchKernelGGL(k_score_mfma<float>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const float *)q,
+                       qw, eps, scores, part, n_blocks, s0, g, sp);
+  return hipGetLastError();
+}
+
+}  // namespace kvmem

@@ -50,7 +50,7 @@ Split recent_split(int n_tok, int n_recent) {
 
 // score_select scratch: per-head scores, per-(row, chunk) softmax statistics, A.
 struct ScoreScratch {
-  size_t scores, part, agg, qn, total;
+  size_t scores, part, agg, total;
 };
 ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   ScoreScratch r;
@@ -59,8 +59,7 @@ ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   r.scores = 0;
   r.part = align_up(rows * max_blocks * sizeof(float));
   r.agg = r.part + align_up(rows * n_slots * sizeof(float2));
-  r.qn = r.agg + align_up((size_t)S * g->n_kv_heads * max_blocks * sizeof(float));
-  r.total = r.qn + align_up(rows * kD * sizeof(float));   // normalised query rows
+  r.total = r.agg + align_up((size_t)S * g->n_kv_heads * max_blocks * sizeof(float));
   return r;
 }
 
@@ -188,9 +187,11 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
       tm.n_all.v[i] = sp.n_all;
     }
     ScoreSplit split;
-    if ((st = hip_status(launch_score_gemv(bf16, index, q, q_norm_w, eps, (float *)(base + sc.qn), scores, part, nb,
-                                           s0, n, g, &split, hs))) != KVMEM_OK)
-      return st;
+    const hipError_t e =
+        bf16 && T * g.G > kGemvMaxRows
+            ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs)
+            : launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs);
+    if ((st = hip_status(e)) != KVMEM_OK) return st;
     if ((st = hip_status(launch_aggregate(scores, part, A, nb, s0, g, split, hs))) != KVMEM_OK) return st;
     if (n_list > 0 &&
         (st = hip_status(launch_topk(A, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)

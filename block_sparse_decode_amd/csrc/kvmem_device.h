@@ -50,6 +50,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// y = hi + lo with hi = bf16(y) and lo = bf16(y - hi): a product with a bf16
+// operand accumulated over both parts carries ~16 significant bits of y.
+__device__ __forceinline__ void split_hi_lo(float y, uint32_t &hi, uint32_t &lo) {
+  hi = f32_to_bf16(y);
+  lo = f32_to_bf16(y - __uint_as_float(hi << 16));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }

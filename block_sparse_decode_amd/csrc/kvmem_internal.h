@@ -41,9 +41,38 @@ struct ScoreSplit {
   int n_sess, rpg, n_rg, ntl, per;
 };
 
-hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *qn,
-                             float *scores, float2 *part, const SessI32 &n_blocks, int s0, int n_sess,
-                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st);
+// Work item = (session, row group, KV head, index tile), tile fastest.  The
+// key (session, row group, head) = item / ntl = (sl * n_rg + rg) * Hkv + h.
+struct ScoreItem {
+  int sl, h, r0, t, nb, key;
+};
+__device__ __forceinline__ ScoreItem decode_score_item(int item, const ScoreSplit &sp, int Hkv, const SessI32 &n_blocks) {
+  ScoreItem it;
+  it.t = item % sp.ntl;
+  it.key = item / sp.ntl;
+  it.h = it.key % Hkv;
+  const int y = it.key / Hkv;
+  it.r0 = (y % sp.n_rg) * sp.rpg;
+  it.sl = y / sp.n_rg;
+  it.nb = n_blocks.v[it.sl];
+  return it;
+}
+// First softmax-statistics slot of a key and the number of slots it has.
+__host__ __device__ __forceinline__ int score_slot0(int key, const ScoreSplit &sp) { return (key * sp.ntl) / sp.per; }
+__host__ __device__ __forceinline__ int score_n_slots(int key, const ScoreSplit &sp) {
+  return ((key + 1) * sp.ntl - 1) / sp.per - score_slot0(key, sp) + 1;
+}
+
+hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *scores,
+                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
+                             ScoreSplit *split, hipStream_t st);
+
+// Matrix-core scorer for bf16 query chunks with more than kGemvMaxRows rows
+// per KV head (row groups of 32).
+constexpr int kGemvMaxRows = 8;
+hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
+                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
+                             ScoreSplit *split, hipStream_t st);
 
 hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, const SessI32 &n_blocks,
                             int s0, const ScoreGeom &g, const ScoreSplit &split, hipStream_t st);
