@@ -36,95 +36,50 @@ constexpr int kQprepMaxT = 32;                          // query tokens per step
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 
-// Query operands of the matrix-core products, prepared once per (session, KV
-// head): q~ (RMSNorm, weight), RoPE at V + t, scaled by log2(e)/sqrt(d), split
-// into bf16 hi + lo, stored in the B-operand lane layout
-// qop[s][h][nt][c*2 + {hi,lo}][lane] (uint4 = 8 bf16).  Lane (qq, col) holds row
-// 16*nt + col; its chunk c holds dims 32c + 8qq .. +7, so the RoPE partner of a
-// dim (+-64) sits in chunk c ^ 2 of the same lane.
-template <int NT>
-__global__ __launch_bounds__(64) void k_attend_qprep(const uint16_t *__restrict__ q, const float *__restrict__ qw,
-                                                     float eps, uint4 *__restrict__ qop, SessI32 view_tok, int s0,
-                                                     AttendGeom g, double theta) {
-  __shared__ float cs_tab[kQprepMaxT][kD / 2][2];
-  const int sl = blockIdx.y;
-  const int s = s0 + sl;
-  const int h = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int qq = lane >> 4;
-  const int col = lane & 15;
-  const int V = view_tok.v[sl];
-  // (cos, sin) of every (query token, frequency) once: lane = frequency index
-  {
-    const double inv_freq = rope_inv_freq(lane, theta);
-    const int n_t = (g.rows + g.G - 1) / g.G;
-    for (int t = 0; t < n_t; ++t) rope_cos_sin((double)(V + t), inv_freq, cs_tab[t][lane][0], cs_tab[t][lane][1]);
-  }
-  __syncthreads();
-  uint4 *dst = qop + ((size_t)(s * g.Hkv + h) * NT) * 8 * 64;
+// Query operands of the matrix-core products for the 16 rows of operand set nt:
+// q~ (RMSNorm, weight), RoPE at V + t, scaled by log2(e)/sqrt(d), split into
+// bf16 hi + lo, in the B-operand lane layout.  Lane (qq, col) holds row
+// 16*nt + col; its chunk c holds dims 32c + 8qq .. +7, so the RoPE partner of
+// a dim (+-64) sits in chunk c ^ 2 of the same lane.  x holds the row's raw
+// values, cs_tab the (cos, sin) of every (query token, frequency).
+__device__ __forceinline__ void build_q_operands(const float (&x)[4][8], bool valid, int t, int qq, const float *qw,
+                                                 float eps, const float (*cs_tab)[kD / 2][2], bf16x8 (&qhi)[4],
+                                                 bf16x8 (&qlo)[4]) {
+  float ss = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = nt * 16 + col;
-    const bool valid = r < g.rows;
-    const int t = valid ? r / g.G : 0;
-    const int gg = valid ? r % g.G : 0;
-    float x[4][8];                                    // [chunk c][j] = dim 32c + 8qq + j
-    if (valid) {
-      const uint16_t *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + 8 * qq;
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(src + 32 * c);
-        const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+    for (int j = 0; j < 8; ++j) ss += x[c][j] * x[c][j];
+  ss = sum_xor16(ss);
+  ss = sum_xor32(ss);
+  const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  float y[4][8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[c][2 * k] = bf16_lo(e[k]);
-          x[c][2 * k + 1] = bf16_hi(e[k]);
-        }
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[c][j] = x[c][j] * rs * qw[32 * c + 8 * qq + j];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      uint32_t h2[2], l2[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ip = 32 * (c & 1) + 8 * qq + j + k;          // pair index (dim mod 64)
+        const float cs = cs_tab[t][ip][0], sn = cs_tab[t][ip][1];
+        const float xo = y[c][j + k], xp = y[c ^ 2][j + k];
+        const float r = (c < 2 ? xo * cs - xp * sn : xo * cs + xp * sn) * kLog2eRsqrtD;
+        split_hi_lo(valid ? r : 0.f, h2[k], l2[k]);
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[c][j] = 0.f;
+      hw[j / 2] = h2[0] | (h2[1] << 16);
+      lw[j / 2] = l2[0] | (l2[1] << 16);
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss += x[c][j] * x[c][j];
-    ss += shfl_xor_f(ss, 16);
-    ss += shfl_xor_f(ss, 32);
-    const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[c][j] = x[c][j] * rs * qw[32 * c + 8 * qq + j];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        uint32_t h2[2], l2[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int ip = 32 * (c & 1) + 8 * qq + j + k;          // pair index (dim mod 64)
-          const float cs = cs_tab[t][ip][0], sn = cs_tab[t][ip][1];
-          const float xo = x[c][j + k], xp = x[c ^ 2][j + k];
-          const float y = (c < 2 ? xo * cs - xp * sn : xo * cs + xp * sn) * kLog2eRsqrtD;
-          split_hi_lo(valid ? y : 0.f, h2[k], l2[k]);
-        }
-        hw[j / 2] = h2[0] | (h2[1] << 16);
-        lw[j / 2] = l2[0] | (l2[1] << 16);
-      }
-      dst[((size_t)nt * 8 + 2 * c) * 64 + lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      dst[((size_t)nt * 8 + 2 * c + 1) * 64 + lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    }
+    qhi[c] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    qlo[c] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
   }
 }
 
-// K and V operands of one 32-token view block for lane (qq, col).  Chunk c of
-// the K operand holds dims 32c + 8qq .. +7 of token 16tt + col, so the four
-// lane groups of one load instruction read one contiguous 64-byte run per row.
 struct KVTile {
   uint4 k[2][4];
   uint4 v[8];
@@ -172,8 +127,8 @@ __device__ __forceinline__ void attend_tile(const KVTile &t, const bf16x8 (&qhi)
   for (int nt = 0; nt < NT; ++nt) {
     float bm = fmaxf(fmaxf(fmaxf(sc[0][nt][0], sc[0][nt][1]), fmaxf(sc[0][nt][2], sc[0][nt][3])),
                      fmaxf(fmaxf(sc[1][nt][0], sc[1][nt][1]), fmaxf(sc[1][nt][2], sc[1][nt][3])));
-    bm = fmaxf(bm, shfl_xor_f(bm, 16));
-    bm = fmaxf(bm, shfl_xor_f(bm, 32));
+    bm = max_xor16(bm);
+    bm = max_xor32(bm);
     const float mn = fmaxf(mrun[nt], bm);
     const float alpha = exp2f(mrun[nt] - mn);
     mrun[nt] = mn;
@@ -209,12 +164,13 @@ __device__ __forceinline__ void attend_tile(const KVTile &t, const bf16x8 (&qhi)
 }
 
 template <int NT>
-__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void k_attend_bf16(const uint4 *__restrict__ qop, const uint16_t *__restrict__ kview,
-                                                     const uint16_t *__restrict__ vview, float *__restrict__ part_o,
-                                                     float2 *__restrict__ part_ml, float *__restrict__ out,
-                                                     SessI32 view_tok, int s0, AttendGeom g) {
+__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void k_attend_bf16(
+    const uint16_t *__restrict__ q, const float *__restrict__ qw, float eps, const uint16_t *__restrict__ kview,
+    const uint16_t *__restrict__ vview, float *__restrict__ part_o, float2 *__restrict__ part_ml,
+    float *__restrict__ out, SessI32 view_tok, int s0, AttendGeom g, double theta) {
   constexpr int RP = 16 * NT;
   constexpr int kPitch = kD + 4;
+  __shared__ float cs_tab[kQprepMaxT][kD / 2][2];
   __shared__ float sm[4][RP];
   __shared__ float sls[4][RP];
   __shared__ float so[4][RP * kPitch];
@@ -234,22 +190,48 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void k_attend_bf16(const uint
   const int qq = lane >> 4;
   const int col = lane & 15;
   const size_t head = (size_t)s * g.Hkv + h;
+  const uint16_t *kbase = kview + head * (size_t)g.max_view * kD;
+  const uint16_t *vbase = vview + head * (size_t)g.max_view * kD;
+  const int tok0 = start + wave * g.tpw;
+  const int tok1 = min(V, tok0 + g.tpw);
 
-  bf16x8 qhi[NT][4], qlo[NT][4];
-  {
-    const uint4 *src = qop + head * NT * 8 * 64;
+  // Loads first, in the order they are needed: the raw query rows of this
+  // lane, then the wavefront's first K/V tile.  The RoPE table is computed
+  // while they are in flight.
+  float x[NT][4][8];
+  int trow[NT];
+  bool rvalid[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = nt * 16 + col;
+    rvalid[nt] = r < g.rows;
+    const int t = rvalid[nt] ? r / g.G : 0, gg = rvalid[nt] ? r % g.G : 0;
+    trow[nt] = t;
+    const uint16_t *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + 8 * qq;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        qhi[nt][c] = as_bf16x8(src[((size_t)nt * 8 + 2 * c) * 64 + lane]);
-        qlo[nt][c] = as_bf16x8(src[((size_t)nt * 8 + 2 * c + 1) * 64 + lane]);
+    for (int c = 0; c < 4; ++c) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(src + 32 * c);
+      const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[nt][c][2 * k] = bf16_lo(e[k]);
+        x[nt][c][2 * k + 1] = bf16_hi(e[k]);
       }
-    // Complete these loads here: otherwise the wait-count insertion treats them as
-    // still outstanding inside the streaming loop and waits for the prefetched
-    // tile before every block.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
   }
+  KVTile tile;
+  if (tok0 < tok1) load_kv_tile(tile, kbase, vbase, tok0, qq, col);
+  {
+    const int n_t = (g.rows + g.G - 1) / g.G;
+    for (int idx = tid; idx < n_t * (kD / 2); idx += 256) {
+      const int t = idx / (kD / 2), i = idx % (kD / 2);
+      rope_cos_sin((double)(V + t), rope_inv_freq(i, theta), cs_tab[t][i][0], cs_tab[t][i][1]);
+    }
+  }
+  __syncthreads();
+  bf16x8 qhi[NT][4], qlo[NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) build_q_operands(x[nt], rvalid[nt], trow[nt], qq, qw, eps, cs_tab, qhi[nt], qlo[nt]);
 
   floatx4 o[NT][8];
   float mrun[NT], lrun[NT];
@@ -260,28 +242,26 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void k_attend_bf16(const uint
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[nt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  const uint16_t *kbase = kview + head * (size_t)g.max_view * kD;
-  const uint16_t *vbase = vview + head * (size_t)g.max_view * kD;
-  // One 32-token tile at a time: load, then compute.  (Holding a second tile in
-  // flight per wavefront measured markedly slower on this part: the stream
-  // runs best with each wavefront walking its run one tile deep.)
-  const int tok0 = start + wave * g.tpw;
-  const int tok1 = min(V, tok0 + g.tpw);
+  // One 32-token tile in flight per wavefront: multiply the tile, then request
+  // the next.  (Holding a second tile in flight per wavefront measured markedly
+  // slower on this part: the stream runs best with each wavefront walking its
+  // run one tile deep.)
   for (int tb = tok0; tb < tok1; tb += kBT) {
-    KVTile t;
-    load_kv_tile(t, kbase, vbase, tb, qq, col);
-    // keep all 16 K and V loads of the tile together at its start (the
-    // scheduler would otherwise sink the V loads below the first product and
-    // expose a second memory latency per tile)
-    __builtin_amdgcn_sched_barrier(0);
-    attend_tile<NT>(t, qhi, qlo, o, mrun, lrun, tb, V, qq);
+    attend_tile<NT>(tile, qhi, qlo, o, mrun, lrun, tb, V, qq);
+    if (tb + kBT < tok1) {
+      load_kv_tile(tile, kbase, vbase, tb + kBT, qq, col);
+      // keep all 16 K and V loads of the tile together (the scheduler would
+      // otherwise sink the V loads below the first product and expose a
+      // second memory latency per tile)
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- merge the 4 wavefronts (log-sum-exp) ----
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    lrun[nt] += shfl_xor_f(lrun[nt], 16);
-    lrun[nt] += shfl_xor_f(lrun[nt], 32);
+    lrun[nt] = sum_xor16(lrun[nt]);
+    lrun[nt] = sum_xor32(lrun[nt]);
     const int row = nt * 16 + col;
     if (qq == 0) {
       sm[wave][row] = mrun[nt];
@@ -443,25 +423,16 @@ __global__ __launch_bounds__(256) void k_attend_f32(const float *__restrict__ q,
 // (session, KV head, query row); 8 groups of 32 threads each take every 8th
 // split for 4 dimensions, then the groups are added in order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_reduce_256(float v, float *red, bool is_max) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float o = shfl_xor_f(v, m);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  const float r = is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return r;
-}
-
+// Log-sum-exp merge of the split partials of one (session, KV head, query row).
+// 256 threads = 8 split groups x 32 float4 slices of the row; each thread
+// folds its splits with an online rescale (no separate max and sum passes, four
+// splits in flight), then the 8 groups are folded in a fixed order, so the
+// result is deterministic.
 __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict__ part_o,
                                                         const float2 *__restrict__ part_ml, float *__restrict__ out,
                                                         SessI32 view_tok, int s0, AttendGeom g) {
-  __shared__ float red[4];
   __shared__ float4 acc_s[8][32];
+  __shared__ float m_s[8], l_s[8];
   const int sl = blockIdx.z;
   const int s = s0 + sl;
   const int h = blockIdx.y;
@@ -479,34 +450,49 @@ __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict_
   }
   const size_t head = (size_t)s * g.Hkv + h;
   const size_t base = head * g.max_splits * g.rows + row;     // + i * rows
-  float m = -INFINITY;
-  for (int i = tid; i < n; i += 256) m = fmaxf(m, part_ml[base + (size_t)i * g.rows].x);
-  const float M = block_reduce_256(m, red, true);
-  float d = 0.f;
-  for (int i = tid; i < n; i += 256) {
-    const float2 ml = part_ml[base + (size_t)i * g.rows];
-    d += exp2f(ml.x - M) * ml.y;
-  }
-  const float den = block_reduce_256(d, red, false);
   const int sg = tid >> 5, q4 = tid & 31;
+  float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = sg; i < n; i += 8) {
+  auto fold = [&](float2 ml, float4 v) {
+    if (ml.x == -INFINITY) return;
+    const float mn = fmaxf(m, ml.x);
+    const float a = exp2f(m - mn), b = exp2f(ml.x - mn);
+    l = l * a + ml.y * b;
+    acc.x = acc.x * a + v.x * b; acc.y = acc.y * a + v.y * b;
+    acc.z = acc.z * a + v.z * b; acc.w = acc.w * a + v.w * b;
+    m = mn;
+  };
+  int i = sg;
+  for (; i + 24 < n; i += 32) {
+    float2 ml[4];
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t pidx = base + (size_t)(i + 8 * u) * g.rows;
+      ml[u] = part_ml[pidx];
+      v[u] = reinterpret_cast<const float4 *>(part_o + pidx * kD)[q4];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fold(ml[u], v[u]);
+  }
+  for (; i < n; i += 8) {
     const size_t pidx = base + (size_t)i * g.rows;
-    const float w = exp2f(part_ml[pidx].x - M);
-    const float4 v = reinterpret_cast<const float4 *>(part_o + pidx * kD)[q4];
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+    fold(part_ml[pidx], reinterpret_cast<const float4 *>(part_o + pidx * kD)[q4]);
   }
   acc_s[sg][q4] = acc;
+  if (q4 == 0) {
+    m_s[sg] = m;
+    l_s[sg] = l;
+  }
   __syncthreads();
   if (tid < 32) {
-    float4 r = acc_s[0][tid];
+    m = -INFINITY;
+    l = 0.f;
+    acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 1; j < 8; ++j) {
-      const float4 v = acc_s[j][tid];
-      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
-    }
-    const float inv = 1.0f / den;
-    reinterpret_cast<float4 *>(dst)[tid] = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    for (int j = 0; j < 8; ++j) fold(make_float2(m_s[j], l_s[j]), acc_s[j][tid]);
+    const float inv = 1.0f / l;
+    reinterpret_cast<float4 *>(dst)[tid] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
@@ -525,7 +511,7 @@ int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view) {
 int attend_max_splits(int max_view, int tpw) { return (max_view + 4 * tpw - 1) / (4 * tpw); }
 
 hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
-                         const void *v_view, float *part_o, float2 *part_ml, uint4 *qop, float *out,
+                         const void *v_view, float *part_o, float2 *part_ml, float *out,
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
                          hipStream_t st) {
   int max_v = 0;
@@ -537,15 +523,13 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
       hipLaunchKernelGGL(k_attend_f32, grid, dim3(256), 0, st, (const float *)q, qw, eps, (const float *)k_view,
                          (const float *)v_view, part_o, part_ml, out, view_tok, s0, g, theta);
     } else if (g.rows <= 16) {
-      hipLaunchKernelGGL(k_attend_qprep<1>, dim3(g.Hkv, n_sess), dim3(64), 0, st, (const uint16_t *)q, qw, eps, qop,
-                         view_tok, s0, g, theta);
-      hipLaunchKernelGGL(k_attend_bf16<1>, grid, dim3(256), 0, st, (const uint4 *)qop, (const uint16_t *)k_view,
-                         (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g);
+      hipLaunchKernelGGL(k_attend_bf16<1>, grid, dim3(256), 0, st, (const uint16_t *)q, qw, eps,
+                         (const uint16_t *)k_view, (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g,
+                         theta);
     } else {
-      hipLaunchKernelGGL(k_attend_qprep<2>, dim3(g.Hkv, n_sess), dim3(64), 0, st, (const uint16_t *)q, qw, eps, qop,
-                         view_tok, s0, g, theta);
-      hipLaunchKernelGGL(k_attend_bf16<2>, grid, dim3(256), 0, st, (const uint4 *)qop, (const uint16_t *)k_view,
-                         (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g);
+      hipLaunchKernelGGL(k_attend_bf16<2>, grid, dim3(256), 0, st, (const uint16_t *)q, qw, eps,
+                         (const uint16_t *)k_view, (const uint16_t *)v_view, part_o, part_ml, out, view_tok, s0, g,
+                         theta);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

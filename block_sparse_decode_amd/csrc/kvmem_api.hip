@@ -64,7 +64,7 @@ ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
 }
 
 struct AttendScratch {
-  size_t part_o, part_ml, qop, total;
+  size_t part_o, part_ml, total;
   int tpw, max_splits;
 };
 AttendScratch attend_scratch(const kvmem_geom *g, int S, int T, int max_view) {
@@ -73,11 +73,9 @@ AttendScratch attend_scratch(const kvmem_geom *g, int S, int T, int max_view) {
   r.max_splits = attend_max_splits(max_view, r.tpw);
   const size_t rows = (size_t)T * (g->n_q_heads / g->n_kv_heads);
   const size_t n = (size_t)S * g->n_kv_heads * r.max_splits * rows;
-  const size_t nt = (rows + 15) / 16;
   r.part_o = 0;
   r.part_ml = align_up(n * kD * sizeof(float));
-  r.qop = r.part_ml + align_up(n * sizeof(float2));
-  r.total = r.qop + align_up((size_t)S * g->n_kv_heads * nt * 8 * 64 * 16);   // q operands (uint4 per lane)
+  r.total = r.part_ml + align_up(n * sizeof(float2));
   return r;
 }
 
@@ -274,7 +272,7 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions, const void
     memset(&vt, 0, sizeof(vt));
     for (int i = 0; i < n; ++i) vt.v[i] = view_tokens_host[s0 + i];
     st = hip_status(launch_attend(bf16, q, q_norm_w, eps, k_view, v_view, (float *)(base + sc.part_o),
-                                  (float2 *)(base + sc.part_ml), (uint4 *)(base + sc.qop), out, vt, s0, n, g,
+                                  (float2 *)(base + sc.part_ml), out, vt, s0, n, g,
                                   (double)rope_theta, (hipStream_t)stream));
     if (st != KVMEM_OK) return st;
   }

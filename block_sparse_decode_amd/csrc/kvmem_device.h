@@ -128,6 +128,27 @@ __device__ __forceinline__ float dpp_f32_rows(float old, float v) {
                                                                CTRL, ROW_MASK, 0xf, false));
 }
 
+// One butterfly step across 16-lane rows (partner lane l ^ 16) or wavefront
+// halves (l ^ 32) with the VALU lane permutes of gfx950: passing v as both
+// operands, the two results hold v[l] and v[l ^ m] in every lane (which is
+// which depends on the lane), so a commutative op of the two is the step.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Whole-wavefront sum / max on the DPP network (no LDS round trips): reduce
 // each 16-lane row (quad swaps, then the half-row and row mirrors), fold row 0
 // into row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1 into rows 2-3

@@ -99,7 +99,7 @@ int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view);
 int attend_max_splits(int max_view, int tpw);
 
 hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
-                         const void *v_view, float *part_o, float2 *part_ml, uint4 *qop, float *out,
+                         const void *v_view, float *part_o, float2 *part_ml, float *out,
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
                          hipStream_t st);
 
