@@ -27,7 +27,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["kvmem_api.hip", "k_index.hip", "k_score.hip", "k_score_mfma.hip", "k_select.hip", "k_materialize.hip",
+SOURCES = ["kvmem_api.hip", "k_index.hip", "k_score.hip", "k_score_mfma.hip", "k_score_long.hip", "k_select.hip", "k_materialize.hip",
            "k_attend.hip"]
 
 

@@ -48,18 +48,38 @@ Split recent_split(int n_tok, int n_recent) {
   return r;
 }
 
-// score_select scratch: per-head scores, per-(row, chunk) softmax statistics, A.
+// Steps with many query rows per KV head (bf16) take the two-pass long-chunk
+// scorer, which never stores the score matrix.
+bool long_chunk(const kvmem_geom *g, int T) {
+  return g->kv_dtype == KVMEM_BF16 && (long)T * (g->n_q_heads / g->n_kv_heads) > kMfmaMaxRows;
+}
+
+// score_select scratch.  Short steps: per-head scores, per-(row, slot)
+// softmax statistics, A.  Long chunks: query operands, per-(row, block group)
+// statistics, per-row log-sum-exp, A.
 struct ScoreScratch {
-  size_t scores, part, agg, total;
+  size_t scores, part, agg, qf, lse, total;
 };
 ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   ScoreScratch r;
+  const size_t a_bytes = align_up((size_t)S * g->n_kv_heads * max_blocks * sizeof(float));
+  if (long_chunk(g, T)) {
+    const LongScratch L = long_scratch_layout(S, g->n_kv_heads, T, g->n_q_heads / g->n_kv_heads, max_blocks);
+    r.scores = 0;
+    r.part = 0;
+    r.qf = align_up(L.part_bytes);
+    r.lse = r.qf + align_up(L.qf_bytes);
+    r.agg = r.lse + align_up(L.lse_bytes);
+    r.total = r.agg + a_bytes;
+    return r;
+  }
   const size_t rows = (size_t)S * T * g->n_q_heads;
   const size_t n_slots = (size_t)idx_tiles(max_blocks) + 1;   // softmax-statistics slots per row
   r.scores = 0;
   r.part = align_up(rows * max_blocks * sizeof(float));
   r.agg = r.part + align_up(rows * n_slots * sizeof(float2));
-  r.total = r.agg + align_up((size_t)S * g->n_kv_heads * max_blocks * sizeof(float));
+  r.qf = r.lse = r.agg;
+  r.total = r.agg + a_bytes;
   return r;
 }
 
@@ -184,13 +204,19 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
       tm.r_start.v[i] = sp.r_start;
       tm.n_all.v[i] = sp.n_all;
     }
-    ScoreSplit split;
-    const hipError_t e =
-        bf16 && T * g.G > kGemvMaxRows
-            ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs)
-            : launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs);
-    if ((st = hip_status(e)) != KVMEM_OK) return st;
-    if ((st = hip_status(launch_aggregate(scores, part, A, nb, s0, g, split, hs))) != KVMEM_OK) return st;
+    if (long_chunk(geom, T)) {
+      if ((st = hip_status(launch_score_long(index, q, q_norm_w, eps, (uint4 *)(base + sc.qf), part,
+                                             (float *)(base + sc.lse), A, scores_opt, nb, s0, n, g, hs))) != KVMEM_OK)
+        return st;
+    } else {
+      ScoreSplit split;
+      const hipError_t e =
+          bf16 && T * g.G > kGemvMaxRows
+              ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs)
+              : launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs);
+      if ((st = hip_status(e)) != KVMEM_OK) return st;
+      if ((st = hip_status(launch_aggregate(scores, part, A, nb, s0, g, split, hs))) != KVMEM_OK) return st;
+    }
     if (n_list > 0 &&
         (st = hip_status(launch_topk(A, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
       return st;

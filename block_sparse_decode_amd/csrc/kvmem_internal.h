@@ -74,6 +74,18 @@ hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const
                              float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
                              ScoreSplit *split, hipStream_t st);
 
+// Long query chunks (bf16, more than kMfmaMaxRows rows per KV head): two passes
+// over the index on the matrix cores without storing the score matrix; writes
+// A directly (no aggregation kernel).  Scratch per LongScratch.
+constexpr int kMfmaMaxRows = 32;
+struct LongScratch {
+  size_t qf_bytes, part_bytes, lse_bytes;
+};
+LongScratch long_scratch_layout(int S, int Hkv, int T, int G, int max_blocks);
+hipError_t launch_score_long(const void *index, const void *q, const float *qw, float eps, uint4 *qf, float2 *part,
+                             float *lse, float *A, float *scores_opt, const SessI32 &n_blocks, int s0, int n_sess,
+                             const ScoreGeom &g, hipStream_t st);
+
 hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, const SessI32 &n_blocks,
                             int s0, const ScoreGeom &g, const ScoreSplit &split, hipStream_t st);
 

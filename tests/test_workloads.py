@@ -3,6 +3,7 @@ and the margin certifier."""
 from __future__ import annotations
 
 import numpy as np
+import pytest
 
 from oracle import kvmem_oracle as O
 from tests.certify import TAU, certify
@@ -71,3 +72,50 @@ def test_certify_opens_the_cut():
         a = np.sort(A[:nc])[::-1]
         assert (a[299] - a[300]) / a[299] >= TAU
     assert any(v[1] > 0 for v in rep.values())      # this seed needs repairs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pool_chunks_match_full_draw_with_repairs(dtype):
+    """Chunk-by-chunk drawing (used for workspaces too large for the host)
+    gives the same pools as the full draw, repair log included."""
+    from workloads import pool_chunks
+    cfg = CONFIGS["c1"].replace(dtype=dtype, n_tokens=(2 * 1024 * 32 + 100,), k_select=8, n_recent=4)
+    rep = [(0, 0, 5, 3, 0.25), (0, 0, 5, 3, -0.125), (0, 0, 1500, 7, 1.0)]
+    full = make_workload(cfg, repairs=rep)
+    lite = make_workload(cfg, pools=False, repairs=rep)
+    assert lite.k_pool is None and lite.n_pages == full.n_pages
+    assert np.array_equal(lite.block_table, full.block_table) and np.array_equal(lite.q, full.q)
+    for which, pool in (("k", full.k_pool), ("v", full.v_pool)):
+        n = 0
+        for s, b0, pages, x in pool_chunks(lite, which, threads=2):
+            assert np.array_equal(pool[pages], x), (which, b0)
+            n += len(pages)
+        assert n == -(-int(full.n_tokens[0]) // 32)
+    # the repairs moved exactly the logged coordinates
+    plain = make_workload(cfg)
+    diff = np.argwhere(plain.k_pool != full.k_pool)
+    pages = {int(full.block_table[0, b]) for b in (5, 1500)}
+    assert {int(p) for p in diff[:, 0]} <= pages and len(diff) > 0
+
+
+def test_certify_streaming_matches_in_memory():
+    """The chunk-by-chunk certification (used for the 10M-token workload) logs
+    repairs that, replayed by the generator, give the same separated cut as
+    the in-memory certification of the same workload."""
+    from tests.certify import certify_streaming, streamed_index
+    # (5% planted, k = 100: head 0's cut needs one repair round on this seed)
+    cfg = CONFIGS["c5"].replace(name="c5_small", n_tokens=(3 * 1024 * 32,), T=4, k_select=100,
+                                plant_fraction=0.05, n_q_heads=8, n_kv_heads=2)
+    wl_mem = make_workload(cfg)
+    rep_mem = certify(wl_mem, t_chunk=2)
+    lite = make_workload(cfg, pools=False)
+    index = streamed_index(lite, threads=2)
+    ws = oracle_ws(wl_mem)
+    repairs, rep, A_all = certify_streaming(lite, index, t_chunk=2, log=lambda m: None)
+    assert {h: r[1] for h, r in rep.items()} == {h: r[1] for (s, h), r in rep_mem.items()}
+    assert len(repairs) > 0
+    replay = make_workload(cfg, repairs=repairs)
+    assert np.array_equal(replay.k_pool, wl_mem.k_pool)
+    for h in range(cfg.n_kv_heads):
+        assert np.array_equal(index[h], O.mean_k_index(ws, 0, h))
+        assert rep[h][2] >= TAU

@@ -25,7 +25,12 @@ Recipe (one seed per workload):
                     Spare pages (never referenced) hold NaN so that a stray
                     read shows up in the results.
 Random streams come from numpy's SeedSequence([seed, stream, ...]) with
-1024-block chunks, so any chunk can be regenerated on its own.
+1024-block chunks, so any chunk can be regenerated on its own (pool_chunks
+yields them one by one, for workspaces too large to hold on the host).
+A workload may carry a key repair log (Workload.extra["repairs"]: ordered
+(session, KV head, block, dim, delta) entries): after a key chunk is drawn,
+each entry adds delta to that coordinate of the block's 32 keys in fp32 and
+re-rounds to the storage dtype, in log order.
 
 Nothing in this module computes any part of the method itself.
 """
@@ -128,7 +133,7 @@ class Workload:
 
     @property
     def n_pages(self) -> int:
-        return int(self.k_pool.shape[0])
+        return int(self.k_pool.shape[0]) if self.k_pool is not None else int(self.extra["n_pages"])
 
     @property
     def max_blocks(self) -> int:
@@ -187,32 +192,48 @@ def _make_table(cfg: Config, lens: np.ndarray, max_blocks: int):
     return table, n_pages
 
 
-def _fill_pool(cfg: Config, pool: np.ndarray, table: np.ndarray, lens: np.ndarray,
-               stream: int, mag: np.ndarray | None, qhat: np.ndarray, threads: int):
-    H, d, Bt = cfg.n_kv_heads, cfg.head_dim, BLOCK_TOKENS
+def _chunk_jobs(cfg: Config, lens: np.ndarray) -> list:
     jobs = []
     for s in range(cfg.n_sessions):
-        nblk = -(-int(lens[s]) // Bt)
+        nblk = -(-int(lens[s]) // BLOCK_TOKENS)
         for c0 in range(0, nblk, CHUNK_BLOCKS):
             jobs.append((s, c0, min(nblk, c0 + CHUNK_BLOCKS)))
+    return jobs
+
+
+def _draw_chunk(cfg: Config, job, lens: np.ndarray, stream: int, mag: np.ndarray | None, qhat: np.ndarray,
+                repairs=()) -> np.ndarray:
+    """Blocks [b0, b1) of session s for all KV heads, in storage form: [nb][H][32][d]."""
+    H, d, Bt = cfg.n_kv_heads, cfg.head_dim, BLOCK_TOKENS
+    s, b0, b1 = job
+    nb = b1 - b0
+    x = np.empty((nb, H, Bt, d), np.float32)
+    _rng(cfg.seed, stream, s, b0 // CHUNK_BLOCKS).standard_normal(out=x, dtype=np.float32)
+    if mag is not None:
+        m = mag[s, :, b0:b1].T.astype(np.float32)                       # [nb][H]
+        x += m[:, :, None, None] * qhat[s][None, :, None, :].astype(np.float32)
+    n_tok = int(lens[s])
+    last_valid = n_tok - (b1 - 1) * Bt                                 # tokens in the last block
+    if last_valid < Bt:                                                # partial tail: zero the rest
+        x[-1, :, last_valid:, :] = 0.0
+    out = f32_to_bf16_bits(x) if cfg.dtype == "bf16" else x
+    for (rs, rh, rb, ri, delta) in repairs:
+        if rs == s and b0 <= rb < b1:
+            if cfg.dtype == "bf16":
+                col = bf16_bits_to_f32(out[rb - b0, rh, :, ri])
+                out[rb - b0, rh, :, ri] = f32_to_bf16_bits(col + np.float32(delta))
+            else:
+                out[rb - b0, rh, :, ri] += np.float32(delta)
+    return out
+
+
+def _fill_pool(cfg: Config, pool: np.ndarray, table: np.ndarray, lens: np.ndarray,
+               stream: int, mag: np.ndarray | None, qhat: np.ndarray, threads: int, repairs=()):
+    jobs = _chunk_jobs(cfg, lens)
 
     def work(job):
         s, b0, b1 = job
-        nb = b1 - b0
-        x = np.empty((nb, H, Bt, d), np.float32)
-        _rng(cfg.seed, stream, s, b0 // CHUNK_BLOCKS).standard_normal(out=x, dtype=np.float32)
-        if mag is not None:
-            m = mag[s, :, b0:b1].T.astype(np.float32)                   # [nb][H]
-            x += m[:, :, None, None] * qhat[s][None, :, None, :].astype(np.float32)
-        n_tok = int(lens[s])
-        last_valid = n_tok - (b1 - 1) * Bt                             # tokens in the last block
-        if last_valid < Bt:                                            # partial tail: zero the rest
-            x[-1, :, last_valid:, :] = 0.0
-        pages = table[s, b0:b1]
-        if cfg.dtype == "bf16":
-            pool[pages] = f32_to_bf16_bits(x)
-        else:
-            pool[pages] = x
+        pool[table[s, b0:b1]] = _draw_chunk(cfg, job, lens, stream, mag, qhat, repairs)
 
     if threads <= 1 or len(jobs) <= 1:
         for j in jobs:
@@ -222,8 +243,36 @@ def _fill_pool(cfg: Config, pool: np.ndarray, table: np.ndarray, lens: np.ndarra
             list(ex.map(work, jobs))
 
 
-def make_workload(cfg: Config, threads: int | None = None, with_v: bool = True) -> Workload:
-    """Draw the full workspace of `cfg` (host arrays)."""
+def pool_chunks(wl: "Workload", which: str = "k", threads: int | None = None, jobs=None):
+    """Yield (session, first block, pages, chunk) for every 1024-block chunk of
+    the K ("k") or V ("v") pool, drawn exactly as make_workload draws them
+    (chunk = [nb][H][32][d] in storage form).  Chunks are drawn on a thread
+    pool and yielded in order; `jobs` restricts the walk to given
+    (session, first block, end block) chunks."""
+    cfg = wl.cfg
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+    lens = wl.n_tokens.astype(np.int64)
+    stream, mag = (_S_K, wl.plant_mag) if which == "k" else (_S_V, None)
+    repairs = tuple(wl.extra.get("repairs", ())) if which == "k" else ()
+    jobs = _chunk_jobs(cfg, lens) if jobs is None else list(jobs)
+    draw = lambda job: _draw_chunk(cfg, job, lens, stream, mag, wl.qhat, repairs)
+    with _cf.ThreadPoolExecutor(max(1, threads)) as ex:
+        futs = [ex.submit(draw, j) for j in jobs[:2 * threads]]
+        for i, job in enumerate(jobs):
+            x = futs[i].result()
+            futs[i] = None
+            if i + 2 * threads < len(jobs):
+                futs.append(ex.submit(draw, jobs[i + 2 * threads]))
+            s, b0, b1 = job
+            yield s, b0, wl.block_table[s, b0:b1], x
+
+
+def make_workload(cfg: Config, threads: int | None = None, with_v: bool = True, pools: bool = True,
+                  repairs=()) -> Workload:
+    """Draw the full workspace of `cfg` (host arrays).  With pools=False the K
+    and V pools are left out (None) and can be drawn chunk by chunk with
+    pool_chunks; `repairs` is a key repair log (see the module notes)."""
     if threads is None:
         threads = min(16, len(os.sched_getaffinity(0)))
     S, Hq, H, d, T = cfg.n_sessions, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.T
@@ -252,6 +301,11 @@ def make_workload(cfg: Config, threads: int | None = None, with_v: bool = True) 
 
     mag = _plant_magnitudes(cfg, lens, max_blocks)
     table, n_pages = _make_table(cfg, lens, max_blocks)
+    extra = {"repairs": list(repairs)} if repairs else {}
+    if not pools:
+        wl = Workload(cfg, None, None, table, lens.astype(np.int32), q, w, qhat, mag, extra)
+        wl.extra["n_pages"] = n_pages
+        return wl
     pdt = np.uint16 if cfg.dtype == "bf16" else np.float32
     nan = np.uint16(0x7FC0) if cfg.dtype == "bf16" else np.float32(np.nan)
     shape = (n_pages, H, BLOCK_TOKENS, d)
@@ -263,7 +317,7 @@ def make_workload(cfg: Config, threads: int | None = None, with_v: bool = True) 
         k_pool[~used] = nan
         if with_v:
             v_pool[~used] = nan
-    _fill_pool(cfg, k_pool, table, lens, _S_K, mag, qhat, threads)
+    _fill_pool(cfg, k_pool, table, lens, _S_K, mag, qhat, threads, tuple(repairs))
     if with_v:
         _fill_pool(cfg, v_pool, table, lens, _S_V, None, qhat, threads)
-    return Workload(cfg, k_pool, v_pool, table, lens.astype(np.int32), q, w, qhat, mag)
+    return Workload(cfg, k_pool, v_pool, table, lens.astype(np.int32), q, w, qhat, mag, extra)
