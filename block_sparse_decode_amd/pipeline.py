@@ -71,8 +71,12 @@ class DeviceWorkspace:
         self.T = cfg.T
         S, H, d = cfg.n_sessions, cfg.n_kv_heads, cfg.head_dim
         self.S, self.H, self.d = S, H, d
-        self.k_pool = to_device(wl.k_pool, cfg.dtype, self.device)
-        self.v_pool = to_device(wl.v_pool, cfg.dtype, self.device) if with_v else None
+        if wl.k_pool is not None:
+            self.k_pool = to_device(wl.k_pool, cfg.dtype, self.device)
+            self.v_pool = to_device(wl.v_pool, cfg.dtype, self.device) if with_v else None
+        else:                                   # pools too large for the host: drawn chunk by chunk
+            self.k_pool = self._stream_pool(wl, "k")
+            self.v_pool = self._stream_pool(wl, "v") if with_v else None
         self.block_table = torch.from_numpy(np.ascontiguousarray(wl.block_table, dtype=np.int32)).to(self.device)
         self.n_tokens = np.ascontiguousarray(wl.n_tokens, dtype=np.int32)
         self.dev_error = torch.zeros(1, dtype=torch.int32, device=self.device)
@@ -101,6 +105,16 @@ class DeviceWorkspace:
         self.attend_scratch = torch.empty(max(na, 1), dtype=torch.uint8, device=self.device)
         self.eps = cfg.eps
         self.theta = cfg.rope_theta
+
+    def _stream_pool(self, wl, which: str) -> torch.Tensor:
+        from workloads import pool_chunks
+        cfg = wl.cfg
+        shape = (wl.n_pages, cfg.n_kv_heads, BLOCK, cfg.head_dim)
+        pool = torch.empty(shape, dtype=self.tdtype, device=self.device)
+        for _, _, pages, x in pool_chunks(wl, which):
+            idx = torch.from_numpy(np.ascontiguousarray(pages, dtype=np.int64)).to(self.device)
+            pool[idx] = to_device(x, cfg.dtype, self.device)
+        return pool
 
     # --- the four calls ---------------------------------------------------
     def build_index(self, stream=None):

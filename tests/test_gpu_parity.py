@@ -10,6 +10,8 @@ Bars (from the scope of the hot path):
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -155,6 +157,9 @@ SMALL = {
                             k=20, R=0, seed=40),
     "empty_and_tiny": small_cfg("empty_and_tiny", "bf16", S=4, Hq=16, Hkv=2, n_tokens=(0, 5, 32, 32 * 40),
                                 k=8, R=2, n_planted=2, seed=41),
+    # more candidates than one 32768-key register tile of the selection kernel
+    "multi_tile_select": small_cfg("multi_tile_select", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 36000 + 9,),
+                                   k=500, R=16, n_planted=300, seed=61),
 }
 
 
@@ -301,3 +306,83 @@ def test_c4_full():
     assert res["err"] == 0
     for s in range(16):
         check_session(wl, res, s, att_heads=(s % 8,), tag=f"c4 s={s}")
+
+
+C5_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "c5_10m_golden.npz")
+
+
+def test_c5_full():
+    """10,000,000 tokens (312,500 blocks), a 512-token query chunk x 64 heads,
+    top-2048 per KV head, 65,536-token view: the two-pass matrix-core scorer
+    at full size.  The oracle at this size takes minutes, so its results (the
+    certified view lists, A on every selected block and on a sample of the
+    others, and the key repair log the certification made) come from
+    tests/golden/make_c5_golden.py; index rows and view blocks of two pool
+    chunks are recomputed here from redrawn chunks."""
+    _need_gpu()
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace, index_rows, v_view_token_major
+    from tests.certify import chunk_workspace
+    from workloads import pool_chunks
+    if not os.path.exists(C5_GOLDEN):
+        pytest.skip("tests/golden/c5_10m_golden.npz not generated")
+    g = np.load(C5_GOLDEN)
+    repairs = [(int(a), int(b), int(c), int(d), float(e)) for a, b, c, d, e in g["repairs"]]
+    cfg = CONFIGS["c5"]
+    wl = make_workload(cfg, pools=False, repairs=repairs)
+    print(f"[gpu] c5: drawing {wl.n_pages} pages of K and V on the device ({len(repairs)} key repairs)", flush=True)
+    dw = DeviceWorkspace(wl, "cuda")
+    H, G, mb = cfg.n_kv_heads, cfg.group, dw.max_blocks
+    ag = torch.full((1, H, mb), float("nan"), device="cuda")
+    dw.build_index()
+    dw.score_select(agg=ag)
+    dw.materialize()
+    torch.cuda.synchronize()
+    assert int(dw.dev_error.item()) == 0
+    n_tok = int(wl.n_tokens[0])
+    nc, _, _ = O.recent_split(n_tok, cfg.n_recent)
+    # selection (bit-exact) and view length
+    vb = dw.view_blocks.cpu().numpy()[0]
+    assert np.array_equal(vb, g["lists"])
+    V = int(dw.view_tokens[0])
+    assert V == int(g["view_tokens"]) == 65536
+    # aggregated scores on the sampled blocks; every head's A sums to T * G
+    A = ag.cpu().numpy()[0].astype(np.float64)
+    for h in range(H):
+        a_ref = g["a_values"][h]
+        a_gpu = A[h, g["a_blocks"][h]]
+        assert np.all(np.abs(a_gpu - a_ref) <= 1e-3 * a_ref + 1e-30), (h, "A")
+        assert abs(A[h, :nc].sum() - g["a_sums"][h]) <= 1e-3 * g["a_sums"][h], (h, "sum A")
+        assert abs(g["a_sums"][h] - cfg.T * G) <= 1e-6 * cfg.T * G
+    # index rows and view blocks of two redrawn chunks (one holding head 0's
+    # first selected block, and the last chunk)
+    lists = g["lists"]
+    last = -(-n_tok // 32)
+    starts = sorted({(int(lists[0, 0]) // 1024) * 1024, ((last - 1) // 1024) * 1024})
+    jobs = [(0, b0, min(b0 + 1024, last)) for b0 in starts]
+    kch = {b0: x for _, b0, _, x in pool_chunks(wl, "k", jobs=jobs)}
+    vch = {b0: x for _, b0, _, x in pool_chunks(wl, "v", jobs=jobs)}
+    idx_dev = index_rows(dw.index, mb)
+    vview = v_view_token_major(dw.v_view)
+    n_view_checked = 0
+    for (_, b0, b1) in jobs:
+        kws = chunk_workspace(wl, 0, b0, kch[b0])
+        vws = chunk_workspace(wl, 0, b0, vch[b0])
+        n = min(b1, n_tok // 32) - b0
+        for h in range(H):
+            got = _bits_to_f64(idx_dev[0, h, b0:b0 + n].contiguous(), "bf16")
+            assert np.array_equal(got, O.mean_k_rows(kws, 0, h, range(n))), (b0, h, "index")
+            for m in np.nonzero((lists[h] >= b0) & (lists[h] < b1))[0]:
+                beta = int(lists[h, m]) - b0
+                pos = 32 * int(m) + np.arange(32)
+                kv = O.round_store(O.rope(O.block_tokens_of(kws, kws.k_pool, 0, h, [beta])[0], pos,
+                                          cfg.rope_theta), "bf16")
+                vv = O.block_tokens_of(vws, vws.k_pool, 0, h, [beta])[0]
+                kg = _bits_to_f64(dw.k_view[0, h, pos[0]:pos[0] + 32].contiguous(), "bf16")
+                vg = _bits_to_f64(vview[0, h, pos[0]:pos[0] + 32].contiguous(), "bf16")
+                ulp = np.ldexp(1.0, np.frexp(np.abs(kv))[1] - 8)
+                rot = 1e-6 * np.abs(kv).max(axis=-1, keepdims=True)
+                assert np.all(np.abs(kg - kv) <= ulp + rot), (h, int(m), "K view")
+                assert np.array_equal(vg, vv), (h, int(m), "V view")
+                n_view_checked += 1
+    print(f"[gpu] c5: selection, A samples, index rows and {n_view_checked} view blocks match", flush=True)
+    assert n_view_checked > 0
