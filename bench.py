@@ -2,6 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
 
+(--workload c5 times the 10M-token, 512-token-chunk stress instead: one
+workspace drawn on the device, score_select -> materialize -> build_index,
+no attention; the scorer is reported against the bf16 matrix-core peak.)
+
 One step is one pass of the whole path over the 1M-token workspace
 (1,048,576 tokens = 32,768 blocks; 64 query / 8 KV heads; d = 128; bf16):
     kvmem_score_select -> kvmem_materialize -> kvmem_attend -> kvmem_build_index.
@@ -33,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "blocks scored/s + view decode-step latency (µs) at 1M-token workspace; % HBM peak"
 HBM_PEAK = 8.0e12   # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 
 # HBM bytes per launch of each stage's main kernel at the 1M-token workspace,
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB device
@@ -70,6 +75,22 @@ def alg_bytes(cfg, n_blocks: int, view_tokens: int) -> dict:
     }
 
 
+def alg_flops(cfg, n_blocks: int) -> float:
+    """Scoring flops the method needs per call: 2 T Hq d per block."""
+    return 2.0 * cfg.T * cfg.n_q_heads * cfg.head_dim * n_blocks
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, heads=(0, 1, 2, 3)) -> dict:
     """The oracle as it stands, timed on a sample: the whole path for a few of
     the 8 KV heads of the workspace, scaled to the full workload."""
@@ -96,6 +117,7 @@ def cpu_baseline(wl, heads=(0, 1, 2, 3)) -> dict:
     per_step = dt * cfg.n_kv_heads / len(heads)
     nb = n_tok // 32
     return {"value": nb / per_step, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus_available": len(os.sched_getaffinity(0)),
             "sample": f"whole path (index, scores, selection, view, attention) for KV heads {list(heads)} of "
                       f"{cfg.n_kv_heads} on the same workspace, {dt:.1f} s, scaled x{cfg.n_kv_heads / len(heads):.2f} "
                       f"to one step; numpy float64, BLAS threads as 'cores', elementwise work single-threaded",
@@ -126,39 +148,40 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    wl = make_workload(cfg)
-    print(f"[bench] workload {cfg.name} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
-    wss = [DeviceWorkspace(wl, dev), DeviceWorkspace(wl, dev)]
+    long_chunk = cfg.T * cfg.group > 32
+    if long_chunk:
+        # 41 GB of K/V: drawn chunk by chunk on the device, one copy (the 640 MB
+        # index already exceeds the 256 MB MALL)
+        wl = make_workload(cfg, pools=False)
+        wss = [DeviceWorkspace(wl, dev)]
+        stages = ["score_select", "materialize", "build_index"]
+    else:
+        wl = make_workload(cfg)
+        wss = [DeviceWorkspace(wl, dev), DeviceWorkspace(wl, dev)]
+        stages = ["score_select", "materialize", "attend", "build_index"]
+    print(f"[bench] workload {cfg.name} ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     for w in wss:
         w.build_index(stream)
     torch.cuda.synchronize()
 
-    stages = ["score_select", "materialize", "attend", "build_index"]
-
     def step(i, evs=None):
-        a, b = wss[i % 2], wss[(i + 1) % 2]
+        a, b = wss[i % len(wss)], wss[(i + 1) % len(wss)]
+        calls = {"score_select": a.score_select, "materialize": a.materialize, "attend": a.attend,
+                 "build_index": b.build_index}
+        for j, name in enumerate(stages):
+            if evs is not None:
+                evs[j].record(stream)
+            calls[name](stream)
         if evs is not None:
-            evs[0].record(stream)
-        a.score_select(stream)
-        if evs is not None:
-            evs[1].record(stream)
-        a.materialize(stream)
-        if evs is not None:
-            evs[2].record(stream)
-        a.attend(stream)
-        if evs is not None:
-            evs[3].record(stream)
-        b.build_index(stream)
-        if evs is not None:
-            evs[4].record(stream)
+            evs[len(stages)].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -179,9 +202,13 @@ def main():
     stage_rep = {}
     for s in stages:
         gbs = ab[s] / mean[s] / 1e9
-        stage_rep[s] = {"us": round(mean[s] * 1e6, 2), "us_p10": round(float(np.percentile(per[s], 10)) * 1e6, 2),
+        stage_rep[s] = {"us": round(mean[s] * 1e6, 2), "us_median": round(float(np.median(per[s])) * 1e6, 2),
+                        "us_p10": round(float(np.percentile(per[s], 10)) * 1e6, 2),
                         "us_p90": round(float(np.percentile(per[s], 90)) * 1e6, 2), "alg_bytes": int(ab[s]),
                         "GB/s": round(gbs, 1), "hbm_frac": round(gbs * 1e9 / HBM_PEAK, 4)}
+    fl = alg_flops(cfg, nb)
+    stage_rep["score_select"]["alg_flops"] = fl
+    stage_rep["score_select"]["TFLOP/s"] = round(fl / mean["score_select"] / 1e12, 2)
     dom = max(stages, key=lambda s: mean[s])
     ms_per_step = wall / args.steps * 1e3
     res = {
@@ -202,21 +229,28 @@ def main():
                                f"d={cfg.head_dim}, {cfg.dtype}, top-{cfg.k_select} + {cfg.n_recent} recent blocks "
                                f"-> {V:,}-token view, T={cfg.T}",
                    "blocks": nb, "view_tokens": V, "query_tokens": cfg.T},
-        "decode_step_latency_us": stage_rep["attend"]["us"],
+        "decode_step_latency_us": stage_rep["attend"]["us"] if "attend" in stage_rep else None,
+        "recall_latency_us": round(stage_rep["score_select"]["us"] + stage_rep["materialize"]["us"], 2),
         "blocks_scored_per_s_score_select": nb / mean["score_select"],
         "stages": stage_rep,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ab[dom] / mean[dom] / 1e9, 1),
-                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(ab[dom] / mean[dom] / HBM_PEAK, 4),
-                     "traffic": (MEASURED_TRAFFIC.get(dom) if args.workload == "c3"
-                                 and kernel_sources_sha() == COUNTER_SOURCES_SHA else None)},
     }
+    if long_chunk:
+        # prefill-style chunk: the scorer is a matrix-core contraction
+        res["roofline"] = {"bound": "mfma", "kernel": "score_select", "achieved": round(fl / mean["score_select"] / 1e12, 2),
+                           "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                           "frac": round(fl / mean["score_select"] / MFMA_BF16_PEAK, 4), "traffic": None}
+    else:
+        res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ab[dom] / mean[dom] / 1e9, 1),
+                           "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(ab[dom] / mean[dom] / HBM_PEAK, 4),
+                           "traffic": (MEASURED_TRAFFIC.get(dom) if args.workload == "c3"
+                                       and kernel_sources_sha() == COUNTER_SOURCES_SHA else None)}
     if args.copy_calibration:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)
         y.copy_(x)
         torch.cuda.synchronize()
         del x, y
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not long_chunk:
         print("[bench] cpu baseline (oracle sample) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl)
     else:

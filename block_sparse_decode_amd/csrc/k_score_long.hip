@@ -97,7 +97,7 @@ struct LongGeom {
 };
 
 template <bool AGG>
-__global__ __launch_bounds__(256) void k_long_pass(const uint16_t *__restrict__ index, const uint4 *__restrict__ qf,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_long_pass(const uint16_t *__restrict__ index, const uint4 *__restrict__ qf,
                                                    float2 *__restrict__ part, const float *__restrict__ lse,
                                                    float *__restrict__ A, float *__restrict__ scores,
                                                    SessI32 n_blocks, int s0, ScoreGeom g, LongGeom L) {
@@ -126,7 +126,10 @@ __global__ __launch_bounds__(256) void k_long_pass(const uint16_t *__restrict__ 
 #pragma unroll
       for (int k = 0; k < 4; ++k) a[4 * m + k] = load_nt16(t + ((4 * k + qq) * kIdxTile + 16 * m + col) * 8);
   }
-  // block b = tile * 64 + 16m + 4qq + i is valid when below nb
+  // block b = tile * 64 + 16m + 4qq + i is valid when below nb; only the last
+  // tile of a history is partial, so the masked path is rare (`full` is the
+  // same for the whole wavefront)
+  const bool full = live && (tile + 1) * kIdxTile <= nb;
   int vmask = 0;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
@@ -137,22 +140,42 @@ __global__ __launch_bounds__(256) void k_long_pass(const uint16_t *__restrict__ 
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 
+  // Staging a chunk of query fragments (and, for AGG, its rows' lse) into LDS
+  // is split in two: the global loads of chunk c + 1 are issued into
+  // registers before chunk c is multiplied, and written to LDS after it, so
+  // their latency hides behind the products.  (Plain code, no lambdas: the
+  // staging registers must stay registers.)
   const uint4 *qsrc = qf + sh * L.n_sets * 8 * 64;
-  auto stage = [&](int chunk, int buf) {
-    const int set0 = chunk * kLongChunkSets;
-    const int nset = min(kLongChunkSets, L.n_sets - set0);
-    for (int i = tid; i < nset * 8 * 64; i += 256) sb[buf][i] = qsrc[(size_t)set0 * 8 * 64 + i];
-    if (AGG && tid < kLongChunkRows) {
-      const int r = set0 * 16 + tid;
-      slse[buf][tid] = r < L.rows_pad ? lse[sh * L.rows_pad + r] : INFINITY;
-    }
-  };
+  constexpr int kPer = kLongChunkSets * 8 * 64 / 256;   // uint4 per thread per chunk
+  u32x4 pre[kPer];                                       // native vectors: HIP's uint4 here stays in scratch
+  float pre_lse = INFINITY;
+#define KVMEM_LONG_FETCH(CHUNK)                                                        \
+  {                                                                                   \
+    const int fset0 = (CHUNK) * kLongChunkSets;                                       \
+    const int fn = min(kLongChunkSets, L.n_sets - fset0) * 8 * 64;                    \
+    _Pragma("unroll") for (int j = 0; j < kPer; ++j) {                                \
+      const int i = j * 256 + tid;                                                    \
+      pre[j] = reinterpret_cast<const u32x4 *>(qsrc)[(size_t)fset0 * 8 * 64 + (i < fn ? i : 0)]; \
+    }                                                                                 \
+    if (AGG && tid < kLongChunkRows) {                                                \
+      const int r = fset0 * 16 + tid;                                                 \
+      pre_lse = r < L.rows_pad ? lse[sh * L.rows_pad + r] : INFINITY;                 \
+    }                                                                                 \
+  }
+#define KVMEM_LONG_STORE(BUF)                                                          \
+  {                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < kPer; ++j)                                 \
+        reinterpret_cast<u32x4 *>(sb[(BUF)])[j * 256 + tid] = pre[j];                 \
+    if (AGG && tid < kLongChunkRows) slse[(BUF)][tid] = pre_lse;                      \
+  }
 
-  stage(0, 0);
+  KVMEM_LONG_FETCH(0)
+  KVMEM_LONG_STORE(0)
   for (int chunk = 0; chunk < L.n_chunks; ++chunk) {
     const int buf = chunk & 1;
     __syncthreads();                                    // chunk staged; the other buffer is free
-    if (chunk + 1 < L.n_chunks) stage(chunk + 1, buf ^ 1);
+    const bool more = chunk + 1 < L.n_chunks;
+    if (more) KVMEM_LONG_FETCH(chunk + 1)
     const int set0 = chunk * kLongChunkSets;
     const int nset = min(kLongChunkSets, L.n_sets - set0);
     for (int cs = 0; cs < nset; ++cs) {
@@ -175,19 +198,33 @@ __global__ __launch_bounds__(256) void k_long_pass(const uint16_t *__restrict__ 
       const int row = (set0 + cs) * 16 + col;          // this lane's query row
       if (!AGG) {
         // the row's max and sum of 2^(s - max) over the wavefront's blocks
-        float mx = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = (vmask >> (4 * m + i)) & 1 ? fmaxf(mx, d[m][i]) : mx;
-        mx = max_xor16(mx);
-        mx = max_xor32(mx);
-        float sum = 0.f;
-        if (mx != -INFINITY) {
+        // (v_exp_f32: results below 2^-126 flush to zero, which no sum here
+        // can notice)
+        float mx = -INFINITY, sum = 0.f;
+        if (full) {
 #pragma unroll
           for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += (vmask >> (4 * m + i)) & 1 ? exp2f(d[m][i] - mx) : 0.f;
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, d[m][i]);
+          mx = max_xor16(mx);
+          mx = max_xor32(mx);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(d[m][i] - mx);
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = (vmask >> (4 * m + i)) & 1 ? fmaxf(mx, d[m][i]) : mx;
+          mx = max_xor16(mx);
+          mx = max_xor32(mx);
+          if (mx != -INFINITY) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sum += (vmask >> (4 * m + i)) & 1 ? __builtin_amdgcn_exp2f(d[m][i] - mx) : 0.f;
+          }
         }
         sum = sum_xor16(sum);
         sum = sum_xor32(sum);
@@ -207,9 +244,10 @@ __global__ __launch_bounds__(256) void k_long_pass(const uint16_t *__restrict__ 
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[4 * m + i] += exp2f(d[m][i] - lr);
+          for (int i = 0; i < 4; ++i) acc[4 * m + i] += __builtin_amdgcn_exp2f(d[m][i] - lr);
       }
     }
+    if (more) KVMEM_LONG_STORE(buf ^ 1)
     if (!AGG) {
       __syncthreads();                                  // the 4 wavefronts' row statistics
       if (tid < nset * 16) {
@@ -247,6 +285,9 @@ __global__ __launch_bounds__(256) void k_long_pass(const uint16_t *__restrict__ 
     }
   }
 }
+
+#undef KVMEM_LONG_FETCH
+#undef KVMEM_LONG_STORE
 
 // lse[row] = M + log2(sum_g S_g 2^(M_g - M)) over the row's block-group
 // partials, M = max_g M_g; padding rows get +inf.  One wavefront per row,
