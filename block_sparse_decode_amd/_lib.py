@@ -61,6 +61,14 @@ def load(path: str | None = None) -> ctypes.CDLL:
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with `python -m block_sparse_decode_amd.build`")
+    # PyTorch wheels bring their own HIP runtime.  Loading it first makes the
+    # library bind to that same runtime, so device memory allocated by torch
+    # and the library's kernels live in one runtime (loading the library first
+    # would pull in a second runtime and every launch on torch memory fails).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(p)
     lib.kvmem_index_bytes.argtypes = [POINTER(Geom), c_int32, c_int32]
     lib.kvmem_index_bytes.restype = c_size_t
