@@ -404,8 +404,10 @@ __global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, 
 
   // One segment per key in the range: the key's query loads go out before its
   // first tile load (vector loads complete in order), then the tiles stream.
-  // bf16 keeps one tile of look-ahead, and the last item re-reads its own tile
-  // (an L2 hit) so that the loads stay unconditional.
+  // bf16 keeps one tile of look-ahead.  After the last item the look-ahead
+  // reads the index's first tile instead, which every wavefront shares and the
+  // caches keep: the loads stay unconditional (a branch around them makes the
+  // compiler wait for both buffers) without costing HBM traffic.
   for (int it = i0; it < i1;) {
     const ScoreItem c0 = decode_score_item(it, sp, g.Hkv, n_blocks);
     const int end = min(i1, (c0.key + 1) * sp.ntl);
@@ -414,10 +416,10 @@ __global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, 
       RowRaw<T> ra, rb;
       load_row(ra, tile_of(it), lane);
       while (true) {
-        load_row(rb, tile_of(min(it + 1, end - 1)), lane);
+        load_row(rb, it + 1 < end ? tile_of(it + 1) : index, lane);
         compute(ra, it);
         if (++it >= end) break;
-        load_row(ra, tile_of(min(it + 1, end - 1)), lane);
+        load_row(ra, it + 1 < end ? tile_of(it + 1) : index, lane);
         compute(rb, it);
         if (++it >= end) break;
       }

@@ -189,8 +189,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 
   // One segment per key in the range: the first tile's loads go out, then the
   // key's query operands are built while they are in flight, then the tiles
-  // stream with one tile of look-ahead; the last item re-reads its own tile
-  // (an L2 hit) so that the loads stay unconditional.
+  // stream with one tile of look-ahead.  After the last item the look-ahead
+  // reads the index's first tile (shared by every wavefront, so cached): the
+  // loads stay unconditional without costing HBM traffic.
   for (int it = i0; it < i1;) {
     const ScoreItem c0 = decode_score_item(it, sp, g.Hkv, n_blocks);
     const int end = min(i1, (c0.key + 1) * sp.ntl);
@@ -198,10 +199,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     load_tile_a(ta, tile_of(it), lane);
     start_key(c0);
     while (true) {
-      load_tile_a(tb, tile_of(min(it + 1, end - 1)), lane);
+      load_tile_a(tb, it + 1 < end ? tile_of(it + 1) : index, lane);
       compute(ta, it);
       if (++it >= end) break;
-      load_tile_a(ta, tile_of(min(it + 1, end - 1)), lane);
+      load_tile_a(ta, it + 1 < end ? tile_of(it + 1) : index, lane);
       compute(tb, it);
       if (++it >= end) break;
     }
