@@ -8,9 +8,8 @@
 //
 // k_score_gemv:  a GEMV on the vector ALUs, one index row per lane, for steps
 //                of at most 8 query rows per KV head (details at the kernel).
-// k_aggregate:   merges the softmax statistics into each row's max and
-//                normaliser, then A[b] = sum_rows exp(s[row][b] - M_row) / Z_row,
-//                summed in row order.
+// Each scoring wavefront writes one (max, sum of exp) slot per query row and
+// key it met; the aggregation kernel merges them.
 #include "kvmem_internal.h"
 
 namespace kvmem {
@@ -301,9 +300,11 @@ template <typename T, int R>
 __global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, const T *__restrict__ q,
                                                    const float *__restrict__ qw, float eps,
                                                    float *__restrict__ scores, float2 *__restrict__ part,
+                                                   uint32_t *__restrict__ zero, int n_zero,
                                                    SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
   constexpr bool kPrefetch = sizeof(T) == 2;
   const int lane = threadIdx.x;
+  for (int i = blockIdx.x * 64 + lane; i < n_zero; i += gridDim.x * 64) zero[i] = 0u;
   const int n_rows = g.Tq * g.G;
   const int total = sp.n_sess * g.Hkv * sp.n_rg * sp.ntl;
   const int i0 = blockIdx.x * sp.per;                   // < total (grid = ceil(total / per))
@@ -434,80 +435,13 @@ __global__ __launch_bounds__(64) void k_score_gemv(const T *__restrict__ index, 
   }
 }
 
-__device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
-  const float M = fmaxf(a.x, b.x);
-  if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
-  return make_float2(M, a.y * expf(a.x - M) + b.y * expf(b.x - M));
-}
-
-constexpr int kAggRowsPerPass = 64;
-
-// One workgroup per (session, KV head, 256 blocks).  Each wavefront first
-// merges the statistics slots of some rows into the row's max M and 1/Z
-// (log-sum-exp merge, slots in order), then every thread owns one block and
-// sums exp(s - M) / Z over the rows in a fixed order.
-__global__ __launch_bounds__(256) void k_aggregate(const float *__restrict__ scores,
-                                                   const float2 *__restrict__ part, float *__restrict__ A,
-                                                   SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
-  __shared__ float sM[kAggRowsPerPass];
-  __shared__ float sInvZ[kAggRowsPerPass];
-  const int sl = blockIdx.z;
-  const int s = s0 + sl;
-  const int h = blockIdx.y;
-  const int nb = n_blocks.v[sl];
-  const int b0 = blockIdx.x * kAggChunk;
-  if (b0 >= nb) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int n_rows = g.Tq * g.G;
-  const int b = b0 + threadIdx.x;
-  const bool valid = b < nb;
-  float acc = 0.f;
-
-  for (int rb = 0; rb < n_rows; rb += kAggRowsPerPass) {
-    const int nr = min(kAggRowsPerPass, n_rows - rb);
-    for (int rr = wave; rr < nr; rr += 4) {
-      const int r = rb + rr;
-      const int t = r / g.G, gg = r % g.G;
-      const size_t row_id = ((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg;
-      // the wavefronts that met this row's key, in order
-      const int key = (sl * sp.n_rg + r / sp.rpg) * g.Hkv + h;
-      const int n_slots = score_n_slots(key, sp);
-      float2 ml = make_float2(-INFINITY, 0.f);
-      for (int c = lane; c < n_slots; c += 64) ml = merge_ml(ml, part[row_id * g.slot_stride + c]);
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        float2 o;
-        o.x = shfl_xor_f(ml.x, m);
-        o.y = shfl_xor_f(ml.y, m);
-        ml = merge_ml(ml, o);
-      }
-      if (lane == 0) {
-        sM[rr] = ml.x;
-        sInvZ[rr] = 1.0f / ml.y;
-      }
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int rr = 0; rr < nr; ++rr) {
-      const int r = rb + rr;
-      const int t = r / g.G, gg = r % g.G;
-      const size_t row_id = ((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg;
-      const float v = valid ? scores[row_id * g.max_blocks + b] : 0.f;
-      acc += expf(v - sM[rr]) * sInvZ[rr];
-    }
-    __syncthreads();
-  }
-  if (valid) A[((size_t)s * g.Hkv + h) * g.max_blocks + b] = acc;
-}
-
 // Wavefronts per SIMD that the scorer's grid aims for: each wavefront then
 // gets several items, so its next tile streams in while it computes.
 constexpr int kScoreWavesPerSimd = 2;
 
 template <typename T, int R>
 hipError_t launch_gemv_r(const void *index, const void *q, const float *qw, float eps, float *scores, float2 *part,
-                         const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g, int max_nb,
+                         uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g, int max_nb,
                          ScoreSplit *split, hipStream_t st) {
   static int cus = 0;                                   // compute units (device property)
   if (cus == 0) {
@@ -528,13 +462,13 @@ hipError_t launch_gemv_r(const void *index, const void *q, const float *qw, floa
   const int grid = (int)((total + sp.per - 1) / sp.per);
   *split = sp;
   hipLaunchKernelGGL((k_score_gemv<T, R>), dim3(grid), dim3(64), 0, st, (const T *)index, (const T *)q, qw, eps,
-                     scores, part, n_blocks, s0, g, sp);
+                     scores, part, zero, n_zero, n_blocks, s0, g, sp);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_gemv_t(const void *index, const void *q, const float *qw, float eps, float *scores, float2 *part,
-                         const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g, ScoreSplit *split,
+                         uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g, ScoreSplit *split,
                          hipStream_t st) {
   int max_nb = 0;
   for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
@@ -543,28 +477,18 @@ hipError_t launch_gemv_t(const void *index, const void *q, const float *qw, floa
   if (max_nb == 0) return hipSuccess;
   const int n_rows = g.Tq * g.G;
   if (n_rows <= 4)
-    return launch_gemv_r<T, 4>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
+    return launch_gemv_r<T, 4>(index, q, qw, eps, scores, part, zero, n_zero, n_blocks, s0, n_sess, g, max_nb, split, st);
   // more rows: groups of 8 rows, each re-reading the index rows
-  return launch_gemv_r<T, 8>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, max_nb, split, st);
+  return launch_gemv_r<T, 8>(index, q, qw, eps, scores, part, zero, n_zero, n_blocks, s0, n_sess, g, max_nb, split, st);
 }
 
 }  // namespace
 
 hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *scores,
-                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
-                             ScoreSplit *split, hipStream_t st) {
-  return bf16 ? launch_gemv_t<uint16_t>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, split, st)
-              : launch_gemv_t<float>(index, q, qw, eps, scores, part, n_blocks, s0, n_sess, g, split, st);
-}
-
-hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, const SessI32 &n_blocks,
-                            int s0, const ScoreGeom &g, const ScoreSplit &split, hipStream_t st) {
-  int max_nb = 0;
-  for (int i = 0; i < split.n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
-  if (max_nb == 0 || split.ntl == 0) return hipSuccess;
-  dim3 grid((unsigned)((max_nb + kAggChunk - 1) / kAggChunk), (unsigned)g.Hkv, (unsigned)split.n_sess);
-  hipLaunchKernelGGL(k_aggregate, grid, dim3(256), 0, st, scores, part, A, n_blocks, s0, g, split);
-  return hipGetLastError();
+                             float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
+                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st) {
+  return bf16 ? launch_gemv_t<uint16_t>(index, q, qw, eps, scores, part, zero, n_zero, n_blocks, s0, n_sess, g, split, st)
+              : launch_gemv_t<float>(index, q, qw, eps, scores, part, zero, n_zero, n_blocks, s0, n_sess, g, split, st);
 }
 
 }  // namespace kvmem

@@ -67,9 +67,11 @@ template <typename TQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_score_mfma(const uint16_t *__restrict__ index, const TQ *__restrict__ q,
                                                    const float *__restrict__ qw, float eps,
                                                    float *__restrict__ scores, float2 *__restrict__ part,
+                                                   uint32_t *__restrict__ zero, int n_zero,
                                                    SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
   const int lane = threadIdx.x;
   const int qq = lane >> 4, col = lane & 15;
+  for (int i = blockIdx.x * 64 + lane; i < n_zero; i += gridDim.x * 64) zero[i] = 0u;
   const int n_rows = g.Tq * g.G;
   const int total = sp.n_sess * g.Hkv * sp.n_rg * sp.ntl;
   const int i0 = blockIdx.x * sp.per;                   // < total (grid = ceil(total / per))
@@ -215,8 +217,8 @@ constexpr int kMfmaWavesPerSimd = 2;
 }  // namespace
 
 hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
-                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
-                             ScoreSplit *split, hipStream_t st) {
+                             float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
+                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st) {
   int max_nb = 0;
   for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
   split->n_sess = n_sess;
@@ -242,10 +244,10 @@ hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const
   *split = sp;
   if (bf16_q)
     hipLaunchKernelGGL(k_score_mfma<uint16_t>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index,
-                       (const uint16_t *)q, qw, eps, scores, part, n_blocks, s0, g, sp);
+                       (const uint16_t *)q, qw, eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
   else
     hipLaunchKernelGGL(k_score_mfma<float>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const float *)q,
-                       qw, eps, scores, part, n_blocks, s0, g, sp);
+                       qw, eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
   return hipGetLastError();
 }
 

@@ -1,23 +1,34 @@
-// Budgeted top-k block selection plus the recent blocks, per (session, KV head).
+// GQA aggregation and budgeted selection.
 //
-// KVMem concatenates the selected KV within the block budget (reproduction
-// README, 'Core equation'), and its recent-only control shares that budget
-// (README, 'Local reproduction').  Here: the k_eff candidates with the largest
-// aggregated score A (ties to the lower block index) are listed in ascending
-// block order, then the recent blocks, then -1 padding.
+// KVMem softmaxes each query head over the blocks and sums the heads of a KV
+// group (reproduction README, '2026-09-08 validation correction'), then keeps
+// the selected KV within the block budget (README, 'Core equation'); its
+// recent-only control shares that budget (README, 'Local reproduction').  Per
+// (session, KV head): the k_eff candidates with the largest aggregated score A
+// (ties to the lower block index) are listed in ascending block order, then
+// the recent blocks, then -1 padding.
 //
-// One 1024-thread workgroup per (session, KV head).  A >= 0, so its fp32 bit
+// k_aggregate: A[b] = sum_rows exp(s[row][b] - M_row) / Z_row for every
+//   complete block (1024 blocks per workgroup), and the candidates counted by
+//   the top digit of A's bits into the (session, head)'s selection histogram.
+// k_topk: the selection, one workgroup per (session, head), starting from
+//   that histogram when there is one.
+//
+// Selection (select_head), one 1024-thread workgroup.  A >= 0, so its fp32 bit
 // patterns order like the values.  Candidates are processed in tiles of 32768
 // keys held in registers, thread t owning the 32 consecutive keys 32t .. 32t+31
-// of a tile; a tile that covers all candidates is loaded once for the whole
-// kernel.  The exact k-th largest key t and the number of keys equal to t that
-// are taken come from an MSB-first radix select whose digits start at the
-// highest bit in which the candidates differ (found by an AND/OR reduction
-// first): A spans few binades, so digits taken from the top of the word would
-// put nearly all keys in a handful of bins and serialise the LDS histogram
-// atomics.  Ordered compaction: per thread the counts of keys above t and equal
-// to t, one block-wide scan of both (packed), then each thread writes its kept
-// blocks in index order; the output is ascending and deterministic.
+// of a tile; a tile that covers all candidates is loaded once.  The exact k-th
+// largest key t and the number of keys equal to t that are taken come from an
+// MSB-first radix select.  When the candidates have already been counted by
+// their top digit (bits 30..20), the select starts from those counts and only
+// the keys of the boundary bin take part in the remaining passes.  Otherwise
+// its digits start at the highest bit in which the candidates differ (found by
+// an AND/OR reduction first): A spans few binades, so digits taken from the top
+// of the word would put nearly all keys in a handful of bins and serialise the
+// LDS histogram atomics.  Ordered compaction: per thread the counts of keys
+// above t and equal to t, one block-wide scan of both (packed), then each
+// thread places its kept blocks in index order into an LDS window of the list,
+// which is written out coalesced; the output is ascending and deterministic.
 #include "kvmem_internal.h"
 
 namespace kvmem {
@@ -29,7 +40,18 @@ constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kEPT = 32;                              // keys per thread per tile
 constexpr int kTile = kTopkThreads * kEPT;            // 32768 keys
 constexpr int kBins = 2048;
+constexpr int kOutLds = 16384;                        // list entries staged in LDS at a time
 constexpr uint32_t kNoKey = 0xffffffffu;              // above every finite non-negative key
+static_assert(kBins == kSelBins && 31 - kSelShift == 11, "selection histogram digit");
+static_assert(kAggChunk == kTopkThreads, "one aggregated block per thread");
+
+struct SelSmem {
+  uint32_t hist[kBins];
+  uint32_t wsum[kTopkWaves];
+  uint32_t wand[kTopkWaves];
+  uint32_t digit, above;
+  int32_t out[kOutLds];
+};
 
 // Exclusive scan of one value per thread over the whole workgroup (thread order).
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
@@ -91,56 +113,78 @@ __device__ __forceinline__ void block_and_or(uint32_t &vand, uint32_t &vor, uint
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__ A, int32_t *__restrict__ view_blocks,
-                                                       TopkMeta meta, int s0, int Hkv, int max_blocks, int n_list) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wsum[kTopkWaves];
-  __shared__ uint32_t wand[kTopkWaves];
-  __shared__ uint32_t sh_digit, sh_above;
-
-  const int sl = blockIdx.y;
-  const int s = s0 + sl;
-  const int h = blockIdx.x;
+// Finds the bin of the k-th largest key from bin counts in descending order:
+// thread t owns bins kBins-1-2t and kBins-2-2t.  Sets sm.digit to the bin and
+// sm.above to the number of keys in the bins above it.
+__device__ __forceinline__ void find_bin(uint32_t c0, uint32_t c1, uint32_t krem, SelSmem &sm) {
   const int tid = threadIdx.x;
-  const int nc = meta.n_cand.v[sl];
-  const int k = meta.k_eff.v[sl];
-  const int r0 = meta.r_start.v[sl];
-  const int nall = meta.n_all.v[sl];
-  const float *a = A + ((size_t)s * Hkv + h) * max_blocks;
-  int32_t *out = view_blocks + ((size_t)s * Hkv + h) * n_list;
+  uint32_t total;
+  const uint32_t before = block_excl_scan(c0 + c1, sm.wsum, total);
+  if (before < krem && krem <= before + c0) {
+    sm.digit = kBins - 1 - 2 * tid;
+    sm.above = before;
+  } else if (before + c0 < krem && krem <= before + c0 + c1) {
+    sm.digit = kBins - 2 - 2 * tid;
+    sm.above = before + c0;
+  }
+  __syncthreads();
+}
+
+// Selection for one (session, KV head) by the whole workgroup.  a: A of the
+// candidates [0, nc); hc: their counts by top digit, or null; out: the head's
+// list of n_list entries.
+__device__ __forceinline__ void select_head(const float *a, const uint32_t *hc, int32_t *out, int nc, int k, int r0, int nall,
+                            int n_list, SelSmem &sm) {
+  const int tid = threadIdx.x;
   const bool take_all = k >= nc;
   const int n_tiles = (nc + kTile - 1) / kTile;
 
+  const bool use_hc = hc != nullptr && k > 0 && !take_all;
+  // the counts first: the bin search then overlaps the key loads
+  const uint32_t c0 = use_hc ? hc[kBins - 1 - 2 * tid] : 0u;
+  const uint32_t c1 = use_hc ? hc[kBins - 2 - 2 * tid] : 0u;
   uint32_t key[kEPT];
   if (n_tiles == 1) load_tile(a, nc, 0, key);
 
   uint32_t thr = 0, krem = 0;
   if (k > 0 && !take_all) {
-    // bits in which the candidates differ: the select only has to decide those
-    uint32_t vand = ~0u, vor = 0u;
-#pragma unroll 1
-    for (int tile = 0; tile < n_tiles; ++tile) {
-      if (n_tiles > 1) load_tile(a, nc, tile * kTile, key);
-#pragma unroll
-      for (int j = 0; j < kEPT; ++j)
-        if (key[j] != kNoKey) {
-          vand &= key[j];
-          vor |= key[j];
-        }
-    }
-    block_and_or(vand, vor, wand, wsum);
-    const uint32_t diff = vand ^ vor;
-    uint32_t prefix = vand & ~((diff == 0u) ? 0u : (0xffffffffu >> __clz(diff)));   // common high bits
+    uint32_t prefix;
+    int hi;
     krem = (uint32_t)k;
-    // digits of up to 11 bits from the highest differing bit down
-    int hi = diff == 0u ? -1 : 31 - __clz(diff);
+    if (use_hc) {
+      // the first digit's counts are given
+      if (tid == 0) sm.digit = sm.above = 0u;
+      find_bin(c0, c1, krem, sm);
+      prefix = sm.digit << kSelShift;
+      krem -= sm.above;
+      hi = kSelShift - 1;
+      __syncthreads();
+    } else {
+      // bits in which the candidates differ: the select only has to decide those
+      uint32_t vand = ~0u, vor = 0u;
+#pragma unroll 1
+      for (int tile = 0; tile < n_tiles; ++tile) {
+        if (n_tiles > 1) load_tile(a, nc, tile * kTile, key);
+#pragma unroll
+        for (int j = 0; j < kEPT; ++j)
+          if (key[j] != kNoKey) {
+            vand &= key[j];
+            vor |= key[j];
+          }
+      }
+      block_and_or(vand, vor, sm.wand, sm.wsum);
+      const uint32_t diff = vand ^ vor;
+      prefix = vand & ~((diff == 0u) ? 0u : (0xffffffffu >> __clz(diff)));   // common high bits
+      // digits of up to 11 bits from the highest differing bit down
+      hi = diff == 0u ? -1 : 31 - __clz(diff);
+    }
 #pragma unroll 1
     while (hi >= 0) {
       const int bits = hi + 1 < 11 ? hi + 1 : 11;
       const int shift = hi + 1 - bits;
       const uint32_t mask = (1u << bits) - 1u;
       const uint32_t hmask = (hi == 31) ? 0u : ~((2u << hi) - 1u);   // bits above the digit
-      for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+      for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
       __syncthreads();
 #pragma unroll 1
       for (int tile = 0; tile < n_tiles; ++tile) {
@@ -148,31 +192,23 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
 #pragma unroll
         for (int j = 0; j < kEPT; ++j) {
           const uint32_t u = key[j];
-          if (u != kNoKey && (u & hmask) == prefix) atomicAdd(&hist[(u >> shift) & mask], 1u);
+          if (u != kNoKey && (u & hmask) == prefix) atomicAdd(&sm.hist[(u >> shift) & mask], 1u);
         }
       }
       __syncthreads();
-      // bins in descending order: thread t owns bins 2047-2t and 2046-2t
-      const uint32_t c0 = hist[kBins - 1 - 2 * tid], c1 = hist[kBins - 2 - 2 * tid];
-      uint32_t total;
-      const uint32_t before = block_excl_scan(c0 + c1, wsum, total);
-      if (before < krem && krem <= before + c0) {
-        sh_digit = kBins - 1 - 2 * tid;
-        sh_above = before;
-      } else if (before + c0 < krem && krem <= before + c0 + c1) {
-        sh_digit = kBins - 2 - 2 * tid;
-        sh_above = before + c0;
-      }
-      __syncthreads();
-      prefix |= (sh_digit & mask) << shift;
-      krem -= sh_above;
+      find_bin(sm.hist[kBins - 1 - 2 * tid], sm.hist[kBins - 2 - 2 * tid], krem, sm);
+      prefix |= (sm.digit & mask) << shift;
+      krem -= sm.above;
       __syncthreads();
       hi = shift - 1;
     }
     thr = prefix;
   }
 
-  if (k > 0) {
+  // list windows of kOutLds entries: positions are recomputed per window
+#pragma unroll 1
+  for (int w0 = 0; w0 < k; w0 += kOutLds) {
+    const uint32_t wn = (uint32_t)min(kOutLds, k - w0);
     uint32_t run_gt = 0, run_eq = 0;
 #pragma unroll 1
     for (int tile = 0; tile < n_tiles; ++tile) {
@@ -187,43 +223,147 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
         n_eq += valid && !take_all && u == thr ? 1u : 0u;
       }
       uint32_t tot;
-      const uint32_t ex = block_excl_scan((n_eq << 16) | n_gt, wsum, tot);
+      const uint32_t ex = block_excl_scan((n_eq << 16) | n_gt, sm.wsum, tot);
       const uint32_t gt_before = run_gt + (ex & 0xffffu), eq_before = run_eq + (ex >> 16);
       uint32_t eq_rank = eq_before;
-      uint32_t pos = gt_before + (eq_before < krem ? eq_before : krem);
+      // list position of the thread's next kept key, relative to the window
+      // (wraps above wn while before it)
+      uint32_t p = gt_before + (eq_before < krem ? eq_before : krem) - (uint32_t)w0;
       const int base = tile * kTile + tid * kEPT;
 #pragma unroll
       for (int j = 0; j < kEPT; ++j) {
         const uint32_t u = key[j];
-        if (u == kNoKey) continue;
-        bool sel;
-        if (take_all || u > thr) {
-          sel = true;
-        } else if (u == thr) {
-          sel = eq_rank < krem;
-          ++eq_rank;
-        } else {
-          sel = false;
-        }
-        if (sel) {
-          if (pos < (uint32_t)k) out[pos] = base + j;
-          ++pos;
-        }
+        const bool valid = u != kNoKey;
+        const bool eq = valid && u == thr;
+        const bool sel = valid && (take_all || u > thr || (eq && eq_rank < krem));
+        eq_rank += eq ? 1u : 0u;
+        if (sel && p < wn) sm.out[p] = base + j;
+        p += sel ? 1u : 0u;
       }
       run_gt += tot & 0xffffu;
       run_eq += tot >> 16;
     }
+    __syncthreads();
+    for (int i = tid; i < (int)wn; i += kTopkThreads) out[w0 + i] = sm.out[i];
+    __syncthreads();
   }
   const int n_rec = nall - r0;
   for (int j = tid; j < n_list - k; j += kTopkThreads) out[k + j] = (j < n_rec) ? r0 + j : -1;
 }
 
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__ A, const uint32_t *__restrict__ hist,
+                                                       int32_t *__restrict__ view_blocks, TopkMeta meta, int s0,
+                                                       int Hkv, int max_blocks, int n_list) {
+  __shared__ SelSmem sm;
+  const int sl = blockIdx.y;
+  const int s = s0 + sl;
+  const int h = blockIdx.x;
+  const uint32_t *hc = hist ? hist + ((size_t)s * Hkv + h) * kSelBins : nullptr;
+  select_head(A + ((size_t)s * Hkv + h) * max_blocks, hc, view_blocks + ((size_t)s * Hkv + h) * n_list,
+              meta.n_cand.v[sl], meta.k_eff.v[sl], meta.r_start.v[sl], meta.n_all.v[sl], n_list, sm);
+}
+
+__device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
+  const float M = fmaxf(a.x, b.x);
+  if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
+  return make_float2(M, a.y * expf(a.x - M) + b.y * expf(b.x - M));
+}
+
+constexpr int kAggRowsPerPass = 8;
+
+// One workgroup per (session, KV head, kAggChunk blocks); thread t owns block
+// b0 + t.  Rows are taken eight at a time: every thread first requests its
+// scores of those rows, then each of eight wavefronts merges the statistics
+// slots of one row into the row's max M and 1/Z (each lane folds its slots,
+// then one DPP max and one DPP sum over the wavefront), and every thread adds
+// exp(s - M) / Z of the rows to its block in row order.  The candidates' A are
+// counted by top digit in LDS and the non-empty bins added to the selection
+// histogram with one global atomic each (the histogram was cleared by the
+// scorer earlier in the same call).
+__global__ __launch_bounds__(kAggChunk) void k_aggregate(const float *__restrict__ scores,
+                                                         const float2 *__restrict__ part, float *__restrict__ A,
+                                                         uint32_t *__restrict__ hist, SessI32 n_blocks,
+                                                         SessI32 n_cand, int s0, ScoreGeom g, ScoreSplit sp) {
+  __shared__ uint32_t shist[kBins];
+  __shared__ float sM[kAggRowsPerPass];
+  __shared__ float sInvZ[kAggRowsPerPass];
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int nb = n_blocks.v[sl];
+  const int nc = n_cand.v[sl];
+  if ((int)blockIdx.x * kAggChunk >= nb) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n_rows = g.Tq * g.G;
+  const int b = blockIdx.x * kAggChunk + tid;
+  const bool valid = b < nb;
+  uint32_t *gh = hist + ((size_t)s * g.Hkv + h) * kSelBins;
+  for (int i = tid; i < kBins; i += kAggChunk) shist[i] = 0u;
+  float acc = 0.f;
+
+  for (int rb = 0; rb < n_rows; rb += kAggRowsPerPass) {
+    const int nr = min(kAggRowsPerPass, n_rows - rb);
+    float sv[kAggRowsPerPass];
+#pragma unroll
+    for (int rr = 0; rr < kAggRowsPerPass; ++rr) {
+      if (rr >= nr) break;
+      const int r = rb + rr;
+      const size_t row_id = ((size_t)s * g.Tq + r / g.G) * g.Hq + (size_t)h * g.G + r % g.G;
+      sv[rr] = valid ? scores[row_id * g.max_blocks + b] : 0.f;
+    }
+    if (wave < nr) {
+      const int r = rb + wave;
+      const size_t row_id = ((size_t)s * g.Tq + r / g.G) * g.Hq + (size_t)h * g.G + r % g.G;
+      // the scoring wavefronts that met this row's key, in order
+      const int key = (sl * sp.n_rg + r / sp.rpg) * g.Hkv + h;
+      const int n_slots = score_n_slots(key, sp);
+      float2 ml = make_float2(-INFINITY, 0.f);
+      for (int c = lane; c < n_slots; c += 64) ml = merge_ml(ml, part[row_id * g.slot_stride + c]);
+      const float M = wave_max_dpp(ml.x);
+      const float Z = wave_sum_dpp(ml.x == -INFINITY ? 0.f : ml.y * expf(ml.x - M));
+      if (lane == 0) {
+        sM[wave] = M;
+        sInvZ[wave] = 1.0f / Z;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < kAggRowsPerPass; ++rr) {
+      if (rr >= nr) break;
+      acc += expf(sv[rr] - sM[rr]) * sInvZ[rr];
+    }
+    __syncthreads();
+  }
+
+  if (valid) A[((size_t)s * g.Hkv + h) * g.max_blocks + b] = acc;
+  if (b < nc) atomicAdd(&shist[(__float_as_uint(acc) >> kSelShift) & (kBins - 1)], 1u);
+  __syncthreads();
+  for (int i = tid; i < kBins; i += kAggChunk) {
+    const uint32_t c = shist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_topk(const float *A, int32_t *view_blocks, const TopkMeta &meta, int s0, int n_sess,
-                       int Hkv, int max_blocks, int n_list, hipStream_t st) {
+hipError_t launch_topk(const float *A, const uint32_t *hist, int32_t *view_blocks, const TopkMeta &meta, int s0,
+                       int n_sess, int Hkv, int max_blocks, int n_list, hipStream_t st) {
   dim3 grid((unsigned)Hkv, (unsigned)n_sess);
-  hipLaunchKernelGGL(k_topk, grid, dim3(kTopkThreads), 0, st, A, view_blocks, meta, s0, Hkv, max_blocks, n_list);
+  hipLaunchKernelGGL(k_topk, grid, dim3(kTopkThreads), 0, st, A, hist, view_blocks, meta, s0, Hkv, max_blocks,
+                     n_list);
+  return hipGetLastError();
+}
+
+hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, uint32_t *hist,
+                            const SessI32 &n_blocks, const SessI32 &n_cand, int s0, int n_sess, const ScoreGeom &g,
+                            const ScoreSplit &split, hipStream_t st) {
+  int max_nb = 0;
+  for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
+  if (max_nb == 0) return hipSuccess;
+  dim3 grid((unsigned)((max_nb + kAggChunk - 1) / kAggChunk), (unsigned)g.Hkv, (unsigned)n_sess);
+  hipLaunchKernelGGL(k_aggregate, grid, dim3(kAggChunk), 0, st, scores, part, A, hist, n_blocks, n_cand, s0, g, split);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ bool long_chunk(const kvmem_geom *g, int T) {
 // softmax statistics, A.  Long chunks: query operands, per-(row, block group)
 // statistics, per-row log-sum-exp, A.
 struct ScoreScratch {
-  size_t scores, part, agg, qf, lse, total;
+  size_t scores, part, agg, qf, lse, hist, total;
 };
 ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   ScoreScratch r;
@@ -70,6 +70,7 @@ ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
     r.qf = align_up(L.part_bytes);
     r.lse = r.qf + align_up(L.qf_bytes);
     r.agg = r.lse + align_up(L.lse_bytes);
+    r.hist = 0;
     r.total = r.agg + a_bytes;
     return r;
   }
@@ -79,7 +80,8 @@ ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   r.part = align_up(rows * max_blocks * sizeof(float));
   r.agg = r.part + align_up(rows * n_slots * sizeof(float2));
   r.qf = r.lse = r.agg;
-  r.total = r.agg + a_bytes;
+  r.hist = r.agg + a_bytes;
+  r.total = r.hist + align_up((size_t)S * g->n_kv_heads * kSelBins * sizeof(uint32_t));
   return r;
 }
 
@@ -204,22 +206,40 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
       tm.r_start.v[i] = sp.r_start;
       tm.n_all.v[i] = sp.n_all;
     }
+    int max_nb = 0;
+    for (int i = 0; i < n; ++i) max_nb = nb.v[i] > max_nb ? nb.v[i] : max_nb;
     if (long_chunk(geom, T)) {
       if ((st = hip_status(launch_score_long(index, q, q_norm_w, eps, (uint4 *)(base + sc.qf), part,
                                              (float *)(base + sc.lse), A, scores_opt, nb, s0, n, g, hs))) != KVMEM_OK)
         return st;
+      if (n_list > 0 &&
+          (st = hip_status(launch_topk(A, nullptr, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
+        return st;
+    } else if (max_nb == 0) {
+      // nothing to score: the lists hold the recent (partial) blocks only
+      if (n_list > 0 &&
+          (st = hip_status(launch_topk(A, nullptr, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
+        return st;
     } else {
+      // the scorer clears this launch's selection histograms, the aggregation
+      // kernel fills them and top-k starts from them
+      uint32_t *hist = (uint32_t *)(base + sc.hist);
+      uint32_t *zero = hist + (size_t)s0 * g.Hkv * kSelBins;
+      const int n_zero = n * g.Hkv * kSelBins;
       ScoreSplit split;
       const hipError_t e =
           bf16 && T * g.G > kGemvMaxRows
-              ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs)
-              : launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, nb, s0, n, g, &split, hs);
+              ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs)
+              : launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split,
+                                  hs);
       if ((st = hip_status(e)) != KVMEM_OK) return st;
-      if ((st = hip_status(launch_aggregate(scores, part, A, nb, s0, g, split, hs))) != KVMEM_OK) return st;
+      if ((st = hip_status(launch_aggregate(scores, part, A, hist, nb, tm.n_cand, s0, n, g, split, hs))) != KVMEM_OK)
+        return st;
+      if (n_list > 0 &&
+          (st = hip_status(launch_topk(A, hist, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) !=
+              KVMEM_OK)
+        return st;
     }
-    if (n_list > 0 &&
-        (st = hip_status(launch_topk(A, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
-      return st;
   }
   return KVMEM_OK;
 }

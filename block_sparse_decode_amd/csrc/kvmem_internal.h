@@ -24,7 +24,13 @@ hipError_t launch_build_index(int bf16, const void *k_pool, const int32_t *table
                               int Hkv, int max_blocks, int n_pages, hipStream_t st);
 
 // --- scoring ------------------------------------------------------------------
-constexpr int kAggChunk = 256;       // blocks per aggregation workgroup (one per thread)
+constexpr int kAggChunk = 1024;      // blocks per aggregation workgroup (one per thread)
+
+// Selection histogram per (session, KV head): the candidates' A counted by
+// the top digit of their fp32 bits (A >= 0, so bits 30..20: the exponent and
+// three significand bits).  Top-k starts its radix select from these counts.
+constexpr int kSelBins = 2048;
+constexpr int kSelShift = 20;
 
 struct ScoreGeom {
   int Tq, Hq, Hkv, G, max_blocks;
@@ -63,16 +69,18 @@ __host__ __device__ __forceinline__ int score_n_slots(int key, const ScoreSplit 
   return ((key + 1) * sp.ntl - 1) / sp.per - score_slot0(key, sp) + 1;
 }
 
+// Both scorers below also clear zero[0 .. n_zero) (the selection histograms
+// of the launch's sessions, which the aggregation kernel then fills).
 hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const float *qw, float eps, float *scores,
-                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
-                             ScoreSplit *split, hipStream_t st);
+                             float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
+                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st);
 
 // Matrix-core scorer for bf16 query chunks with more than kGemvMaxRows rows
 // per KV head (row groups of 32).
 constexpr int kGemvMaxRows = 8;
 hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
-                             float2 *part, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
-                             ScoreSplit *split, hipStream_t st);
+                             float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
+                             const ScoreGeom &g, ScoreSplit *split, hipStream_t st);
 
 // Long query chunks (bf16, more than kMfmaMaxRows rows per KV head): two passes
 // over the index on the matrix cores without storing the score matrix; writes
@@ -86,15 +94,21 @@ hipError_t launch_score_long(const void *index, const void *q, const float *qw, 
                              float *lse, float *A, float *scores_opt, const SessI32 &n_blocks, int s0, int n_sess,
                              const ScoreGeom &g, hipStream_t st);
 
-hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, const SessI32 &n_blocks,
-                            int s0, const ScoreGeom &g, const ScoreSplit &split, hipStream_t st);
-
 // --- selection ------------------------------------------------------------------
 struct TopkMeta {
   SessI32 n_cand, k_eff, r_start, n_all;
 };
-hipError_t launch_topk(const float *A, int32_t *view_blocks, const TopkMeta &meta, int s0, int n_sess,
-                       int Hkv, int max_blocks, int n_list, hipStream_t st);
+
+// A for every complete block of the scored sessions, and the candidates
+// (blocks below n_cand) counted into hist[(s * Hkv + h) * kSelBins + digit]
+// (cleared by the scorer of the same call).
+hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, uint32_t *hist,
+                            const SessI32 &n_blocks, const SessI32 &n_cand, int s0, int n_sess, const ScoreGeom &g,
+                            const ScoreSplit &split, hipStream_t st);
+
+// Selection from A; hist: the candidates' selection histograms, or null.
+hipError_t launch_topk(const float *A, const uint32_t *hist, int32_t *view_blocks, const TopkMeta &meta, int s0,
+                       int n_sess, int Hkv, int max_blocks, int n_list, hipStream_t st);
 
 // --- materialise ------------------------------------------------------------------
 hipError_t launch_materialize(int bf16, const void *k_pool, const void *v_pool, const int32_t *table,

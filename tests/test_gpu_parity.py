@@ -160,6 +160,9 @@ SMALL = {
     # more candidates than one 32768-key register tile of the selection kernel
     "multi_tile_select": small_cfg("multi_tile_select", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 36000 + 9,),
                                    k=500, R=16, n_planted=300, seed=61),
+    # a list longer than the selection kernel's 16384-entry LDS window
+    "two_list_windows": small_cfg("two_list_windows", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 18000 + 7,),
+                                  k=16_500, R=8, n_planted=100, seed=62),
 }
 
 
