@@ -28,6 +28,8 @@ EXPORTED = [
     "kvmem_materialize",
     "kvmem_attend_scratch_bytes",
     "kvmem_attend",
+    "kvmem_update_index",
+    "kvmem_append",
     "kvmem_status_string",
     "kvmem_version",
 ]
@@ -88,6 +90,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_attend.argtypes = [POINTER(Geom), c_int32, c_void_p, c_int32, c_void_p, c_float, c_void_p,
                                  c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.kvmem_attend.restype = c_int32
+    lib.kvmem_update_index.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p, c_void_p]
+    lib.kvmem_update_index.restype = c_int32
+    lib.kvmem_append.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                 c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p]
+    lib.kvmem_append.restype = c_int32
     lib.kvmem_status_string.argtypes = [c_int32]
     lib.kvmem_status_string.restype = ctypes.c_char_p
     lib.kvmem_version.argtypes = []
@@ -141,7 +148,7 @@ def make_workspace(k_pool, v_pool, block_table, n_tokens_host: np.ndarray, dev_e
                      int(k_pool.shape[0]), _p(dev_error))
 
 
-# --- the four entry points (same names as the C ABI) ------------------------
+# --- the entry points (same names as the C ABI) ------------------------------
 
 def kvmem_index_bytes(geom: Geom, n_sessions: int, max_blocks: int) -> int:
     return int(load().kvmem_index_bytes(ctypes.byref(geom), n_sessions, max_blocks))
@@ -195,6 +202,29 @@ def kvmem_attend(geom: Geom, n_sessions: int, q, T: int, q_norm_w, eps: float, k
                              scratch_bytes, _stream(stream))
     if check:
         _check(st, "kvmem_attend")
+    return st
+
+
+def kvmem_update_index(geom: Geom, ws: Workspace, first_block_host: np.ndarray | None, index, stream=None,
+                       check: bool = True) -> int:
+    if first_block_host is not None:
+        assert first_block_host.dtype == np.int32
+    st = load().kvmem_update_index(ctypes.byref(geom), ctypes.byref(ws), _p(first_block_host), _p(index),
+                                   _stream(stream))
+    if check:
+        _check(st, "kvmem_update_index")
+    return st
+
+
+def kvmem_append(geom: Geom, ws: Workspace, k_pool, v_pool, k_new, v_new, T_new: int,
+                 view_tokens_host: np.ndarray, max_view: int, rope_theta: float, k_view, v_view, stream=None,
+                 check: bool = True) -> int:
+    assert view_tokens_host.dtype == np.int32
+    st = load().kvmem_append(ctypes.byref(geom), ctypes.byref(ws), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new),
+                             T_new, _p(view_tokens_host), max_view, rope_theta, _p(k_view), _p(v_view),
+                             _stream(stream))
+    if check:
+        _check(st, "kvmem_append")
     return st
 
 

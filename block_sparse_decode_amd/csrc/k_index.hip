@@ -9,6 +9,8 @@
 // bf16 or fp32 keys is exact before the single rounding to the storage type.
 // Rows are written in the index's tiled layout (16-byte word w of 64
 // consecutive blocks contiguous), which the scorer reads fully coalesced.
+// A launch covers blocks [first_block, n_blocks) of each session: the whole
+// history, or only the blocks completed since the last update.
 #include "kvmem_internal.h"
 
 namespace kvmem {
@@ -72,7 +74,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_build_index(const T *__restrict__ kpool,
                                                      const int32_t *__restrict__ table,
                                                      T *__restrict__ index, int32_t *dev_err,
-                                                     SessI32 n_blocks, int s0, int Hkv,
+                                                     SessI32 first_block, SessI32 n_blocks, int s0, int Hkv,
                                                      int max_blocks, int n_pages) {
   const int sl = blockIdx.y;
   const int s = s0 + sl;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void k_build_index(const T *__restrict__ kpool
   // workgroup = (16 consecutive blocks, one head): each 16-byte word of the
   // 16 rows it writes is one contiguous 256-byte run of the tiled index
   const int h = (int)(blockIdx.x % Hkv);
-  const long beta = (long)(blockIdx.x / Hkv) * kJobsPerWG + (threadIdx.x >> 4);
+  const long beta = first_block.v[sl] + (long)(blockIdx.x / Hkv) * kJobsPerWG + (threadIdx.x >> 4);
   if (beta >= n_blocks.v[sl]) return;
 
   T *tile = index + (((size_t)s * Hkv + h) * idx_tiles(max_blocks) + beta / kIdxTile) * (size_t)(kIdxTile * kD);
@@ -103,18 +105,21 @@ __global__ __launch_bounds__(256) void k_build_index(const T *__restrict__ kpool
 }  // namespace
 
 hipError_t launch_build_index(int bf16, const void *k_pool, const int32_t *table, void *index,
-                              int32_t *dev_err, const SessI32 &n_blocks, int s0, int n_sess,
-                              int Hkv, int max_blocks, int n_pages, hipStream_t st) {
-  int max_nb = 0;
-  for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
+                              int32_t *dev_err, const SessI32 &first_block, const SessI32 &n_blocks, int s0,
+                              int n_sess, int Hkv, int max_blocks, int n_pages, hipStream_t st) {
+  int max_nb = 0;   // most blocks any session has to (re)build
+  for (int i = 0; i < n_sess; ++i) {
+    const int n = n_blocks.v[i] - first_block.v[i];
+    max_nb = n > max_nb ? n : max_nb;
+  }
   if (max_nb == 0) return hipSuccess;
   dim3 grid((unsigned)(((long)max_nb + kJobsPerWG - 1) / kJobsPerWG * Hkv), (unsigned)n_sess);
   if (bf16)
     hipLaunchKernelGGL(k_build_index<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)k_pool, table,
-                       (uint16_t *)index, dev_err, n_blocks, s0, Hkv, max_blocks, n_pages);
+                       (uint16_t *)index, dev_err, first_block, n_blocks, s0, Hkv, max_blocks, n_pages);
   else
     hipLaunchKernelGGL(k_build_index<float>, grid, dim3(256), 0, st, (const float *)k_pool, table,
-                       (float *)index, dev_err, n_blocks, s0, Hkv, max_blocks, n_pages);
+                       (float *)index, dev_err, first_block, n_blocks, s0, Hkv, max_blocks, n_pages);
   return hipGetLastError();
 }
 

@@ -17,67 +17,6 @@ namespace kvmem {
 
 namespace {
 
-template <typename T>
-struct Row8;
-
-template <>
-struct Row8<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t *p, float (&v)[8]) {
-    const uint4 w = load_nt16(p);
-    const uint32_t e[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = bf16_lo(e[k]);
-      v[2 * k + 1] = bf16_hi(e[k]);
-    }
-  }
-  static __device__ __forceinline__ void load_raw(const uint16_t *p, uint16_t (&v)[8]) {
-    const uint4 w = load_nt16(p);
-    const uint32_t e[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = (uint16_t)(e[k] & 0xffffu);
-      v[2 * k + 1] = (uint16_t)(e[k] >> 16);
-    }
-  }
-  // 16 raw elements from LDS (2-byte aligned) to global memory (32-byte aligned)
-  static __device__ __forceinline__ void copy16(uint16_t *dst, const uint16_t *src) {
-    uint32_t w[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = (uint32_t)src[2 * k] | ((uint32_t)src[2 * k + 1] << 16);
-    reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  }
-  static __device__ __forceinline__ void store(uint16_t *p, const float (&v)[8]) {
-    uint4 w;
-    w.x = pack_bf16x2(v[0], v[1]);
-    w.y = pack_bf16x2(v[2], v[3]);
-    w.z = pack_bf16x2(v[4], v[5]);
-    w.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4 *>(p) = w;
-  }
-};
-
-template <>
-struct Row8<float> {
-  static __device__ __forceinline__ void load(const float *p, float (&v)[8]) {
-    const float4 a = load_nt16f(p);
-    const float4 b = load_nt16f(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-  static __device__ __forceinline__ void load_raw(const float *p, float (&v)[8]) { load(p, v); }
-  static __device__ __forceinline__ void copy16(float *dst, const float *src) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      reinterpret_cast<float4 *>(dst)[k] = make_float4(src[4 * k], src[4 * k + 1], src[4 * k + 2], src[4 * k + 3]);
-  }
-  static __device__ __forceinline__ void store(float *p, const float (&v)[8]) {
-    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
-  }
-};
-
 constexpr int kVtPitch = kBT + 2;   // padded slot pitch of the LDS transpose tile
 
 template <typename T>

@@ -116,7 +116,7 @@ const char *kvmem_status_string(kvmem_status st) {
   return "unknown status";
 }
 
-int32_t kvmem_version(void) { return 200; }
+int32_t kvmem_version(void) { return 300; }
 
 size_t kvmem_index_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t max_blocks) {
   if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || max_blocks <= 0) return 0;
@@ -124,19 +124,64 @@ size_t kvmem_index_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t max
   return (size_t)n_sessions * geom->n_kv_heads * idx_tiles(max_blocks) * kIdxTile * kD * elem;
 }
 
-kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws, void *index, void *stream) {
+kvmem_status kvmem_update_index(const kvmem_geom *geom, const kvmem_workspace *ws, const int32_t *first_block_host,
+                                void *index, void *stream) {
   kvmem_status st = check_geom(geom);
   if (st != KVMEM_OK) return st;
   if ((st = check_ws(ws, false)) != KVMEM_OK) return st;
   if (!index) return KVMEM_E_ARG;
+  if (first_block_host)
+    for (int s = 0; s < ws->n_sessions; ++s)
+      if (first_block_host[s] < 0 || first_block_host[s] > ws->n_tokens_host[s] / kBT) return KVMEM_E_ARG;
   const int bf16 = geom->kv_dtype == KVMEM_BF16;
   for (int s0 = 0; s0 < ws->n_sessions; s0 += kMaxSess) {
     const int n = ws->n_sessions - s0 < kMaxSess ? ws->n_sessions - s0 : kMaxSess;
-    SessI32 nb;
+    SessI32 nb, first;
     memset(&nb, 0, sizeof(nb));
-    for (int i = 0; i < n; ++i) nb.v[i] = ws->n_tokens_host[s0 + i] / kBT;
-    st = hip_status(launch_build_index(bf16, ws->k_pool, ws->block_table, index, ws->dev_error, nb, s0, n,
+    memset(&first, 0, sizeof(first));
+    for (int i = 0; i < n; ++i) {
+      nb.v[i] = ws->n_tokens_host[s0 + i] / kBT;
+      first.v[i] = first_block_host ? first_block_host[s0 + i] : 0;
+    }
+    st = hip_status(launch_build_index(bf16, ws->k_pool, ws->block_table, index, ws->dev_error, first, nb, s0, n,
                                        geom->n_kv_heads, ws->max_blocks, ws->n_pages, (hipStream_t)stream));
+    if (st != KVMEM_OK) return st;
+  }
+  return KVMEM_OK;
+}
+
+kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws, void *index, void *stream) {
+  return kvmem_update_index(geom, ws, nullptr, index, stream);
+}
+
+kvmem_status kvmem_append(const kvmem_geom *geom, const kvmem_workspace *ws, void *k_pool, void *v_pool,
+                          const void *k_new, const void *v_new, int32_t T_new, const int32_t *view_tokens_host,
+                          int32_t max_view, float rope_theta, void *k_view, void *v_view, void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if ((st = check_ws(ws, true)) != KVMEM_OK) return st;
+  // the pools are the workspace's own, named writable here
+  if (!k_pool || !v_pool || k_pool != ws->k_pool || v_pool != ws->v_pool) return KVMEM_E_ARG;
+  if (!k_new || !v_new || !view_tokens_host || !k_view || !v_view || T_new < 0) return KVMEM_E_ARG;
+  if (max_view <= 0 || max_view % kBT != 0 || !(rope_theta > 1.0f) || !isfinite(rope_theta)) return KVMEM_E_ARG;
+  for (int s = 0; s < ws->n_sessions; ++s) {
+    if ((long)ws->n_tokens_host[s] + T_new > (long)ws->max_blocks * kBT) return KVMEM_E_ARG;
+    if (view_tokens_host[s] < 0 || (long)view_tokens_host[s] + T_new > max_view) return KVMEM_E_ARG;
+  }
+  if (T_new == 0) return KVMEM_OK;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  for (int s0 = 0; s0 < ws->n_sessions; s0 += kMaxSess) {
+    const int n = ws->n_sessions - s0 < kMaxSess ? ws->n_sessions - s0 : kMaxSess;
+    SessI32 nt, vt;
+    memset(&nt, 0, sizeof(nt));
+    memset(&vt, 0, sizeof(vt));
+    for (int i = 0; i < n; ++i) {
+      nt.v[i] = ws->n_tokens_host[s0 + i];
+      vt.v[i] = view_tokens_host[s0 + i];
+    }
+    st = hip_status(launch_append(bf16, k_pool, v_pool, ws->block_table, k_new, v_new, T_new, k_view, v_view,
+                                  ws->dev_error, nt, vt, s0, n, geom->n_kv_heads, ws->max_blocks, ws->n_pages,
+                                  max_view, (double)rope_theta, (hipStream_t)stream));
     if (st != KVMEM_OK) return st;
   }
   return KVMEM_OK;

@@ -19,9 +19,10 @@ namespace kvmem {
 constexpr int kIdxTile = 64;
 __host__ __device__ constexpr int idx_tiles(int max_blocks) { return (max_blocks + kIdxTile - 1) / kIdxTile; }
 
+// Rows of blocks [first_block, n_blocks) of each session.
 hipError_t launch_build_index(int bf16, const void *k_pool, const int32_t *table, void *index,
-                              int32_t *dev_err, const SessI32 &n_blocks, int s0, int n_sess,
-                              int Hkv, int max_blocks, int n_pages, hipStream_t st);
+                              int32_t *dev_err, const SessI32 &first_block, const SessI32 &n_blocks, int s0,
+                              int n_sess, int Hkv, int max_blocks, int n_pages, hipStream_t st);
 
 // --- scoring ------------------------------------------------------------------
 constexpr int kAggChunk = 1024;      // blocks per aggregation workgroup (one per thread)
@@ -116,6 +117,14 @@ hipError_t launch_materialize(int bf16, const void *k_pool, const void *v_pool, 
                               const SessI32 &view_tok, const SessI32 &n_all, int s0, int n_sess,
                               int Hkv, int max_blocks, int n_pages, int n_list, int max_view,
                               double theta, hipStream_t st);
+
+// --- append ---------------------------------------------------------------------
+// Writes T_new new tokens per session into the pools at history positions
+// n_tok + t and into the view at positions view_tok + t (K re-RoPE'd there).
+hipError_t launch_append(int bf16, void *k_pool, void *v_pool, const int32_t *table, const void *k_new,
+                         const void *v_new, int T_new, void *k_view, void *v_view, int32_t *dev_err,
+                         const SessI32 &n_tok, const SessI32 &view_tok, int s0, int n_sess, int Hkv, int max_blocks,
+                         int n_pages, int max_view, double theta, hipStream_t st);
 
 // --- attend ---------------------------------------------------------------------
 struct AttendGeom {

@@ -1,4 +1,4 @@
-"""Device buffers for one KV workspace and the four library calls in order.
+"""Device buffers for one KV workspace and the library calls in order.
 
 Plumbing only: torch allocates device memory; every computation is a call
 into libkvmem.so.  Used by the tests, the benchmark and the smoke check.
@@ -78,7 +78,7 @@ class DeviceWorkspace:
             self.k_pool = self._stream_pool(wl, "k")
             self.v_pool = self._stream_pool(wl, "v") if with_v else None
         self.block_table = torch.from_numpy(np.ascontiguousarray(wl.block_table, dtype=np.int32)).to(self.device)
-        self.n_tokens = np.ascontiguousarray(wl.n_tokens, dtype=np.int32)
+        self.n_tokens = np.array(wl.n_tokens, dtype=np.int32, copy=True)   # own copy: append advances it
         self.dev_error = torch.zeros(1, dtype=torch.int32, device=self.device)
         self.max_blocks = int(wl.block_table.shape[1])
         self.q = to_device(wl.q, cfg.dtype, self.device)
@@ -133,6 +133,21 @@ class DeviceWorkspace:
         L.kvmem_attend(self.geom, self.S, self.q, self.T, self.q_norm_w, self.eps, self.k_view, self.v_view,
                        self.view_tokens, self.max_view, self.theta, self.out, scratch=self.attend_scratch,
                        stream=stream)
+
+    # --- decoding over the reused view ---------------------------------------
+    def append(self, k_new, v_new, stream=None):
+        """Append T_new tokens per session ([S][T_new][Hkv][d] device tensors,
+        pre-RoPE) to the pools and the view, then index the blocks they
+        completed.  Advances the host lengths in place (the workspace struct
+        points at them)."""
+        T_new = int(k_new.shape[1])
+        L.kvmem_append(self.geom, self.ws, self.k_pool, self.v_pool, k_new, v_new, T_new, self.view_tokens,
+                       self.max_view, self.theta, self.k_view, self.v_view, stream)
+        first = (self.n_tokens // BLOCK).astype(np.int32)
+        self.n_tokens += T_new
+        self.view_tokens += T_new
+        if np.any(self.n_tokens // BLOCK > first):
+            L.kvmem_update_index(self.geom, self.ws, first, self.index, stream)
 
     def run(self, stream=None):
         self.build_index(stream)

@@ -14,6 +14,12 @@
  *                        order, re-RoPE'd to contiguous view positions.
  *   kvmem_attend         decode attention of the step's queries over the view.
  *
+ * and, for decoding many tokens over one view (step-level reuse):
+ *
+ *   kvmem_append         new tokens' K/V into the paged history and the view.
+ *   kvmem_update_index   Mean-K rows of the blocks completed since the last
+ *                        index build.
+ *
  * Sources, cited by page title and section:
  *   [README] "KVMEM: Virtualizing a million-token agent workspace with paged
  *            KV" (reproduction README): 'Background and main changes',
@@ -21,7 +27,7 @@
  *            'Local reproduction'.
  *   [REVIEW] "KVMem: Virtualizing Million-Token Agent Workspaces on a Consumer
  *            GPU" (evolve.pub review): 'Summary', 'Key claims under review',
- *            'Scope & Claims'.
+ *            'Strengths', 'Scope & Claims'.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -127,6 +133,13 @@ size_t kvmem_index_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t max
 kvmem_status kvmem_build_index(const kvmem_geom *geom, const kvmem_workspace *ws,
                                void *index, void *stream);
 
+/* Incremental form: writes the rows of blocks first_block_host[s] <= beta <
+ * n_tokens[s] / 32 only (same values as kvmem_build_index), e.g. the blocks a
+ * decode step completed.  first_block_host: HOST [n_sessions], each in
+ * [0, n_tokens[s] / 32]; NULL means 0 (then this is kvmem_build_index).     */
+kvmem_status kvmem_update_index(const kvmem_geom *geom, const kvmem_workspace *ws,
+                                const int32_t *first_block_host, void *index, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Query-conditioned block selection ([README 'Core equation']:
  * s_b = <q, k_bar_b>/sqrt(d), selected KV within the block budget;
@@ -226,6 +239,42 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions,
                           const int32_t *view_tokens_host, int32_t max_view,
                           float rope_theta, float *out,
                           void *scratch, size_t scratch_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Step-level view reuse ([REVIEW 'Scope & Claims']: recall is scheduled per
+ * agent step; [REVIEW 'Strengths']: attention is stable within a step and
+ * shifts across step boundaries).  The view selected and materialised at a
+ * step boundary serves all of the step's decode tokens; each new token's K/V
+ * is appended to both the paged history and the view, and blocks are indexed
+ * as they complete (kvmem_update_index), so the next selection sees them.
+ *
+ * For session s with history length N = n_tokens_host[s] (BEFORE the append)
+ * and view length V = view_tokens_host[s], new token t < T_new, KV head h:
+ *   K[page(s, (N+t)/32)][h][(N+t) % 32] = k_new[s][t][h]       (bit copy)
+ *   V[page(s, (N+t)/32)][h][(N+t) % 32] = v_new[s][t][h]       (bit copy)
+ *   K_view[s][h][V+t] = round( RoPE(k_new[s][t][h], position V + t) )
+ *   V_view[s][h][V+t] = v_new[s][t][h]        (at its slot, bit copy)
+ * with RoPE and rounding exactly as in kvmem_materialize, so an appended
+ * token equals the same token gathered into view position V + t.  View slots
+ * from V + T_new to the end of that 32-token view block are set to zero (the
+ * state kvmem_materialize leaves after a view's last token).  Afterwards the
+ * caller advances n_tokens_host[s] and view_tokens_host[s] by T_new; the
+ * decode queries of later steps then attend to the appended tokens.
+ *
+ * k_pool, v_pool : the workspace's pools (must equal ws->k_pool and
+ *                  ws->v_pool), written.  The block table must map the
+ *                  blocks holding positions [N, N + T_new) to pages; a bad
+ *                  page sets KVMEM_DEVERR_PAGE and skips that pool write.
+ * k_new, v_new   : [n_sessions][T_new][Hkv][d] in kv_dtype, keys pre-RoPE.
+ * k_view, v_view : as for kvmem_materialize.
+ * Requires N + T_new <= 32 * max_blocks and V + T_new <= max_view for every
+ * session; T_new = 0 does nothing.
+ * ------------------------------------------------------------------------- */
+kvmem_status kvmem_append(const kvmem_geom *geom, const kvmem_workspace *ws,
+                          void *k_pool, void *v_pool,
+                          const void *k_new, const void *v_new, int32_t T_new,
+                          const int32_t *view_tokens_host, int32_t max_view,
+                          float rope_theta, void *k_view, void *v_view, void *stream);
 
 /* Static text for a status code. */
 const char *kvmem_status_string(kvmem_status status);

@@ -306,6 +306,50 @@ def attend(qn_group: np.ndarray, k_view: np.ndarray, v_view: np.ndarray, theta: 
 
 
 # ---------------------------------------------------------------------------
+# F1  step-level view reuse ([REVIEW 'Scope & Claims']: recall is scheduled per
+#     agent step; [REVIEW 'Strengths']: attention is stable within a step and
+#     shifts across step boundaries -> the view selected at a step boundary
+#     serves the step's decode tokens, which are appended to it)
+# ---------------------------------------------------------------------------
+
+def append_history(ws: Workspace, s: int, k_new_raw: np.ndarray, v_new_raw: np.ndarray) -> Workspace:
+    """History of session s after T_new new tokens: token t is stored (bit
+    copy) at history position N + t, i.e. slot (N + t) % 32 of the page the
+    block table names for block (N + t) // 32.  k_new_raw, v_new_raw: stored
+    values [T_new][Hkv][d].  Returns a new Workspace (pools copied) with
+    n_tokens[s] advanced by T_new."""
+    kp, vp = ws.k_pool.copy(), ws.v_pool.copy()
+    n0 = int(ws.n_tokens[s])
+    for t in range(k_new_raw.shape[0]):
+        pos = n0 + t
+        page = int(ws.block_table[s, pos // BLOCK_TOKENS])
+        kp[page, :, pos % BLOCK_TOKENS] = k_new_raw[t]
+        vp[page, :, pos % BLOCK_TOKENS] = v_new_raw[t]
+    n_tok = np.array(ws.n_tokens, copy=True)
+    n_tok[s] = n0 + k_new_raw.shape[0]
+    return Workspace(kp, vp, ws.block_table, n_tok, ws.dtype, ws.n_q_heads, ws.n_kv_heads, ws.head_dim)
+
+
+def append_view(k_view: np.ndarray, v_view: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                theta: float, dtype: str):
+    """View of one KV head after appending T_new tokens: with V = len(k_view),
+    position V + t takes round_store(RoPE(k_new[t], V + t)) and v_new[t]
+    exactly (the same rule as materialisation at that position).  k_new,
+    v_new: float64 [T_new][d]."""
+    V = k_view.shape[0]
+    pos = V + np.arange(k_new.shape[0])
+    k_add = round_store(rope(k_new, pos, theta), dtype)
+    return np.concatenate([k_view, k_add]), np.concatenate([v_view, np.asarray(v_new, dtype=np.float64)])
+
+
+def update_index_rows(ws: Workspace, s: int, h: int, first_block: int) -> np.ndarray:
+    """Mean-K rows of the complete blocks first_block .. Nb - 1 (the blocks a
+    decode step completed): [Nb - first_block][d]."""
+    nb, _ = block_counts(int(ws.n_tokens[s]))
+    return mean_k_rows(ws, s, h, range(first_block, nb)) if nb > first_block else np.zeros((0, ws.head_dim))
+
+
+# ---------------------------------------------------------------------------
 # whole path for one session
 # ---------------------------------------------------------------------------
 

@@ -150,3 +150,41 @@ def test_attend_rejects(lib):
     assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
     assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head in bf16
     assert call(geom=_geom(bt=64)) == L.KVMEM_E_UNSUPPORTED
+
+
+def test_update_index_rejects(lib):
+    g = _geom()
+    ws, n = _ws()
+    first = np.array([0, 64], np.int32)          # session 1 has 2048 // 32 = 64 complete blocks
+    bad = lambda *a, **k: L.kvmem_update_index(*a, check=False, **k)
+    assert bad(g, ws, np.array([-1, 0], np.int32), 0x4000) == L.KVMEM_E_ARG
+    assert bad(g, ws, np.array([0, 65], np.int32), 0x4000) == L.KVMEM_E_ARG     # past the complete blocks
+    assert bad(g, ws, np.array([4, 0], np.int32), 0x4000) == L.KVMEM_E_ARG      # session 0 has 3 blocks
+    assert bad(g, ws, first, None) == L.KVMEM_E_ARG
+    assert bad(_geom(d=64), ws, first, 0x4000) == L.KVMEM_E_UNSUPPORTED
+
+
+def test_append_rejects(lib):
+    g = _geom()
+    ws, n = _ws(n_tok=(100, 2000))
+    vt = np.array([64, 96], np.int32)
+    kp, vp = 0x1000, 0x2000                      # the workspace's own pools
+
+    def bad(geom=g, ws_=ws, k_pool=kp, v_pool=vp, k_new=0x5000, v_new=0x6000, T_new=4, view=vt, max_view=256,
+            theta=1e6, kv=0x7000, vv=0x8000):
+        return L.kvmem_append(geom, ws_, k_pool, v_pool, k_new, v_new, T_new, view, max_view, theta, kv, vv,
+                              check=False)
+
+    assert bad(k_pool=0x1100) == L.KVMEM_E_ARG            # not the workspace's pool
+    assert bad(v_pool=None) == L.KVMEM_E_ARG
+    assert bad(k_new=None) == L.KVMEM_E_ARG
+    assert bad(kv=None) == L.KVMEM_E_ARG
+    assert bad(T_new=-1) == L.KVMEM_E_ARG
+    assert bad(max_view=250) == L.KVMEM_E_ARG             # not a multiple of 32
+    assert bad(theta=1.0) == L.KVMEM_E_ARG
+    assert bad(view=np.array([64, 253], np.int32)) == L.KVMEM_E_ARG     # view would overflow max_view
+    assert bad(T_new=49) == L.KVMEM_E_ARG                 # 2000 + 49 > 64 blocks of 32
+    assert bad(geom=_geom(bt=16)) == L.KVMEM_E_UNSUPPORTED
+    ws_nov = L.Workspace(0x1000, None, 0x3000, n.ctypes.data, 2, 64, 70, None)
+    assert bad(ws_=ws_nov, v_pool=None) == L.KVMEM_E_ARG  # V pool required
+    assert bad(T_new=0) == L.KVMEM_OK                     # nothing to do, nothing enqueued

@@ -416,3 +416,87 @@ def test_planted_blocks_are_found():
     nc, _, _ = O.recent_split(int(wl.n_tokens[0]), cfg.n_recent)
     planted = set(np.nonzero(wl.plant_mag[0, 0] > 0)[0].tolist())
     assert set(O.select_topk(A[0], nc, cfg.k_select).tolist()) == planted
+
+
+# ---------------------------------------------------------------------------
+# step-level view reuse: append and incremental index
+# ---------------------------------------------------------------------------
+
+def _decode_wl(dtype, n_tokens, extra, seed):
+    from workloads import draw_decode_tokens, with_decode_capacity
+    cfg = small_cfg(f"dec_{dtype}", dtype, S=len(n_tokens), Hq=4, Hkv=2, n_tokens=n_tokens, k=3, R=2,
+                    n_planted=2, seed=seed)
+    return with_decode_capacity(make_workload(cfg), extra), draw_decode_tokens
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_append_history_lands_at_history_positions(dtype):
+    """The appended tokens read back, through the page table directly, at
+    positions N .. N + T_new - 1; every earlier token is unchanged; the
+    blocks the append completed index to the mean of their keys."""
+    wl, draw = _decode_wl(dtype, (32 * 5 + 7, 32 * 3), 80, 71)
+    ws = oracle_ws(wl)
+    kn, vn = draw(wl.cfg, 0, 45)
+    for s in range(2):
+        n0 = int(ws.n_tokens[s])
+        ws2 = O.append_history(ws, s, kn[s], vn[s])
+        assert int(ws2.n_tokens[s]) == n0 + 45
+        wl2 = type(wl)(wl.cfg, ws2.k_pool, ws2.v_pool, wl.block_table, ws2.n_tokens, wl.q, wl.q_norm_w,
+                       wl.qhat, wl.plant_mag)
+        for h in range(2):
+            before = logical_tokens(wl, wl.k_pool, s, h)
+            after_k = logical_tokens(wl2, ws2.k_pool, s, h)
+            after_v = logical_tokens(wl2, ws2.v_pool, s, h)
+            assert np.array_equal(after_k[:n0], before)
+            assert np.array_equal(after_k[n0:], O.decode(kn[s, :, h], dtype))
+            assert np.array_equal(after_v[n0:], O.decode(vn[s, :, h], dtype))
+            # newly completed blocks: the rounded mean of their 32 keys
+            first = n0 // 32
+            rows = O.update_index_rows(ws2, s, h, first)
+            nb2 = (n0 + 45) // 32
+            assert rows.shape[0] == nb2 - first
+            for i, b in enumerate(range(first, nb2)):
+                want = O.round_store(after_k[32 * b:32 * b + 32].mean(axis=0), dtype)
+                assert np.array_equal(rows[i], want)
+            # and rows of untouched blocks equal the full index
+            full = O.mean_k_index(ws2, s, h)
+            assert np.array_equal(full[first:], rows)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_append_view_equals_gathering_the_block(dtype):
+    """Appending the 32 tokens of a block to a view of whole blocks gives
+    exactly the view that lists that block last (positions continue at V)."""
+    wl, _ = _decode_wl(dtype, (32 * 9,), 0, 72)
+    ws = oracle_ws(wl)
+    lst = np.array([1, 4, 6], np.int64)
+    theta = 1e6
+    for h in range(2):
+        kv, vv = O.materialize(ws, 0, h, lst, 96, theta)
+        blk = O.block_tokens_of(ws, ws.k_pool, 0, h, [7])[0]
+        vblk = O.block_tokens_of(ws, ws.v_pool, 0, h, [7])[0]
+        k2, v2 = O.append_view(kv, vv, blk, vblk, theta, dtype)
+        kw, vw = O.materialize(ws, 0, h, np.append(lst, 7), 128, theta)
+        assert np.array_equal(k2, kw) and np.array_equal(v2, vw)
+        # an off-by-one position would rotate the block differently
+        k_wrong = O.round_store(O.rope(blk, 97 + np.arange(32), theta), dtype)
+        assert not np.array_equal(k_wrong, kw[96:])
+
+
+def test_append_one_at_a_time_equals_all_at_once():
+    """Position bookkeeping: appending tokens one per step gives the same
+    history and view as appending them in one call."""
+    wl, draw = _decode_wl("bf16", (32 * 4 + 30,), 40, 73)
+    ws = oracle_ws(wl)
+    kn, vn = draw(wl.cfg, 1, 5)
+    theta = 1e6
+    kv0 = np.zeros((0, 128)); vv0 = np.zeros((0, 128))
+    ws_all = O.append_history(ws, 0, kn[0], vn[0])
+    k_all, v_all = O.append_view(kv0, vv0, O.decode(kn[0, :, 1], "bf16"), O.decode(vn[0, :, 1], "bf16"), theta, "bf16")
+    ws_one, k_one, v_one = ws, kv0, vv0
+    for t in range(5):
+        ws_one = O.append_history(ws_one, 0, kn[0, t:t + 1], vn[0, t:t + 1])
+        k_one, v_one = O.append_view(k_one, v_one, O.decode(kn[0, t:t + 1, 1], "bf16"),
+                                     O.decode(vn[0, t:t + 1, 1], "bf16"), theta, "bf16")
+    assert np.array_equal(ws_one.k_pool, ws_all.k_pool) and np.array_equal(ws_one.v_pool, ws_all.v_pool)
+    assert np.array_equal(k_one, k_all) and np.array_equal(v_one, v_all)

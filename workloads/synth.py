@@ -32,6 +32,12 @@ A workload may carry a key repair log (Workload.extra["repairs"]: ordered
 each entry adds delta to that coordinate of the block's 32 keys in fp32 and
 re-rounds to the storage dtype, in log order.
 
+Decoding over a reused view (with_decode_capacity, draw_decode_tokens): the
+block table gains pages for the blocks the histories grow into (new pages
+appended to the pools, NaN-filled, mapped in a seeded order), and each decode
+step's new tokens have K, V ~ N(0, 1) per element, rounded once, from the
+streams (seed, decode K or V, step).
+
 Nothing in this module computes any part of the method itself.
 """
 from __future__ import annotations
@@ -47,7 +53,7 @@ BLOCK_TOKENS = 32
 CHUNK_BLOCKS = 1024
 
 # stream ids
-_S_K, _S_V, _S_QHAT, _S_Q, _S_PLANT, _S_TABLE, _S_W, _S_LEN = range(1, 9)
+_S_K, _S_V, _S_QHAT, _S_Q, _S_PLANT, _S_TABLE, _S_W, _S_LEN, _S_DEC_K, _S_DEC_V, _S_DEC_TABLE = range(1, 12)
 
 
 def _rng(seed: int, *ids: int) -> np.random.Generator:
@@ -321,3 +327,51 @@ def make_workload(cfg: Config, threads: int | None = None, with_v: bool = True, 
     if with_v:
         _fill_pool(cfg, v_pool, table, lens, _S_V, None, qhat, threads)
     return Workload(cfg, k_pool, v_pool, table, lens.astype(np.int32), q, w, qhat, mag, extra)
+
+
+def with_decode_capacity(wl: Workload, extra_tokens: int) -> Workload:
+    """A copy of wl whose histories can each grow by extra_tokens: the blocks
+    they grow into get new pages (appended to the pools, NaN-filled) mapped in
+    the block table, whose width grows as needed."""
+    cfg = wl.cfg
+    S = cfg.n_sessions
+    lens = wl.n_tokens.astype(np.int64)
+    have = [-(-int(n) // BLOCK_TOKENS) for n in lens]
+    need = [-(-(int(n) + extra_tokens) // BLOCK_TOKENS) for n in lens]
+    n_new = int(sum(b - a for a, b in zip(have, need)))
+    max_blocks = max(wl.max_blocks, max(need) if need else 1)
+    table = np.full((S, max_blocks), -1, np.int32)
+    table[:, :wl.max_blocks] = wl.block_table
+    base = wl.n_pages
+    pages = base + _rng(cfg.seed, _S_DEC_TABLE).permutation(n_new).astype(np.int32)
+    off = 0
+    for s in range(S):
+        k = need[s] - have[s]
+        table[s, have[s]:need[s]] = pages[off:off + k]
+        off += k
+    nan = np.uint16(0x7FC0) if cfg.dtype == "bf16" else np.float32(np.nan)
+
+    def grow(pool):
+        if pool is None:
+            return None
+        extra = np.full((n_new,) + pool.shape[1:], nan, pool.dtype)
+        return np.concatenate([pool, extra], axis=0)
+
+    mag = np.zeros((S, cfg.n_kv_heads, max_blocks), np.float32)
+    mag[:, :, :wl.max_blocks] = wl.plant_mag
+    out = Workload(cfg, grow(wl.k_pool), grow(wl.v_pool) if wl.v_pool is not None and len(wl.v_pool) else wl.v_pool,
+                   table, wl.n_tokens.copy(), wl.q, wl.q_norm_w, wl.qhat, mag, dict(wl.extra))
+    if wl.k_pool is None:
+        out.extra["n_pages"] = base + n_new
+    return out
+
+
+def draw_decode_tokens(cfg: Config, step: int, T_new: int):
+    """K and V of decode step `step`'s T_new new tokens per session, pre-RoPE:
+    [S][T_new][Hkv][d] in the storage dtype (bf16 as raw uint16 bits)."""
+    shape = (cfg.n_sessions, T_new, cfg.n_kv_heads, cfg.head_dim)
+    k = _rng(cfg.seed, _S_DEC_K, step).standard_normal(shape).astype(np.float32)
+    v = _rng(cfg.seed, _S_DEC_V, step).standard_normal(shape).astype(np.float32)
+    if cfg.dtype == "bf16":
+        return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    return k, v
