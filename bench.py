@@ -124,6 +124,58 @@ def cpu_baseline(wl, heads=(0, 1, 2, 3)) -> dict:
             "seconds_per_step": per_step}
 
 
+def decode_loop(wl, dev, stream, n_dec: int) -> dict:
+    """Decoding over a reused view: one selection and gather, then n_dec
+    decode steps of (attention of one query token over the view, append of
+    that token's K/V to the history and the view, Mean-K row of each block the
+    history completes).  Timed per step with HIP events on the library's
+    stream, after the view is built."""
+    import torch
+
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace, to_device
+    from workloads import draw_decode_tokens, with_decode_capacity
+
+    cfg = wl.cfg
+    wd = with_decode_capacity(wl, n_dec)
+    V0 = int(max(DeviceWorkspace.view_length_of(wd)))
+    dw = DeviceWorkspace(wd, dev, max_view=-(-(V0 + n_dec) // 32) * 32)
+    kn, vn = draw_decode_tokens(cfg, 0, n_dec)
+    kd, vd = to_device(kn, cfg.dtype, dev), to_device(vn, cfg.dtype, dev)
+    toks = [(kd[:, t:t + 1].contiguous(), vd[:, t:t + 1].contiguous()) for t in range(n_dec)]
+    dw.build_index(stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    dw.score_select(stream)
+    ev[1].record(stream)
+    dw.materialize(stream)
+    ev[2].record(stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_dec)]
+    for t in range(n_dec):
+        evs[t][0].record(stream)
+        dw.attend(stream)
+        evs[t][1].record(stream)
+        dw.append(*toks[t], stream=stream)
+        evs[t][2].record(stream)
+    torch.cuda.synchronize()
+    att = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    app = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
+    step_us = att + app
+    recall = ev[0].elapsed_time(ev[2]) * 1e3
+    blocks_done = [t for t in range(n_dec) if (int(wl.n_tokens[0]) + t + 1) % 32 == 0]
+    plain = [t for t in range(n_dec) if t not in blocks_done]
+    return {"tokens": n_dec, "view_tokens_start": V0,
+            "step_us_median": round(float(np.median(step_us)), 2),
+            "attend_us_median": round(float(np.median(att)), 2),
+            "append_us_median": round(float(np.median(app[plain])), 2),
+            "append_with_index_update_us_median": round(float(np.median(app[blocks_done])), 2) if blocks_done else None,
+            "attend_hbm_frac": round(2 * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4) * V0
+                                     / (np.median(att) * 1e-6) / HBM_PEAK, 4),
+            "recall_us": round(recall, 2),
+            "tokens_per_s_view_reused": round(n_dec / ((recall + step_us.sum()) * 1e-6), 1),
+            "tokens_per_s_reselect_each_token": round(1.0 / ((recall + float(np.median(att))) * 1e-6), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +183,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-tokens", type=int, default=256,
+                    help="decode steps over one reused view after the timed steps (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run one plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -229,7 +283,7 @@ def main():
                                f"d={cfg.head_dim}, {cfg.dtype}, top-{cfg.k_select} + {cfg.n_recent} recent blocks "
                                f"-> {V:,}-token view, T={cfg.T}",
                    "blocks": nb, "view_tokens": V, "query_tokens": cfg.T},
-        "decode_step_latency_us": stage_rep["attend"]["us"] if "attend" in stage_rep else None,
+        "decode_step_latency_us": None,
         "recall_latency_us": round(stage_rep["score_select"]["us"] + stage_rep["materialize"]["us"], 2),
         "blocks_scored_per_s_score_select": nb / mean["score_select"],
         "stages": stage_rep,
@@ -244,6 +298,13 @@ def main():
                            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(ab[dom] / mean[dom] / HBM_PEAK, 4),
                            "traffic": (MEASURED_TRAFFIC.get(dom) if args.workload == "c3"
                                        and kernel_sources_sha() == COUNTER_SOURCES_SHA else None)}
+    if not long_chunk and args.decode_tokens > 0:
+        wss.clear()                                   # frees the two timed workspaces
+        torch.cuda.empty_cache()
+        print(f"[bench] decode loop over one reused view ({args.decode_tokens} tokens) ...", file=sys.stderr, flush=True)
+        dec = decode_loop(wl, dev, stream, args.decode_tokens)
+        res["decode"] = dec
+        res["decode_step_latency_us"] = dec["step_us_median"]
     if args.copy_calibration:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)

@@ -22,6 +22,14 @@ namespace kvmem {
 
 namespace {
 
+// 8 elements (16 or 32 bytes, 16-byte aligned) copied bit for bit.
+template <typename T>
+__device__ __forceinline__ void copy8(T *dst, const T *src) {
+#pragma unroll
+  for (int k = 0; k < (int)sizeof(T) / 2; ++k)
+    reinterpret_cast<uint4 *>(dst)[k] = reinterpret_cast<const uint4 *>(src)[k];
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__restrict__ vpool,
                                                 const int32_t *__restrict__ table, const T *__restrict__ knew,
@@ -29,6 +37,7 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
                                                 T *__restrict__ vview, int32_t *dev_err, SessI32 n_tok,
                                                 SessI32 view_tok, int s0, int Hkv, int max_blocks, int n_pages,
                                                 int max_view, double theta) {
+  __shared__ double inv_freq[kD / 2];
   const int t = blockIdx.x;
   const int sl = blockIdx.y;
   const int s = s0 + sl;
@@ -40,29 +49,26 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
   const bool page_ok = page >= 0 && page < n_pages;
   if (!page_ok && threadIdx.x == 0) dev_flag(dev_err, 1);
 
+  if (threadIdx.x < kD / 2) inv_freq[threadIdx.x] = rope_inv_freq(threadIdx.x, theta);
+  __syncthreads();
   float cs[8], sn[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) rope_cos_sin((double)vpos, rope_inv_freq(8 * j + e, theta), cs[e], sn[e]);
+  for (int e = 0; e < 8; ++e) rope_cos_sin((double)vpos, inv_freq[8 * j + e], cs[e], sn[e]);
 
   const int m = vpos / kBT;
   const int slot = v_slot(vpos % kBT);
   for (int h = threadIdx.x >> 3; h < Hkv; h += blockDim.x / 8) {
     const size_t src = (((size_t)s * T_new + t) * Hkv + h) * kD;
-    T k1[8], k2[8], v1[8], v2[8];
-    Row8<T>::load_raw(knew + src + 8 * j, k1);
-    Row8<T>::load_raw(knew + src + 64 + 8 * j, k2);
+    T v1[8], v2[8];
     Row8<T>::load_raw(vnew + src + 8 * j, v1);
     Row8<T>::load_raw(vnew + src + 64 + 8 * j, v2);
-    // history: bit copies at (page, head, token of the block)
+    // history: bit copies at (page, head, token of the block), 16 bytes a time
     if (page_ok) {
       const size_t dst = (((size_t)page * Hkv + h) * kBT + hist % kBT) * kD;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kpool[dst + 8 * j + e] = k1[e];
-        kpool[dst + 64 + 8 * j + e] = k2[e];
-        vpool[dst + 8 * j + e] = v1[e];
-        vpool[dst + 64 + 8 * j + e] = v2[e];
-      }
+      copy8(kpool + dst + 8 * j, knew + src + 8 * j);
+      copy8(kpool + dst + 64 + 8 * j, knew + src + 64 + 8 * j);
+      copy8(vpool + dst + 8 * j, vnew + src + 8 * j);
+      copy8(vpool + dst + 64 + 8 * j, vnew + src + 64 + 8 * j);
     }
     // view: K rotated at position vpos and rounded; V at its slot
     float x1[8], x2[8], y1[8], y2[8];
@@ -83,10 +89,11 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
       vb[(size_t)(64 + 8 * j + e) * kBT + slot] = v2[e];
     }
     // The slots after the new view length up to the end of its 32-token view
-    // block stay zero, as the gather leaves them (the attention masks their
-    // logits, and zero V keeps the masked products finite).  Only the last
-    // token's workgroup writes them: no other workgroup touches those slots.
-    if (t == T_new - 1) {
+    // block must be zero, as the gather leaves them (the attention masks their
+    // logits, and zero V keeps the masked products finite).  They already are
+    // unless this append opened that view block; then the last token's
+    // workgroup clears them (no other workgroup touches those slots).
+    if (t == T_new - 1 && m * kBT >= view_tok.v[sl]) {
       const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int z = vpos + 1; z < (m + 1) * kBT; ++z) {
         T *kz = kview + (((size_t)s * Hkv + h) * max_view + z) * kD;

@@ -419,38 +419,41 @@ __global__ __launch_bounds__(256) void k_attend_f32(const float *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// merge of the splits (fixed order -> deterministic): one workgroup per
-// (session, KV head, query row); 8 groups of 32 threads each take every 8th
-// split for 4 dimensions, then the groups are added in order.
-// ---------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials of one (session, KV head, query row).
-// 256 threads = 8 split groups x 32 float4 slices of the row; each thread
-// folds its splits with an online rescale (no separate max and sum passes, four
-// splits in flight), then the 8 groups are folded in a fixed order, so the
+// Log-sum-exp merge of the split partials of one (session, KV head, query
+// row), one workgroup per quarter of the row's 128 dimensions: 256 threads =
+// 32 split groups x 8 float4 slices of the quarter.  Each thread folds every
+// 32nd split with an online rescale (no separate max and sum passes, four
+// splits in flight), then the 32 groups are folded in a fixed order, so the
 // result is deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kCombGroups = 32;
+constexpr int kCombQuarters = 4;
+
 __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict__ part_o,
                                                         const float2 *__restrict__ part_ml, float *__restrict__ out,
                                                         SessI32 view_tok, int s0, AttendGeom g) {
-  __shared__ float4 acc_s[8][32];
-  __shared__ float m_s[8], l_s[8];
+  __shared__ float4 acc_s[kCombGroups][8];
+  __shared__ float m_s[kCombGroups], l_s[kCombGroups];
   const int sl = blockIdx.z;
   const int s = s0 + sl;
   const int h = blockIdx.y;
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / kCombQuarters;
+  const int quarter = blockIdx.x % kCombQuarters;
   const int tid = threadIdx.x;
   const int V = view_tok.v[sl];
   const int split_tok = 4 * g.tpw;
   const int n = (V + split_tok - 1) / split_tok;
   if (n == 1) return;                     // written by the attention kernel itself
   const int t = row / g.G, gg = row % g.G;
-  float *dst = out + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
+  float *dst = out + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + quarter * (kD / kCombQuarters);
   if (n == 0) {
-    if (tid < kD) dst[tid] = 0.f;
+    if (tid < kD / kCombQuarters) dst[tid] = 0.f;
     return;
   }
   const size_t head = (size_t)s * g.Hkv + h;
   const size_t base = head * g.max_splits * g.rows + row;     // + i * rows
-  const int sg = tid >> 5, q4 = tid & 31;
+  const int sg = tid >> 3, q4 = tid & 7;
+  const int slice = quarter * 8 + q4;                         // float4 slice of the row
   float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   auto fold = [&](float2 ml, float4 v) {
@@ -463,21 +466,21 @@ __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict_
     m = mn;
   };
   int i = sg;
-  for (; i + 24 < n; i += 32) {
+  for (; i + 3 * kCombGroups < n; i += 4 * kCombGroups) {
     float2 ml[4];
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const size_t pidx = base + (size_t)(i + 8 * u) * g.rows;
+      const size_t pidx = base + (size_t)(i + kCombGroups * u) * g.rows;
       ml[u] = part_ml[pidx];
-      v[u] = reinterpret_cast<const float4 *>(part_o + pidx * kD)[q4];
+      v[u] = reinterpret_cast<const float4 *>(part_o + pidx * kD)[slice];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) fold(ml[u], v[u]);
   }
-  for (; i < n; i += 8) {
+  for (; i < n; i += kCombGroups) {
     const size_t pidx = base + (size_t)i * g.rows;
-    fold(part_ml[pidx], reinterpret_cast<const float4 *>(part_o + pidx * kD)[q4]);
+    fold(part_ml[pidx], reinterpret_cast<const float4 *>(part_o + pidx * kD)[slice]);
   }
   acc_s[sg][q4] = acc;
   if (q4 == 0) {
@@ -485,12 +488,11 @@ __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict_
     l_s[sg] = l;
   }
   __syncthreads();
-  if (tid < 32) {
+  if (tid < 8) {
     m = -INFINITY;
     l = 0.f;
     acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) fold(make_float2(m_s[j], l_s[j]), acc_s[j][tid]);
+    for (int j = 0; j < kCombGroups; ++j) fold(make_float2(m_s[j], l_s[j]), acc_s[j][tid]);
     const float inv = 1.0f / l;
     reinterpret_cast<float4 *>(dst)[tid] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
@@ -534,7 +536,7 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 cgrid((unsigned)g.rows, (unsigned)g.Hkv, (unsigned)n_sess);
+  dim3 cgrid((unsigned)(g.rows * kCombQuarters), (unsigned)g.Hkv, (unsigned)n_sess);
   hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
   return hipGetLastError();
 }

@@ -106,6 +106,13 @@ class DeviceWorkspace:
         self.eps = cfg.eps
         self.theta = cfg.rope_theta
 
+    @staticmethod
+    def view_length_of(wl, k_select=None, n_recent=None) -> list:
+        """View tokens of every session of a workload (host arithmetic on the lengths)."""
+        k = wl.cfg.k_select if k_select is None else k_select
+        r = wl.cfg.n_recent if n_recent is None else n_recent
+        return [view_length(int(n), k, r) for n in wl.n_tokens]
+
     def _stream_pool(self, wl, which: str) -> torch.Tensor:
         from workloads import pool_chunks
         cfg = wl.cfg

@@ -256,8 +256,10 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions,
  *   V_view[s][h][V+t] = v_new[s][t][h]        (at its slot, bit copy)
  * with RoPE and rounding exactly as in kvmem_materialize, so an appended
  * token equals the same token gathered into view position V + t.  View slots
- * from V + T_new to the end of that 32-token view block are set to zero (the
- * state kvmem_materialize leaves after a view's last token).  Afterwards the
+ * from V + T_new to the end of that 32-token view block are zero afterwards:
+ * a view block the append opens is cleared past the new end, and a block
+ * already holding view tokens keeps the zeros kvmem_materialize (or an
+ * earlier append) left after the view's last token.  Afterwards the
  * caller advances n_tokens_host[s] and view_tokens_host[s] by T_new; the
  * decode queries of later steps then attend to the appended tokens.
  *

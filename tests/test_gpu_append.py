@@ -1,8 +1,9 @@
 """GPU parity of decoding over a reused view (append + incremental index),
 through the C ABI, against the CPU oracle.
 
-After one selection and gather, two appends (45 then 35 tokens: they cross
-history-block and view-block boundaries) each followed by attention.  Bars:
+After one selection and gather, three appends (45, 35, 3 tokens: the first two cross
+history-block and view-block boundaries, the third does not) each followed by
+attention.  Bars:
 pools bit-exact (every page, spare pages included), index rows bit-exact, V
 view bit-exact, K view within one bf16 ulp (the gather's bar), the view's tail
 slots zero, attention within the attention bar.
@@ -27,7 +28,7 @@ CASES = {
     "f32_g4": small_cfg("dec_f32_g4", "f32", S=2, Hq=8, Hkv=2, n_tokens=(32 * 200 + 31, 32 * 40),
                         k=10, R=2, n_planted=4, seed=82),
 }
-STEPS = (45, 35)
+STEPS = (45, 35, 3)             # the third stays inside a view block the second opened
 
 
 def _raw_bits(t: torch.Tensor) -> np.ndarray:
