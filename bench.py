@@ -176,6 +176,47 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
             "tokens_per_s_reselect_each_token": round(1.0 / ((recall + float(np.median(att))) * 1e-6), 1)}
 
 
+def mass_diagnostic(wl, dev, stream, reps: int = 5) -> dict:
+    """Selection-quality diagnostic: share of full attention over the history
+    that the selected blocks carry, and that the recent-only control (the
+    recent blocks alone, same list length) carries.  Timed with HIP events;
+    the kernel streams every history key once."""
+    import torch
+
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace
+
+    cfg = wl.cfg
+    dw = DeviceWorkspace(wl, dev, with_v=False)
+    dw.build_index(stream)
+    dw.score_select(stream)
+    S, H, T, Hq = cfg.n_sessions, cfg.n_kv_heads, cfg.T, cfg.n_q_heads
+    n_tok = int(wl.n_tokens[0])
+    nb_all = -(-n_tok // 32)
+    r0 = max(0, nb_all - cfg.n_recent)
+    rec = torch.full((S, H, dw.n_list), -1, dtype=torch.int32, device=dev)
+    rec[:, :, :nb_all - r0] = torch.arange(r0, nb_all, dtype=torch.int32, device=dev)
+    mass = torch.empty((S, T, Hq), device=dev)
+    m_rec = torch.empty((S, T, Hq), device=dev)
+    dw.attention_mass(mass, stream=stream)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dw.attention_mass(mass, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    dw.attention_mass(m_rec, view_blocks=rec, stream=stream)
+    torch.cuda.synchronize()
+    t = float(np.median(ts))
+    nbytes = n_tok * H * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+    return {"mass_selected_mean": round(float(mass.mean()), 4), "mass_selected_min": round(float(mass.min()), 4),
+            "mass_recent_only_mean": round(float(m_rec.mean()), 4),
+            "blocks_selected": cfg.k_select, "blocks_recent": cfg.n_recent,
+            "us": round(t * 1e6, 2), "alg_bytes": nbytes, "hbm_frac": round(nbytes / t / HBM_PEAK, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +224,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-diagnostic", action="store_true",
+                    help="skip the selection-quality diagnostic after the timed steps")
     ap.add_argument("--decode-tokens", type=int, default=256,
                     help="decode steps over one reused view after the timed steps (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -305,6 +348,9 @@ def main():
         dec = decode_loop(wl, dev, stream, args.decode_tokens)
         res["decode"] = dec
         res["decode_step_latency_us"] = dec["step_us_median"]
+    if not long_chunk and not args.no_diagnostic:
+        print("[bench] selection-quality diagnostic ...", file=sys.stderr, flush=True)
+        res["selection_quality"] = mass_diagnostic(wl, dev, stream)
     if args.copy_calibration:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)

@@ -30,6 +30,8 @@ EXPORTED = [
     "kvmem_attend",
     "kvmem_update_index",
     "kvmem_append",
+    "kvmem_attention_mass_scratch_bytes",
+    "kvmem_attention_mass",
     "kvmem_status_string",
     "kvmem_version",
 ]
@@ -95,6 +97,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_append.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                  c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p]
     lib.kvmem_append.restype = c_int32
+    lib.kvmem_attention_mass_scratch_bytes.argtypes = [POINTER(Geom), c_int32, c_int32, c_int32]
+    lib.kvmem_attention_mass_scratch_bytes.restype = c_size_t
+    lib.kvmem_attention_mass.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
+                                         c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.kvmem_attention_mass.restype = c_int32
     lib.kvmem_status_string.argtypes = [c_int32]
     lib.kvmem_status_string.restype = ctypes.c_char_p
     lib.kvmem_version.argtypes = []
@@ -225,6 +232,23 @@ def kvmem_append(geom: Geom, ws: Workspace, k_pool, v_pool, k_new, v_new, T_new:
                              _stream(stream))
     if check:
         _check(st, "kvmem_append")
+    return st
+
+
+def kvmem_attention_mass_scratch_bytes(geom: Geom, n_sessions: int, T: int, max_blocks: int) -> int:
+    return int(load().kvmem_attention_mass_scratch_bytes(ctypes.byref(geom), n_sessions, T, max_blocks))
+
+
+def kvmem_attention_mass(geom: Geom, ws: Workspace, q, T: int, q_norm_w, eps: float, view_blocks, n_list: int,
+                         rope_theta: float, mass, lse=None, scratch=None, scratch_bytes: int | None = None,
+                         stream=None, check: bool = True) -> int:
+    if scratch_bytes is None:
+        scratch_bytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    st = load().kvmem_attention_mass(ctypes.byref(geom), ctypes.byref(ws), _p(q), T, _p(q_norm_w), eps,
+                                     _p(view_blocks), n_list, rope_theta, _p(mass), _p(lse), _p(scratch),
+                                     scratch_bytes, _stream(stream))
+    if check:
+        _check(st, "kvmem_attention_mass")
     return st
 
 

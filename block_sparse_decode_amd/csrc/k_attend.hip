@@ -419,6 +419,307 @@ __global__ __launch_bounds__(256) void k_attend_f32(const float *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
+// Selection-quality diagnostic: the share of full attention over the whole
+// history that the listed blocks capture.  Full attention here is attention
+// over a full-budget view: every history token j rotated at its own position
+// and rounded to storage, the query token t at position N + t.
+//
+// k_mass_bf16: one workgroup of 8 wavefronts per (session, chunk of history
+// blocks, group of 8 KV heads); wavefront w serves KV head 8 * group + w.  For
+// each block the workgroup first forms the 32 x 64 RoPE (cos, sin) table of the
+// block's positions (shared by the 8 heads), then each wavefront rotates the
+// pre-RoPE K tile of its head, read straight from the page in the A-operand
+// lane layout (a dim and its +-64 partner sit in chunks c and c ^ 2 of the same
+// lane), rounds it to bf16 and forms S^T = K Q^T on the matrix cores with the
+// same query operands as the view attention.  Online softmax statistics (log2
+// units) are kept over all tokens and over the tokens of listed blocks; each
+// wavefront writes one (m_all, l_all, m_sel, l_sel) per query row and chunk.
+// k_mass_combine folds the chunks in order into mass = l_sel / l_all (after
+// rescaling) and the log-sum-exp of the logits.
+// ---------------------------------------------------------------------------
+constexpr int kMassWaves = 8;
+constexpr int kMassMaxChunk = 256;
+
+__device__ __forceinline__ void mass_fold(float &m, float &l, float bm, float bl) {
+  if (bm == -INFINITY) return;
+  const float mn = fmaxf(m, bm);
+  l = l * exp2f(m - mn) + bl * exp2f(bm - mn);
+  m = mn;
+}
+
+template <int NT>
+__global__ __launch_bounds__(512) void k_mass_bf16(const uint16_t *__restrict__ q, const float *__restrict__ qw,
+                                                   float eps, const uint16_t *__restrict__ kpool,
+                                                   const int32_t *__restrict__ table,
+                                                   const int32_t *__restrict__ vblocks, float4 *__restrict__ part,
+                                                   int32_t *dev_err, SessI32 n_tok, int s0, MassGeom g,
+                                                   double theta) {
+  __shared__ double inv_freq[kD / 2];
+  __shared__ double step_cs[kD / 2][2];                  // cos, sin of 32 * phi_i
+  __shared__ float cs_tab[kQprepMaxT][kD / 2][2];        // query positions N + t
+  __shared__ float ktab[2][kBT][kD / 2][2];              // positions of the current block
+  __shared__ uint8_t listed[kMassWaves][kMassMaxChunk];
+
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int chunk = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qq = lane >> 4;
+  const int col = lane & 15;
+  const int h = blockIdx.y * kMassWaves + wave;
+  const bool head_ok = h < g.Hkv;
+  const int N = n_tok.v[sl];
+  const int n_all = (N + kBT - 1) / kBT;
+  const int b0 = chunk * g.chunk;
+  if (b0 >= n_all) return;                             // uniform over the workgroup
+  const int b1 = min(n_all, b0 + g.chunk);
+
+  if (tid < kD / 2) {
+    inv_freq[tid] = rope_inv_freq(tid, theta);
+    sincos((double)kBT * inv_freq[tid], &step_cs[tid][1], &step_cs[tid][0]);
+  }
+  for (int i = tid; i < kMassWaves * kMassMaxChunk; i += 512) listed[i / kMassMaxChunk][i % kMassMaxChunk] = 0;
+
+  // raw query rows of this wavefront's head (as the view attention)
+  float x[NT][4][8];
+  int trow[NT];
+  bool rvalid[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = nt * 16 + col;
+    rvalid[nt] = head_ok && r < g.rows;
+    const int t = rvalid[nt] ? r / g.G : 0, gg = rvalid[nt] ? r % g.G : 0;
+    trow[nt] = t;
+    const uint16_t *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)(head_ok ? h : 0) * g.G + gg) * kD + 8 * qq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(src + 32 * c);
+      const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[nt][c][2 * k] = bf16_lo(e[k]);
+        x[nt][c][2 * k + 1] = bf16_hi(e[k]);
+      }
+    }
+  }
+  __syncthreads();                                     // inv_freq, cleared flags
+
+  // listed blocks of this chunk: the list's valid entries ascend (selected,
+  // then recent, then -1), so a coarse probe per lane finds the segment that
+  // holds the first entry >= b0, and the chunk's entries follow it
+  if (head_ok && g.n_list > 0) {
+    const int32_t *lst = vblocks + ((size_t)s * g.Hkv + h) * g.n_list;
+    const int step = (g.n_list + 63) / 64;
+    const int probe = lane * step;
+    const uint32_t e = probe < g.n_list ? (uint32_t)lst[probe] : 0xffffffffu;   // -1 -> above every block
+    const uint64_t below = __ballot(probe < g.n_list && e < (uint32_t)b0);
+    const int start = below == 0 ? 0 : (63 - __clzll(below)) * step;
+    for (int k = lane; k < step + g.chunk; k += 64) {
+      const int idx = start + k;
+      if (idx < g.n_list) {
+        const int v = lst[idx];
+        if (v >= b0 && v < b1) listed[wave][v - b0] = 1;
+      }
+    }
+  }
+  {
+    const int n_t = (g.rows + g.G - 1) / g.G;
+    for (int idx = tid; idx < n_t * (kD / 2); idx += 512) {
+      const int t = idx / (kD / 2), i = idx % (kD / 2);
+      rope_cos_sin((double)(N + t), inv_freq[i], cs_tab[t][i][0], cs_tab[t][i][1]);
+    }
+  }
+  __syncthreads();
+  bf16x8 qhi[NT][4], qlo[NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) build_q_operands(x[nt], rvalid[nt], trow[nt], qq, qw, eps, cs_tab, qhi[nt], qlo[nt]);
+
+  float m_all[NT], l_all[NT], m_sel[NT], l_sel[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_all[nt] = m_sel[nt] = -INFINITY;
+    l_all[nt] = l_sel[nt] = 0.f;
+  }
+  const int32_t *trow_tab = table + (size_t)s * g.max_blocks;
+  auto tile_src = [&](int beta, bool &ok) -> const uint16_t * {
+    const int page = trow_tab[beta];
+    ok = head_ok && page >= 0 && page < g.n_pages;
+    return kpool + ((size_t)(ok ? page : 0) * g.Hkv + (head_ok ? h : 0)) * (size_t)(kBT * kD);
+  };
+  uint4 kr[2][4];
+  bool ok_cur;
+  const uint16_t *src = tile_src(b0, ok_cur);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(src + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+
+  // RoPE table of the current block's positions, shared by the 8 heads: each
+  // thread owns 4 of its 32 x 64 entries, exact at the chunk's first block
+  // and advanced one block (angle + 32 phi_i) per step by an fp64 rotation.
+  constexpr int kOwn = kBT * (kD / 2) / 512;
+  double tc[kOwn], ts[kOwn];
+#pragma unroll
+  for (int k = 0; k < kOwn; ++k) {
+    const int idx = tid + 512 * k;
+    const int u = idx / (kD / 2), i = idx % (kD / 2);
+    float c, sn;
+    rope_cos_sin((double)(kBT * b0 + u), inv_freq[i], c, sn);
+    tc[k] = c;
+    ts[k] = sn;
+  }
+
+  for (int beta = b0; beta < b1; ++beta) {
+    const int buf = (beta - b0) & 1;
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      const int idx = tid + 512 * k;
+      ktab[buf][idx / (kD / 2)][idx % (kD / 2)][0] = (float)tc[k];
+      ktab[buf][idx / (kD / 2)][idx % (kD / 2)][1] = (float)ts[k];
+      const double sc = step_cs[idx % (kD / 2)][0], ss = step_cs[idx % (kD / 2)][1];
+      const double c2 = tc[k] * sc - ts[k] * ss;
+      ts[k] = ts[k] * sc + tc[k] * ss;
+      tc[k] = c2;
+    }
+    __syncthreads();
+    const bool ok = ok_cur;
+    if (!ok && head_ok && lane == 0) dev_flag(dev_err, 1);
+    uint4 cur[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cur[tt][c] = kr[tt][c];
+    if (beta + 1 < b1) {
+      src = tile_src(beta + 1, ok_cur);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(src + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+    }
+    if (!ok) continue;                                 // per wavefront: no barrier below
+    // rotate K at its own positions and round to bf16: A operands
+    bf16x8 ka[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int u = 16 * tt + col;
+      float kv[4][8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t e[4] = {cur[tt][c].x, cur[tt][c].y, cur[tt][c].z, cur[tt][c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          kv[c][2 * k] = bf16_lo(e[k]);
+          kv[c][2 * k + 1] = bf16_hi(e[k]);
+        }
+      }
+      uint32_t w[4][4];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          float y1[2], y2[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int ip = 32 * c + 8 * qq + j + k;
+            const float cs = ktab[buf][u][ip][0], sn = ktab[buf][u][ip][1];
+            y1[k] = kv[c][j + k] * cs - kv[c + 2][j + k] * sn;
+            y2[k] = kv[c + 2][j + k] * cs + kv[c][j + k] * sn;
+          }
+          w[c][j / 2] = pack_bf16x2(y1[0], y1[1]);
+          w[c + 2][j / 2] = pack_bf16x2(y2[0], y2[1]);
+        }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ka[tt][c] = as_bf16x8(make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]));
+    }
+    const bool sel = listed[wave][beta - b0] != 0;
+    const int tb = kBT * beta;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      floatx4 sc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        floatx4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][c], qhi[nt][c], a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][c], qlo[nt][c], a, 0, 0, 0);
+        }
+        sc[tt] = a;
+      }
+      if (tb + kBT > N) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tb + 16 * tt + 4 * qq + i >= N) sc[tt][i] = -INFINITY;
+      }
+      float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      bm = max_xor16(bm);
+      bm = max_xor32(bm);                              // block max of the row, in every lane of the row
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps += exp2f(sc[0][i] - bm) + exp2f(sc[1][i] - bm);
+      mass_fold(m_all[nt], l_all[nt], bm, ps);        // lane-partial sums, common maxima
+      if (sel) mass_fold(m_sel[nt], l_sel[nt], bm, ps);
+    }
+  }
+  if (!head_ok) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float la = sum_xor32(sum_xor16(l_all[nt]));
+    const float ls = sum_xor32(sum_xor16(l_sel[nt]));
+    const int row = nt * 16 + col;
+    if (qq == 0 && row < g.rows)
+      part[(((size_t)s * g.Hkv + h) * g.n_chunks + chunk) * g.rows + row] = make_float4(m_all[nt], la, m_sel[nt], ls);
+  }
+}
+
+// One wavefront per (session, KV head, query row): folds the chunks' partials
+// (lane c takes chunks c, c + 64, ...; then a fixed butterfly order).
+__global__ __launch_bounds__(64) void k_mass_combine(const float4 *__restrict__ part, float *__restrict__ mass,
+                                                     float *__restrict__ lse, SessI32 n_tok, int s0, MassGeom g) {
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int n_all = (n_tok.v[sl] + kBT - 1) / kBT;
+  const int nc = (n_all + g.chunk - 1) / g.chunk;
+  float ma = -INFINITY, la = 0.f, ms = -INFINITY, ls = 0.f;
+  for (int c = lane; c < nc; c += 64) {
+    const float4 p = part[(((size_t)s * g.Hkv + h) * g.n_chunks + c) * g.rows + row];
+    mass_fold(ma, la, p.x, p.y);
+    mass_fold(ms, ls, p.z, p.w);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float oma = __shfl_xor(ma, off, 64), ola = __shfl_xor(la, off, 64);
+    const float oms = __shfl_xor(ms, off, 64), ols = __shfl_xor(ls, off, 64);
+    // both partners fold the same two values in the same order (lower lane first)
+    float am = (lane & off) ? oma : ma, al = (lane & off) ? ola : la;
+    float bm = (lane & off) ? ma : oma, bl = (lane & off) ? la : ola;
+    mass_fold(am, al, bm, bl);
+    ma = am;
+    la = al;
+    float sm_ = (lane & off) ? oms : ms, sl_ = (lane & off) ? ols : ls;
+    float tm = (lane & off) ? ms : oms, tl = (lane & off) ? ls : ols;
+    mass_fold(sm_, sl_, tm, tl);
+    ms = sm_;
+    ls = sl_;
+  }
+  if (lane == 0) {
+    const int t = row / g.G, gg = row % g.G;
+    const size_t o = ((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg;
+    const float m = (ms == -INFINITY || la == 0.f) ? 0.f : ls * exp2f(ms - ma) / la;
+    mass[o] = m;
+    if (lse) lse[o] = la == 0.f ? -INFINITY : (ma + log2f(la)) * 0.6931471805599453f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Log-sum-exp merge of the split partials of one (session, KV head, query
 // row), one workgroup per quarter of the row's 128 dimensions: 256 threads =
 // 32 split groups x 8 float4 slices of the quarter.  Each thread folds every
@@ -539,6 +840,44 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
   dim3 cgrid((unsigned)(g.rows * kCombQuarters), (unsigned)g.Hkv, (unsigned)n_sess);
   hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
   return hipGetLastError();
+}
+
+}  // namespace kvmem
+
+namespace kvmem {
+
+hipError_t launch_mass(const void *q, const float *qw, float eps, const void *k_pool, const int32_t *table,
+                       const int32_t *view_blocks, float4 *part, float *mass, float *lse, int32_t *dev_err,
+                       const SessI32 &n_tok, int s0, int n_sess, const MassGeom &g, double theta, hipStream_t st) {
+  int max_all = 0;
+  for (int i = 0; i < n_sess; ++i) {
+    const int n = (n_tok.v[i] + kBT - 1) / kBT;
+    max_all = n > max_all ? n : max_all;
+  }
+  const int groups = (g.Hkv + kMassWaves - 1) / kMassWaves;
+  if (max_all > 0) {
+    dim3 grid((unsigned)((max_all + g.chunk - 1) / g.chunk), (unsigned)groups, (unsigned)n_sess);
+    if (g.rows <= 16)
+      hipLaunchKernelGGL(k_mass_bf16<1>, grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,
+                         (const uint16_t *)k_pool, table, view_blocks, part, dev_err, n_tok, s0, g, theta);
+    else
+      hipLaunchKernelGGL(k_mass_bf16<2>, grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,
+                         (const uint16_t *)k_pool, table, view_blocks, part, dev_err, n_tok, s0, g, theta);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 cgrid((unsigned)g.rows, (unsigned)g.Hkv, (unsigned)n_sess);
+  hipLaunchKernelGGL(k_mass_combine, cgrid, dim3(64), 0, st, part, mass, lse, n_tok, s0, g);
+  return hipGetLastError();
+}
+
+int mass_chunk(int n_sessions, int Hkv, int max_blocks) {
+  // aim for >= 256 workgroups; 8 .. 256 blocks per chunk
+  const long groups = (Hkv + kMassWaves - 1) / kMassWaves;
+  long c = ((long)max_blocks * groups * n_sessions + 255) / 256;
+  if (c < 8) c = 8;
+  if (c > kMassMaxChunk) c = kMassMaxChunk;
+  return (int)c;
 }
 
 }  // namespace kvmem

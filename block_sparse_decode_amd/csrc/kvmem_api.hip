@@ -289,6 +289,52 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
   return KVMEM_OK;
 }
 
+size_t kvmem_attention_mass_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T, int32_t max_blocks) {
+  if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || max_blocks <= 0 || T <= 0) return 0;
+  const int chunk = mass_chunk(n_sessions, geom->n_kv_heads, max_blocks);
+  const size_t n_chunks = (size_t)((max_blocks + chunk - 1) / chunk);
+  const size_t rows = (size_t)T * (geom->n_q_heads / geom->n_kv_heads);
+  return align_up((size_t)n_sessions * geom->n_kv_heads * n_chunks * rows * sizeof(float4));
+}
+
+kvmem_status kvmem_attention_mass(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
+                                  const float *q_norm_w, float eps, const int32_t *view_blocks, int32_t n_list,
+                                  float rope_theta, float *mass, float *lse_opt, void *scratch, size_t scratch_bytes,
+                                  void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if ((st = check_ws(ws, false)) != KVMEM_OK) return st;
+  if (!q || !q_norm_w || !mass || T <= 0 || n_list < 0 || (n_list > 0 && !view_blocks)) return KVMEM_E_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps) || !(rope_theta > 1.0f) || !isfinite(rope_theta)) return KVMEM_E_ARG;
+  const int G = geom->n_q_heads / geom->n_kv_heads;
+  if (geom->kv_dtype != KVMEM_BF16 || (long)T * G > kMfmaMaxRows) return KVMEM_E_UNSUPPORTED;
+  const int S = ws->n_sessions;
+  if ((long)S * geom->n_kv_heads * n_list >= (1L << 31)) return KVMEM_E_UNSUPPORTED;
+  const size_t need = kvmem_attention_mass_scratch_bytes(geom, S, T, ws->max_blocks);
+  if (!scratch || scratch_bytes < need) return KVMEM_E_WORKSPACE;
+  MassGeom g;
+  g.Tq = T;
+  g.Hq = geom->n_q_heads;
+  g.Hkv = geom->n_kv_heads;
+  g.G = G;
+  g.rows = T * G;
+  g.max_blocks = ws->max_blocks;
+  g.n_pages = ws->n_pages;
+  g.n_list = n_list;
+  g.chunk = mass_chunk(S, geom->n_kv_heads, ws->max_blocks);
+  g.n_chunks = (ws->max_blocks + g.chunk - 1) / g.chunk;
+  for (int s0 = 0; s0 < S; s0 += kMaxSess) {
+    const int n = S - s0 < kMaxSess ? S - s0 : kMaxSess;
+    SessI32 nt;
+    memset(&nt, 0, sizeof(nt));
+    for (int i = 0; i < n; ++i) nt.v[i] = ws->n_tokens_host[s0 + i];
+    st = hip_status(launch_mass(q, q_norm_w, eps, ws->k_pool, ws->block_table, view_blocks, (float4 *)scratch, mass,
+                                lse_opt, ws->dev_error, nt, s0, n, g, (double)rope_theta, (hipStream_t)stream));
+    if (st != KVMEM_OK) return st;
+  }
+  return KVMEM_OK;
+}
+
 kvmem_status kvmem_materialize(const kvmem_geom *geom, const kvmem_workspace *ws, const int32_t *view_blocks,
                                int32_t n_list, const int32_t *view_tokens_host, int32_t max_view, float rope_theta,
                                void *k_view, void *v_view, void *stream) {

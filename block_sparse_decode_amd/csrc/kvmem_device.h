@@ -42,12 +42,12 @@ __device__ __forceinline__ float4 load_nt16f(const void *p) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, nearest with ties to even (NaN kept quiet).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, nearest with ties to even (gfx950's conversion
+// instruction; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | (u >> 16);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // y = hi + lo with hi = bf16(y) and lo = bf16(y - hi): a product with a bf16
@@ -57,8 +57,10 @@ __device__ __forceinline__ void split_hi_lo(float y, uint32_t &hi, uint32_t &lo)
   lo = f32_to_bf16(y - __uint_as_float(hi << 16));
 }
 
+// Two fp32 -> packed bf16 (lo in bits 0..15), one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // fp64 -> bf16 bits with a single rounding (nearest, ties to even).  The

@@ -138,4 +138,15 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
                          hipStream_t st);
 
+// --- selection-quality diagnostic ------------------------------------------------
+struct MassGeom {
+  int Tq, Hq, Hkv, G, rows, max_blocks, n_pages, n_list;
+  int chunk;      // history blocks per workgroup
+  int n_chunks;   // chunk slots per (session, head) in the partials
+};
+int mass_chunk(int n_sessions, int Hkv, int max_blocks);
+hipError_t launch_mass(const void *q, const float *qw, float eps, const void *k_pool, const int32_t *table,
+                       const int32_t *view_blocks, float4 *part, float *mass, float *lse, int32_t *dev_err,
+                       const SessI32 &n_tok, int s0, int n_sess, const MassGeom &g, double theta, hipStream_t st);
+
 }  // namespace kvmem

@@ -156,6 +156,18 @@ class DeviceWorkspace:
         if np.any(self.n_tokens // BLOCK > first):
             L.kvmem_update_index(self.geom, self.ws, first, self.index, stream)
 
+    # --- selection-quality diagnostic ---------------------------------------
+    def attention_mass(self, mass, lse=None, view_blocks=None, n_list=None, stream=None):
+        """Share of full attention over the history that the listed blocks
+        carry (default: the current selection's lists)."""
+        vb = self.view_blocks if view_blocks is None else view_blocks
+        nl = self.n_list if n_list is None else n_list
+        if not hasattr(self, "mass_scratch"):
+            nbytes = L.kvmem_attention_mass_scratch_bytes(self.geom, self.S, self.T, self.max_blocks)
+            self.mass_scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        L.kvmem_attention_mass(self.geom, self.ws, self.q, self.T, self.q_norm_w, self.eps, vb, nl, self.theta,
+                               mass, lse, scratch=self.mass_scratch, stream=stream)
+
     def run(self, stream=None):
         self.build_index(stream)
         self.score_select(stream)

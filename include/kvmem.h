@@ -20,6 +20,11 @@
  *   kvmem_update_index   Mean-K rows of the blocks completed since the last
  *                        index build.
  *
+ * and a selection-quality diagnostic:
+ *
+ *   kvmem_attention_mass share of full attention over the whole history that
+ *                        the listed blocks capture.
+ *
  * Sources, cited by page title and section:
  *   [README] "KVMEM: Virtualizing a million-token agent workspace with paged
  *            KV" (reproduction README): 'Background and main changes',
@@ -277,6 +282,41 @@ kvmem_status kvmem_append(const kvmem_geom *geom, const kvmem_workspace *ws,
                           const void *k_new, const void *v_new, int32_t T_new,
                           const int32_t *view_tokens_host, int32_t max_view,
                           float rope_theta, void *k_view, void *v_view, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Selection-quality diagnostic ([REVIEW 'Strengths']: a few top blocks carry
+ * most of the attention mass, which motivates block selection; [README 'Local
+ * reproduction']: selection is compared with full attention and with the
+ * recent-only control at the same budget).
+ *
+ * Full attention over the history is attention over a full-budget view:
+ * every history token j < N = n_tokens[s] with its key rotated at its own
+ * position and rounded to kv_dtype, the query token t at position N + t
+ * (q~ and RoPE as in kvmem_attend, the step's tokens attend to the history
+ * only).  For session s, query token t and query head g:
+ *   l_j         = <RoPE(q~[t][g], N + t), round(RoPE(K[j], j))> / sqrt(d)
+ *   mass[t][g]  = sum over tokens j of the blocks listed in
+ *                 view_blocks[s][h(g)][0 .. n_list) of softmax_j(l)
+ *   lse[t][g]   = log sum_j exp(l_j)                  (natural log)
+ * with the partial tail block's valid tokens included.  Listed entries must
+ * ascend and be followed only by -1 padding (the layout kvmem_score_select
+ * writes); entries outside [0, ceil(N/32)) are ignored.  mass is 0 for an
+ * empty history or list.  Pass the selection's list for the method's mass and
+ * a list of the recent blocks only for the recent-only control.
+ *
+ * q, q_norm_w, eps : as for kvmem_score_select (T * G <= 32).
+ * mass, lse_opt    : [n_sessions][T][Hq] fp32 (lse_opt may be NULL).
+ * scratch          : at least kvmem_attention_mass_scratch_bytes() bytes.
+ * Reads the K pool only (v_pool may be NULL).  bf16 workspaces only
+ * (KVMEM_E_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+size_t kvmem_attention_mass_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T,
+                                          int32_t max_blocks);
+kvmem_status kvmem_attention_mass(const kvmem_geom *geom, const kvmem_workspace *ws,
+                                  const void *q, int32_t T, const float *q_norm_w, float eps,
+                                  const int32_t *view_blocks, int32_t n_list, float rope_theta,
+                                  float *mass, float *lse_opt,
+                                  void *scratch, size_t scratch_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *kvmem_status_string(kvmem_status status);

@@ -350,6 +350,42 @@ def update_index_rows(ws: Workspace, s: int, h: int, first_block: int) -> np.nda
 
 
 # ---------------------------------------------------------------------------
+# F3  selection-quality diagnostic ([REVIEW 'Strengths']: a few top blocks
+#     carry most of the attention mass; [README 'Local reproduction']: the
+#     selection is compared with full attention and the recent-only control)
+# ---------------------------------------------------------------------------
+
+def attention_mass(qn_group: np.ndarray, keys: np.ndarray, listed_blocks, theta: float, dtype: str):
+    """Share of full attention over the history that the listed blocks carry.
+
+    Full attention = attention over a full-budget view: history token j's key
+    rotated at position j and stored-rounded, query token t at position N + t
+    (N = len(keys)).  keys: pre-RoPE keys [N][d] float64 of one KV head, in
+    history order; listed_blocks: block indices (entries outside the history
+    are ignored).  Returns (mass [T][G], lse [T][G]) with lse the natural
+    log-sum-exp of the logits.  An empty history gives mass 0, lse -inf.
+    """
+    T, G, d = qn_group.shape
+    N = keys.shape[0]
+    if N == 0:
+        return np.zeros((T, G)), np.full((T, G), -np.inf)
+    kfull = round_store(rope(keys, np.arange(N), theta), dtype)
+    pos = (N + np.arange(T, dtype=np.float64))[:, None]
+    qr = rope(qn_group, np.broadcast_to(pos, (T, G)), theta)
+    logits = (qr.reshape(T * G, d) @ kfull.T) / np.sqrt(d)
+    mx = logits.max(axis=-1, keepdims=True)
+    z = np.exp(logits - mx)
+    tot = z.sum(axis=-1)
+    in_list = np.zeros(N, bool)
+    for b in np.asarray(listed_blocks, dtype=np.int64):
+        if 0 <= b and BLOCK_TOKENS * b < N:
+            in_list[BLOCK_TOKENS * b:BLOCK_TOKENS * (b + 1)] = True
+    mass = z[:, in_list].sum(axis=-1) / tot
+    lse = mx[:, 0] + np.log(tot)
+    return mass.reshape(T, G), lse.reshape(T, G)
+
+
+# ---------------------------------------------------------------------------
 # whole path for one session
 # ---------------------------------------------------------------------------
 

@@ -500,3 +500,76 @@ def test_append_one_at_a_time_equals_all_at_once():
                                      O.decode(vn[0, t:t + 1, 1], "bf16"), theta, "bf16")
     assert np.array_equal(ws_one.k_pool, ws_all.k_pool) and np.array_equal(ws_one.v_pool, ws_all.v_pool)
     assert np.array_equal(k_one, k_all) and np.array_equal(v_one, v_all)
+
+
+# ---------------------------------------------------------------------------
+# selection-quality diagnostic
+# ---------------------------------------------------------------------------
+
+def _mass_case(seed=91, n_tok=32 * 37 + 11, T=2):
+    rng = np.random.default_rng(seed)
+    d = 128
+    keys = O.round_bf16(rng.standard_normal((n_tok, d)))
+    q = rng.standard_normal((T, 4, d)) * 0.3 + 1.0
+    qn = O.q_rmsnorm(q, np.ones(d), 1e-6)
+    return qn, keys
+
+
+def test_attention_mass_closed_forms_and_additivity():
+    qn, keys = _mass_case()
+    nb_all = -(-keys.shape[0] // 32)
+    full, lse = O.attention_mass(qn, keys, np.arange(nb_all), 1e6, "bf16")
+    assert np.allclose(full, 1.0, atol=1e-13)
+    empty, lse2 = O.attention_mass(qn, keys, [], 1e6, "bf16")
+    assert np.all(empty == 0) and np.array_equal(lse, lse2)
+    a, _ = O.attention_mass(qn, keys, [0, 5, 9, nb_all - 1], 1e6, "bf16")
+    b, _ = O.attention_mass(qn, keys, [1, 2, 30], 1e6, "bf16")
+    ab, _ = O.attention_mass(qn, keys, [0, 1, 2, 5, 9, 30, nb_all - 1], 1e6, "bf16")
+    assert np.allclose(a + b, ab, atol=1e-14)
+    ign, _ = O.attention_mass(qn, keys, [0, 5, 9, nb_all - 1, nb_all + 3, -1], 1e6, "bf16")
+    assert np.array_equal(ign, a)                              # entries outside the history are ignored
+    assert np.all(O.attention_mass(np.zeros((1, 1, 128)), np.zeros((0, 128)), [0], 1e6, "bf16")[0] == 0)
+
+
+def test_attention_mass_against_complex_rope_and_torch():
+    """Independent weights: RoPE written with complex numbers, softmax and
+    logsumexp from torch in float64."""
+    qn, keys = _mass_case(seed=92, n_tok=32 * 21 + 5, T=3)
+    T, G, d = qn.shape
+    N = keys.shape[0]
+    theta = 1e6
+    freq = theta ** (-np.arange(64) * 2.0 / d)
+
+    def crope(x, pos):
+        z = (x[..., :64] + 1j * x[..., 64:]) * np.exp(1j * np.asarray(pos, dtype=np.float64)[..., None] * freq)
+        return np.concatenate([z.real, z.imag], axis=-1)
+
+    kr = O.round_bf16(crope(keys, np.arange(N)))
+    qr = crope(qn, (N + np.arange(T))[:, None] * np.ones((1, G)))
+    logits = torch.from_numpy(np.einsum("tgd,jd->tgj", qr, kr) / np.sqrt(d))
+    p = torch.softmax(logits, dim=-1).numpy()
+    listed = [0, 3, 4, 11, 21]
+    tok = np.concatenate([np.arange(32 * b, min(N, 32 * b + 32)) for b in listed])
+    mass, lse = O.attention_mass(qn, keys, listed, theta, "bf16")
+    assert np.allclose(mass, p[..., tok].sum(axis=-1), atol=1e-12)
+    assert np.allclose(lse, torch.logsumexp(logits, dim=-1).numpy(), atol=1e-10)
+
+
+def test_attention_mass_is_attention_over_the_full_view():
+    """Mass of one block = the attention output over a full-budget view whose
+    values are that block's indicator (same query position N + t)."""
+    wl = make_workload(small_cfg("mass_view", "bf16", S=1, Hq=8, Hkv=2, n_tokens=(32 * 12 + 9,), T=2, k=2, R=1,
+                                 n_planted=2, seed=93))
+    ws = oracle_ws(wl)
+    N = int(wl.n_tokens[0])
+    nb_all = -(-N // 32)
+    qn = O.q_rmsnorm(O.decode(wl.q[0], "bf16"), wl.q_norm_w, wl.cfg.eps)
+    for h in range(2):
+        kv, _ = O.materialize(ws, 0, h, np.arange(nb_all), N, 1e6)
+        keys = logical_tokens(wl, wl.k_pool, 0, h)
+        for b in (0, 4, nb_all - 1):
+            vv = np.zeros((N, 128))
+            vv[32 * b:min(N, 32 * b + 32), 0] = 1.0
+            o = O.attend(qn[:, 4 * h:4 * h + 4], kv, vv, 1e6)
+            mass, _ = O.attention_mass(qn[:, 4 * h:4 * h + 4], keys, [b], 1e6, "bf16")
+            assert np.allclose(o[..., 0], mass, atol=1e-13)
