@@ -176,6 +176,46 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
             "tokens_per_s_reselect_each_token": round(1.0 / ((recall + float(np.median(att))) * 1e-6), 1)}
 
 
+def paged_vs_view(wl, dev, stream, reps: int = 10) -> dict:
+    """Attention straight from the pages against gather + attention over the
+    view, on the same selection (HIP events, medians).  A view serving n
+    decode tokens costs materialize + n * attend; reading the pages costs
+    n * paged."""
+    import torch
+
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace
+
+    cfg = wl.cfg
+    dw = DeviceWorkspace(wl, dev)
+    dw.build_index(stream)
+    dw.score_select(stream)
+    dw.materialize(stream)
+    dw.attend(stream)
+    dw.attend_paged(stream=stream)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    t_mat = timed(dw.materialize)
+    t_att = timed(dw.attend)
+    t_pg = timed(lambda st: dw.attend_paged(stream=st))
+    V = int(dw.view_tokens[0])
+    nbytes = 2 * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4) * V
+    breakeven = t_mat / (t_pg - t_att) if t_pg > t_att else None
+    return {"paged_us": round(t_pg, 2), "paged_hbm_frac": round(nbytes / (t_pg * 1e-6) / HBM_PEAK, 4),
+            "view_attend_us": round(t_att, 2), "materialize_us": round(t_mat, 2),
+            "tokens_per_view_breakeven": None if breakeven is None else round(breakeven, 1)}
+
+
 def mass_diagnostic(wl, dev, stream, reps: int = 5) -> dict:
     """Selection-quality diagnostic: share of full attention over the history
     that the selected blocks carry, and that the recent-only control (the
@@ -349,6 +389,8 @@ def main():
         res["decode"] = dec
         res["decode_step_latency_us"] = dec["step_us_median"]
     if not long_chunk and not args.no_diagnostic:
+        print("[bench] attention from the pages vs gather + view attention ...", file=sys.stderr, flush=True)
+        res["paged_attend"] = paged_vs_view(wl, dev, stream)
         print("[bench] selection-quality diagnostic ...", file=sys.stderr, flush=True)
         res["selection_quality"] = mass_diagnostic(wl, dev, stream)
     if args.copy_calibration:

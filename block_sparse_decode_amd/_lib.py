@@ -30,6 +30,8 @@ EXPORTED = [
     "kvmem_attend",
     "kvmem_update_index",
     "kvmem_append",
+    "kvmem_attend_paged_scratch_bytes",
+    "kvmem_attend_paged",
     "kvmem_attention_mass_scratch_bytes",
     "kvmem_attention_mass",
     "kvmem_status_string",
@@ -97,6 +99,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_append.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                  c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p]
     lib.kvmem_append.restype = c_int32
+    lib.kvmem_attend_paged_scratch_bytes.argtypes = [POINTER(Geom), c_int32, c_int32, c_int32]
+    lib.kvmem_attend_paged_scratch_bytes.restype = c_size_t
+    lib.kvmem_attend_paged.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
+                                       c_void_p, c_int32, c_void_p, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.kvmem_attend_paged.restype = c_int32
     lib.kvmem_attention_mass_scratch_bytes.argtypes = [POINTER(Geom), c_int32, c_int32, c_int32]
     lib.kvmem_attention_mass_scratch_bytes.restype = c_size_t
     lib.kvmem_attention_mass.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
@@ -232,6 +239,23 @@ def kvmem_append(geom: Geom, ws: Workspace, k_pool, v_pool, k_new, v_new, T_new:
                              _stream(stream))
     if check:
         _check(st, "kvmem_append")
+    return st
+
+
+def kvmem_attend_paged_scratch_bytes(geom: Geom, n_sessions: int, T: int, n_list: int) -> int:
+    return int(load().kvmem_attend_paged_scratch_bytes(ctypes.byref(geom), n_sessions, T, n_list))
+
+
+def kvmem_attend_paged(geom: Geom, ws: Workspace, q, T: int, q_norm_w, eps: float, view_blocks, n_list: int,
+                       view_tokens_host: np.ndarray, rope_theta: float, out, scratch=None,
+                       scratch_bytes: int | None = None, stream=None, check: bool = True) -> int:
+    if scratch_bytes is None:
+        scratch_bytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    st = load().kvmem_attend_paged(ctypes.byref(geom), ctypes.byref(ws), _p(q), T, _p(q_norm_w), eps,
+                                   _p(view_blocks), n_list, _p(view_tokens_host), rope_theta, _p(out), _p(scratch),
+                                   scratch_bytes, _stream(stream))
+    if check:
+        _check(st, "kvmem_attend_paged")
     return st
 
 

@@ -28,7 +28,8 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 SOURCES = ["kvmem_api.hip", "k_index.hip", "k_score.hip", "k_score_mfma.hip", "k_score_long.hip", "k_select.hip", "k_materialize.hip",
-           "k_attend.hip", "k_append.hip"]
+           "k_attend.hip", "k_append.hip",
+           "k_attend_paged.hip"]
 
 
 def hipcc() -> str:

@@ -24,61 +24,11 @@
 //
 // fp32 path (k_attend_f32): a plain vector-ALU kernel with the same split and
 // merge structure (logits and probabilities staged in LDS).
-#include "kvmem_internal.h"
+#include "attend_common.h"
 
 namespace kvmem {
 
 namespace {
-
-constexpr float kLog2eRsqrtD = 0.12751743074480953f;   // log2(e) / sqrt(128)
-constexpr int kQprepMaxT = 32;                          // query tokens per step in the bf16 path
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
-
-
-// Query operands of the matrix-core products for the 16 rows of operand set nt:
-// q~ (RMSNorm, weight), RoPE at V + t, scaled by log2(e)/sqrt(d), split into
-// bf16 hi + lo, in the B-operand lane layout.  Lane (qq, col) holds row
-// 16*nt + col; its chunk c holds dims 32c + 8qq .. +7, so the RoPE partner of
-// a dim (+-64) sits in chunk c ^ 2 of the same lane.  x holds the row's raw
-// values, cs_tab the (cos, sin) of every (query token, frequency).
-__device__ __forceinline__ void build_q_operands(const float (&x)[4][8], bool valid, int t, int qq, const float *qw,
-                                                 float eps, const float (*cs_tab)[kD / 2][2], bf16x8 (&qhi)[4],
-                                                 bf16x8 (&qlo)[4]) {
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ss += x[c][j] * x[c][j];
-  ss = sum_xor16(ss);
-  ss = sum_xor32(ss);
-  const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-  float y[4][8];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) y[c][j] = x[c][j] * rs * qw[32 * c + 8 * qq + j];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      uint32_t h2[2], l2[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int ip = 32 * (c & 1) + 8 * qq + j + k;          // pair index (dim mod 64)
-        const float cs = cs_tab[t][ip][0], sn = cs_tab[t][ip][1];
-        const float xo = y[c][j + k], xp = y[c ^ 2][j + k];
-        const float r = (c < 2 ? xo * cs - xp * sn : xo * cs + xp * sn) * kLog2eRsqrtD;
-        split_hi_lo(valid ? r : 0.f, h2[k], l2[k]);
-      }
-      hw[j / 2] = h2[0] | (h2[1] << 16);
-      lw[j / 2] = l2[0] | (l2[1] << 16);
-    }
-    qhi[c] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    qlo[c] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-  }
-}
 
 struct KVTile {
   uint4 k[2][4];
@@ -837,6 +787,11 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return launch_attend_combine(part_o, part_ml, out, view_tok, s0, n_sess, g, st);
+}
+
+hipError_t launch_attend_combine(const float *part_o, const float2 *part_ml, float *out, const SessI32 &view_tok,
+                                 int s0, int n_sess, const AttendGeom &g, hipStream_t st) {
   dim3 cgrid((unsigned)(g.rows * kCombQuarters), (unsigned)g.Hkv, (unsigned)n_sess);
   hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
   return hipGetLastError();

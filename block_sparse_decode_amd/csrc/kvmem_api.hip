@@ -289,6 +289,74 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
   return KVMEM_OK;
 }
 
+struct PagedScratch {
+  size_t part_o, part_ml, total;
+  int bps, max_splits;
+};
+PagedScratch paged_scratch(const kvmem_geom *g, int S, int T, int n_list) {
+  PagedScratch r;
+  r.bps = paged_blocks_per_split(S, g->n_kv_heads, n_list);
+  r.max_splits = (n_list + r.bps - 1) / r.bps;
+  const size_t rows = (size_t)T * (g->n_q_heads / g->n_kv_heads);
+  const size_t n = (size_t)S * g->n_kv_heads * r.max_splits * rows;
+  r.part_o = 0;
+  r.part_ml = align_up(n * kD * sizeof(float));
+  r.total = r.part_ml + align_up(n * sizeof(float2));
+  return r;
+}
+
+size_t kvmem_attend_paged_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T, int32_t n_list) {
+  if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || T <= 0 || n_list <= 0) return 0;
+  return paged_scratch(geom, n_sessions, T, n_list).total;
+}
+
+kvmem_status kvmem_attend_paged(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
+                                const float *q_norm_w, float eps, const int32_t *view_blocks, int32_t n_list,
+                                const int32_t *view_tokens_host, float rope_theta, float *out, void *scratch,
+                                size_t scratch_bytes, void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if ((st = check_ws(ws, true)) != KVMEM_OK) return st;
+  if (!q || !q_norm_w || !out || !view_tokens_host || T <= 0 || n_list < 0 || (n_list > 0 && !view_blocks))
+    return KVMEM_E_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps) || !(rope_theta > 1.0f) || !isfinite(rope_theta)) return KVMEM_E_ARG;
+  const int G = geom->n_q_heads / geom->n_kv_heads;
+  if (geom->kv_dtype != KVMEM_BF16 || (long)T * G > kMfmaMaxRows) return KVMEM_E_UNSUPPORTED;
+  const int S = ws->n_sessions;
+  for (int s = 0; s < S; ++s)
+    if (view_tokens_host[s] < 0 || (long)view_tokens_host[s] > (long)kBT * n_list) return KVMEM_E_ARG;
+  if ((long)S * geom->n_kv_heads * n_list >= (1L << 31)) return KVMEM_E_UNSUPPORTED;
+  const PagedScratch sc = paged_scratch(geom, S, T, n_list > 0 ? n_list : 1);
+  if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
+  PagedGeom g;
+  g.Tq = T;
+  g.Hq = geom->n_q_heads;
+  g.Hkv = geom->n_kv_heads;
+  g.G = G;
+  g.rows = T * G;
+  g.max_blocks = ws->max_blocks;
+  g.n_pages = ws->n_pages;
+  g.n_list = n_list;
+  g.bps = sc.bps;
+  g.max_splits = sc.max_splits;
+  char *base = (char *)scratch;
+  for (int s0 = 0; s0 < S; s0 += kMaxSess) {
+    const int n = S - s0 < kMaxSess ? S - s0 : kMaxSess;
+    SessI32 vt, na;
+    memset(&vt, 0, sizeof(vt));
+    memset(&na, 0, sizeof(na));
+    for (int i = 0; i < n; ++i) {
+      vt.v[i] = view_tokens_host[s0 + i];
+      na.v[i] = (ws->n_tokens_host[s0 + i] + kBT - 1) / kBT;
+    }
+    st = hip_status(launch_attend_paged(q, q_norm_w, eps, ws->k_pool, ws->v_pool, ws->block_table, view_blocks,
+                                        (float *)(base + sc.part_o), (float2 *)(base + sc.part_ml), out,
+                                        ws->dev_error, vt, na, s0, n, g, (double)rope_theta, (hipStream_t)stream));
+    if (st != KVMEM_OK) return st;
+  }
+  return KVMEM_OK;
+}
+
 size_t kvmem_attention_mass_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T, int32_t max_blocks) {
   if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || max_blocks <= 0 || T <= 0) return 0;
   const int chunk = mass_chunk(n_sessions, geom->n_kv_heads, max_blocks);

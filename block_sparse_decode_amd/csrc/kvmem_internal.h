@@ -138,6 +138,22 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
                          hipStream_t st);
 
+// Merge of split partials (layout of the view attention) into out.
+hipError_t launch_attend_combine(const float *part_o, const float2 *part_ml, float *out, const SessI32 &view_tok,
+                                 int s0, int n_sess, const AttendGeom &g, hipStream_t st);
+
+// --- attention straight from the pages ------------------------------------------
+struct PagedGeom {
+  int Tq, Hq, Hkv, G, rows, max_blocks, n_pages, n_list;
+  int bps;          // list blocks per split
+  int max_splits;   // split slots per (session, head) in the partials
+};
+int paged_blocks_per_split(int n_sessions, int Hkv, int n_list);
+hipError_t launch_attend_paged(const void *q, const float *qw, float eps, const void *k_pool, const void *v_pool,
+                               const int32_t *table, const int32_t *view_blocks, float *part_o, float2 *part_ml,
+                               float *out, int32_t *dev_err, const SessI32 &view_tok, const SessI32 &n_all, int s0,
+                               int n_sess, const PagedGeom &g, double theta, hipStream_t st);
+
 // --- selection-quality diagnostic ------------------------------------------------
 struct MassGeom {
   int Tq, Hq, Hkv, G, rows, max_blocks, n_pages, n_list;

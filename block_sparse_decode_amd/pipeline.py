@@ -156,6 +156,17 @@ class DeviceWorkspace:
         if np.any(self.n_tokens // BLOCK > first):
             L.kvmem_update_index(self.geom, self.ws, first, self.index, stream)
 
+    # --- attention straight from the pages ----------------------------------
+    def attend_paged(self, out=None, stream=None):
+        """The attention of kvmem_attend over the current lists, read from the
+        pages (no materialised view)."""
+        if not hasattr(self, "paged_scratch"):
+            nbytes = L.kvmem_attend_paged_scratch_bytes(self.geom, self.S, self.T, max(1, self.n_list))
+            self.paged_scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        L.kvmem_attend_paged(self.geom, self.ws, self.q, self.T, self.q_norm_w, self.eps, self.view_blocks,
+                             self.n_list, self.view_tokens, self.theta, self.out if out is None else out,
+                             scratch=self.paged_scratch, stream=stream)
+
     # --- selection-quality diagnostic ---------------------------------------
     def attention_mass(self, mass, lse=None, view_blocks=None, n_list=None, stream=None):
         """Share of full attention over the history that the listed blocks

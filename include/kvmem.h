@@ -13,6 +13,8 @@
  *   kvmem_materialize    gather of the selected blocks in their original
  *                        order, re-RoPE'd to contiguous view positions.
  *   kvmem_attend         decode attention of the step's queries over the view.
+ *   kvmem_attend_paged   the same attention computed straight from the pages
+ *                        through the view lists (no materialised view).
  *
  * and, for decoding many tokens over one view (step-level reuse):
  *
@@ -244,6 +246,35 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions,
                           const int32_t *view_tokens_host, int32_t max_view,
                           float rope_theta, float *out,
                           void *scratch, size_t scratch_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Attention straight from the paged history ([README 'Core equation']: the
+ * address space and the execution window are separate; [REVIEW 'Summary']:
+ * the view is the selected blocks re-RoPE'd to contiguous positions).
+ *
+ * Computes exactly what kvmem_materialize followed by kvmem_attend computes
+ * with the same view_blocks and view lengths, without writing the view: the
+ * m-th listed block of (s, h) is read from its page, its keys rotated at view
+ * positions 32m .. 32m + 31 and rounded to kv_dtype there, its values used
+ * as stored; view positions at or past V are masked.  A bad list entry or
+ * page sets the KVMEM_DEVERR_* bit and counts as a zero block (as the gather
+ * writes it).  Worth it when a view serves few decode tokens: it reads the
+ * selected K/V once per call, where the gather reads them and writes the
+ * view once per step.
+ *
+ * view_blocks, n_list : as written by kvmem_score_select.
+ * view_tokens_host    : HOST [n_sessions] view lengths V (<= 32 * n_list).
+ * q, q_norm_w, eps, out, rope_theta : as for kvmem_attend (T * G <= 32).
+ * scratch             : at least kvmem_attend_paged_scratch_bytes() bytes.
+ * bf16 workspaces only (KVMEM_E_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+size_t kvmem_attend_paged_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T,
+                                        int32_t n_list);
+kvmem_status kvmem_attend_paged(const kvmem_geom *geom, const kvmem_workspace *ws,
+                                const void *q, int32_t T, const float *q_norm_w, float eps,
+                                const int32_t *view_blocks, int32_t n_list,
+                                const int32_t *view_tokens_host, float rope_theta, float *out,
+                                void *scratch, size_t scratch_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Step-level view reuse ([REVIEW 'Scope & Claims']: recall is scheduled per

@@ -1,0 +1,81 @@
+"""GPU parity of attention straight from the pages (kvmem_attend_paged)
+against the oracle's gather + attention and against the library's own view
+attention, through the C ABI.
+
+Bars: the attention bar against the oracle (2e-2 max-abs for bf16); against
+kvmem_materialize + kvmem_attend on the same lists <= 5e-5 max-abs: the same
+rounded keys and operands, only the split structure, hence the order of the
+fp32 sums, differs (over up to 2^18 terms: ~sqrt(n) * 2^-24 * |o| ~ 3e-5).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvmem_oracle as O
+from tests.certify import certify
+from tests.helpers import make_workload, oracle_ws, small_cfg
+from tests.test_gpu_parity import ATT_TOL, SMALL
+from workloads import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+CASES = {n: SMALL[n] for n in ("bf16_ragged", "bf16_t2_g8", "bf16_t4_g8", "bf16_g1", "recent_only",
+                               "budget_covers_all", "r0_partial", "empty_and_tiny")}
+CASES["nine_heads"] = small_cfg("paged_nine_heads", "bf16", S=2, Hq=18, Hkv=9, n_tokens=(32 * 210 + 3, 32 * 90),
+                                k=30, R=3, n_planted=4, seed=111)
+
+
+def _run(wl, heads=None):
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace
+    cfg = wl.cfg
+    print(f"[gpu] paged {cfg.name} N={list(wl.n_tokens)[:4]} T={cfg.T} k={cfg.k_select} R={cfg.n_recent}", flush=True)
+    dw = DeviceWorkspace(wl, "cuda")
+    dw.build_index()
+    dw.score_select()
+    dw.materialize()
+    dw.attend()
+    torch.cuda.synchronize()
+    out_view = dw.out.cpu().numpy().astype(np.float64)
+    out_p = torch.full_like(dw.out, float("nan"))
+    dw.attend_paged(out=out_p)
+    torch.cuda.synchronize()
+    out_paged = out_p.cpu().numpy().astype(np.float64)
+    assert int(dw.dev_error.item()) == 0
+    d = float(np.abs(out_paged - out_view).max())
+    assert d <= 5e-5, (cfg.name, "paged vs view", d)
+    ws = oracle_ws(wl)
+    G = cfg.group
+    vb = dw.view_blocks.cpu().numpy()
+    heads = range(cfg.n_kv_heads) if heads is None else heads
+    worst = 0.0
+    for s in range(cfg.n_sessions):
+        qn = O.q_rmsnorm(O.decode(wl.q[s], cfg.dtype), wl.q_norm_w, cfg.eps)
+        V = int(dw.view_tokens[s])
+        for h in heads:
+            lst = vb[s, h][vb[s, h] >= 0].astype(np.int64)
+            kv, vv = O.materialize(ws, s, h, lst, V, cfg.rope_theta)
+            o_ref = O.attend(qn[:, h * G:(h + 1) * G], kv, vv, cfg.rope_theta)
+            err = float(np.abs(out_paged[s, :, h * G:(h + 1) * G] - o_ref).max())
+            worst = max(worst, err)
+            assert err <= ATT_TOL[cfg.dtype], (cfg.name, s, h, err)
+    print(f"[gpu] paged {cfg.name}: |paged - view| {d:.2e}, |paged - oracle| {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_paged_parity(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wl = make_workload(CASES[name])
+    certify(wl)
+    _run(wl)
+
+
+def test_paged_c3_full():
+    """The 1M-token workspace: 8192-block lists, 256 splits per head; two
+    heads against the oracle, all heads against the view attention."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wl = make_workload(CONFIGS["c3"])
+    _run(wl, heads=(0, 7))
