@@ -15,6 +15,15 @@
 //               writes the scores and per-row softmax statistics in the same
 //               form as the vector-ALU scorer, so the same aggregation kernel
 //               follows.
+// k_score_r8:   at most 8 query rows per KV head (the T = 1 decode step with
+//               G <= 8): one wavefront per index tile.  The 8 rows' hi and lo
+//               parts form one 16-column B operand (hi in columns 0..7, lo in
+//               8..15) and the two halves of the product are added with one
+//               DPP rotation, so a tile is 16 products.  Every wavefront asks
+//               for its whole 16 KiB tile at once and a launch keeps every
+//               tile of the index in flight (a plain 64 MiB stream measured
+//               fastest that way), where the vector-ALU GEMV for the same 8
+//               rows is bound by its FMAs and their overlap with the loads.
 #include "kvmem_internal.h"
 
 namespace kvmem {
@@ -212,9 +221,157 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   }
 }
 
+// Scores of at most 8 query rows against NTILE consecutive index tiles of one
+// (session, KV head) per wavefront.  Items are (session, KV head, tile)
+// (ScoreSplit with rpg = 8, one row group, per = NTILE, NTILE dividing the
+// tiles per head), so each wavefront writes one statistics slot per row.
+// Lane (qq, col) holds B column col: query row col & 7, dims 32c + 8qq .. +7
+// of chunk c, the hi part for col < 8 and the lo part for col >= 8.  D[m]
+// holds, for lane (qq, col), blocks 16m + 4qq + i of column col; after adding
+// the rotation by 8 lanes, lanes col < 8 hold the full scores of row col.
+// All NTILE tiles are requested at once; the first is multiplied while the
+// others stream in.
+template <int NTILE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NTILE == 1 ? 4 : 2))) void k_score_r8(
+    const uint16_t *__restrict__ index, const uint16_t *__restrict__ q, const float *__restrict__ qw, float eps,
+    float *__restrict__ scores, float2 *__restrict__ part, uint32_t *__restrict__ zero, int n_zero,
+    SessI32 n_blocks, int s0, ScoreGeom g, ScoreSplit sp) {
+  const int lane = threadIdx.x;
+  const int qq = lane >> 4, col = lane & 15;
+  for (int i = blockIdx.x * 64 + lane; i < n_zero; i += gridDim.x * 64) zero[i] = 0u;
+  const ScoreItem it = decode_score_item(blockIdx.x * NTILE, sp, g.Hkv, n_blocks);
+  const int s = s0 + it.sl;
+  const int n_rows = g.Tq * g.G;
+  const int r = col & 7;
+  const bool row_ok = r < n_rows;
+  const int t = row_ok ? r / g.G : 0, gg = row_ok ? r % g.G : 0;
+  const size_t row_id = ((size_t)s * g.Tq + t) * g.Hq + (size_t)it.h * g.G + gg;
+  const int slot = blockIdx.x - score_slot0(it.key, sp);
+  const int b0 = it.t * kIdxTile;
+  if (b0 >= it.nb) {                                   // tiles past this session's history: empty slot
+    if (col < 8 && qq == 0 && row_ok) part[row_id * g.slot_stride + slot] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+
+  // query loads first, then the tiles (vector loads complete in order)
+  float x[4][8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) load8(q + row_id * kD + 32 * c + 8 * qq, x[c]);
+  TileA a[NTILE];
+  const uint16_t *tile0 = index + ((size_t)((size_t)s * g.Hkv + it.h) * g.n_tiles + it.t) * (size_t)(kIdxTile * kD);
+#pragma unroll
+  for (int k = 0; k < NTILE; ++k)   // a tile past the history reads the first one (its scores are not used)
+    load_tile_a(a[k], b0 + k * kIdxTile < it.nb ? tile0 + (size_t)k * (kIdxTile * kD) : tile0, lane);
+
+  // q~ / sqrt(d): the row's sum of squares over the four lanes holding it
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += x[c][j] * x[c][j];
+  ss = sum_xor32(sum_xor16(ss));
+  const float rs = (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * 0.08838834764831845f;   // 1/sqrt(128)
+  // columns 0..7 take bf16(y), columns 8..15 take bf16(y - bf16(y))
+  const float rsv = row_ok ? rs : 0.f;
+  bf16x8 bq[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float y0 = x[c][j] * rsv * qw[32 * c + 8 * qq + j];
+      const float y1 = x[c][j + 1] * rsv * qw[32 * c + 8 * qq + j + 1];
+      const uint32_t hi = pack_bf16x2(y0, y1);
+      const uint32_t lo = pack_bf16x2(y0 - bf16_lo(hi), y1 - bf16_hi(hi));
+      w[j / 2] = col < 8 ? hi : lo;
+    }
+    bq[c] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+  }
+
+  const bool vec = (g.max_blocks & 3) == 0 && (((uintptr_t)scores) & 15) == 0;
+  constexpr float kLog2e = 1.4426950408889634f;
+  float Mrun = -INFINITY, Lrun = 0.f;
+#pragma unroll
+  for (int k = 0; k < NTILE; ++k) {
+    const int bt = b0 + k * kIdxTile;
+    float sc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[k].w[4 * m + c]), bq[c], d, 0, 0, 0);
+      const int b = bt + 16 * m + 4 * qq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = d[i] + dpp_f32<kDppRor8>(d[i]);
+        sc[m][i] = b + i < it.nb ? v : -INFINITY;
+      }
+      if (col < 8 && row_ok && bt < it.nb) {
+        float *dst = scores + row_id * g.max_blocks + b;
+        if (vec && b + 3 < it.nb) {
+          *reinterpret_cast<float4 *>(dst) = make_float4(sc[m][0], sc[m][1], sc[m][2], sc[m][3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (b + i < it.nb) dst[i] = sc[m][i];
+        }
+      }
+    }
+    // the tile's softmax statistics per row: its maximum over the four lanes
+    // holding the row, then one exponential per score (log2 units,
+    // v_exp_f32), folded into the wavefront's running pair
+    float M = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) M = fmaxf(M, sc[m][i]);
+    M = max_xor32(max_xor16(M));
+    if (M == -INFINITY) continue;                      // tile past the history (uniform)
+    const float Ml = M * kLog2e;
+    float L = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L += __builtin_amdgcn_exp2f(fmaf(sc[m][i], kLog2e, -Ml));
+    L = sum_xor32(sum_xor16(L));
+    const float Mn = fmaxf(Mrun, M);
+    Lrun = Lrun * __builtin_amdgcn_exp2f((Mrun - Mn) * kLog2e) + L * __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+    Mrun = Mn;
+  }
+  if (col < 8 && qq == 0 && row_ok) part[row_id * g.slot_stride + slot] = make_float2(Mrun, Lrun);
+}
+
 constexpr int kMfmaWavesPerSimd = 2;
 
 }  // namespace
+
+hipError_t launch_score_r8(const void *index, const void *q, const float *qw, float eps, float *scores, float2 *part,
+                          uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
+                          ScoreSplit *split, hipStream_t st) {
+  int max_nb = 0;
+  for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
+  split->n_sess = n_sess;
+  split->ntl = 0;
+  if (max_nb == 0) return hipSuccess;
+  ScoreSplit sp;
+  sp.n_sess = n_sess;
+  sp.rpg = kGemvMaxRows;
+  sp.n_rg = 1;
+  sp.ntl = idx_tiles(max_nb);
+  // two tiles per wavefront when they divide a head's tiles (a wavefront
+  // then never meets two keys)
+  sp.per = (sp.ntl % 2 == 0) ? 2 : 1;
+  *split = sp;
+  const int grid = n_sess * g.Hkv * sp.ntl / sp.per;
+  if (sp.per == 2)
+    hipLaunchKernelGGL(k_score_r8<2>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const uint16_t *)q, qw,
+                       eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
+  else
+    hipLaunchKernelGGL(k_score_r8<1>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const uint16_t *)q, qw,
+                       eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
+  return hipGetLastError();
+}
 
 hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
                              float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,

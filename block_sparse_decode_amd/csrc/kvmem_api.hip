@@ -272,11 +272,13 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
       uint32_t *zero = hist + (size_t)s0 * g.Hkv * kSelBins;
       const int n_zero = n * g.Hkv * kSelBins;
       ScoreSplit split;
+      // bf16: matrix cores (one tile per wavefront up to 8 rows, row groups of
+      // 32 above); fp32: the vector-ALU GEMV
       const hipError_t e =
-          bf16 && T * g.G > kGemvMaxRows
+          !bf16 ? launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs)
+          : T * g.G > kGemvMaxRows
               ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs)
-              : launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split,
-                                  hs);
+              : launch_score_r8(index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs);
       if ((st = hip_status(e)) != KVMEM_OK) return st;
       if ((st = hip_status(launch_aggregate(scores, part, A, hist, nb, tm.n_cand, s0, n, g, split, hs))) != KVMEM_OK)
         return st;

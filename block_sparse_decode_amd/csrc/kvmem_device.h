@@ -187,6 +187,7 @@ constexpr int kDppMirror8 = 0x141;    // row_half_mirror: lane i <-> 7 - i withi
 constexpr int kDppMirror16 = 0x140;   // row_mirror: lane i <-> 15 - i within 16
 constexpr int kDppBcast15 = 0x142;    // row_bcast:15: lane 15 of each row -> the next row
 constexpr int kDppBcast31 = 0x143;    // row_bcast:31: lane 31 -> rows 2 and 3
+constexpr int kDppRor8 = 0x128;       // row_ror:8: lane i <-> lane i ^ 8 within 16
 
 // DPP move that writes only the rows in ROW_MASK; other lanes get `old`.
 template <int CTRL, int ROW_MASK>

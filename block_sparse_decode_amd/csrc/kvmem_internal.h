@@ -76,9 +76,12 @@ hipError_t launch_score_gemv(int bf16, const void *index, const void *q, const f
                              float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
                              const ScoreGeom &g, ScoreSplit *split, hipStream_t st);
 
-// Matrix-core scorer for bf16 query chunks with more than kGemvMaxRows rows
-// per KV head (row groups of 32).
+// Matrix-core scorers for bf16 steps: at most kGemvMaxRows rows per KV head
+// (one wavefront per index tile), and more (row groups of 32).
 constexpr int kGemvMaxRows = 8;
+hipError_t launch_score_r8(const void *index, const void *q, const float *qw, float eps, float *scores, float2 *part,
+                          uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
+                          ScoreSplit *split, hipStream_t st);
 hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
                              float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
                              const ScoreGeom &g, ScoreSplit *split, hipStream_t st);
