@@ -407,7 +407,9 @@ __global__ __launch_bounds__(512) void k_mass_bf16(const uint16_t *__restrict__ 
   __shared__ double inv_freq[kD / 2];
   __shared__ double step_cs[kD / 2][2];                  // cos, sin of 32 * phi_i
   __shared__ float cs_tab[kQprepMaxT][kD / 2][2];        // query positions N + t
-  __shared__ float ktab[2][kBT][kD / 2][2];              // positions of the current block
+  // (cos, sin) of the current block's positions; rows padded by one pair so
+  // that the 16 tokens one read instruction touches fall in different banks
+  __shared__ float ktab[2][kBT][kD / 2 + 1][2];
   __shared__ uint8_t listed[kMassWaves][kMassMaxChunk];
 
   const int sl = blockIdx.z;

@@ -45,7 +45,9 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
     SessI32 view_tok, SessI32 n_all, int s0, PagedGeom g, double theta) {
   __shared__ double inv_freq[kD / 2];
   __shared__ float cs_tab[kQprepMaxT][kD / 2][2];        // query positions V + t
-  __shared__ float ktab[2][kBT][kD / 2][2];              // view positions of the current block
+  // (cos, sin) of the current block's positions; rows padded by one pair so
+  // that the 16 tokens one read instruction touches fall in different banks
+  __shared__ float ktab[2][kBT][kD / 2 + 1][2];
   __shared__ __align__(16) uint16_t vt[kPgWaves][kBT * kPgPitch];
 
   const int sl = blockIdx.z;
