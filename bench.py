@@ -44,9 +44,9 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
 # taken on (sha256 over block_sparse_decode_amd/csrc/*); otherwise reported null.
-COUNTER_SOURCES_SHA = "37601e4551e6b3c34326dc86b3181c99889811d2ffddb951c3c089d4a2fcc10a"
-MEASURED_TRAFFIC = {"build_index": 2.216e9, "materialize": 2.163e9, "attend": 1.085e9,
-                    "score_select": 7.703e7}
+COUNTER_SOURCES_SHA = "146ac4a41fcf00b194bfae5f2e3a28da9b099ae1d9afcc7d8f9d3f0f31909a26"
+MEASURED_TRAFFIC = {"build_index": 2.216e9, "materialize": 2.162e9, "attend": 1.085e9,
+                    "score_select": 7.643e7}
 
 
 def kernel_sources_sha() -> str:
