@@ -11,10 +11,12 @@
 // k_aggregate: A[b] = sum_rows exp(s[row][b] - M_row) / Z_row for every
 //   complete block (1024 blocks per workgroup), and the candidates counted by
 //   the top digit of A's bits into the (session, head)'s selection histogram.
-// k_topk: the selection, one workgroup per (session, head), starting from
-//   that histogram when there is one.
+// k_topk_tile: the selection when every session has at most 32768 candidates
+//   and the histogram is there (described with the kernel).
+// k_topk: the selection otherwise, one workgroup per (session, head),
+//   starting from that histogram when there is one.
 //
-// Selection (select_head), one 1024-thread workgroup.  A >= 0, so its fp32 bit
+// Selection of k_topk (select_head), one 1024-thread workgroup.  A >= 0, so its fp32 bit
 // patterns order like the values.  Candidates are processed in tiles of 32768
 // keys held in registers, thread t owning the 32 consecutive keys 32t .. 32t+31
 // of a tile; a tile that covers all candidates is loaded once.  The exact k-th
@@ -263,6 +265,230 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
               meta.n_cand.v[sl], meta.k_eff.v[sl], meta.r_start.v[sl], meta.n_all.v[sl], n_list, sm);
 }
 
+// ---------------------------------------------------------------------------
+// Selection of up to one tile of candidates from the aggregation histogram.
+// Wavefront w reads keys w*2048 + j*64 + lane (j < 32) as plain dword loads,
+// so every load instruction covers 256 contiguous bytes and the 128 KiB of a
+// head arrive in a few hundred cache-line requests; index order is (w, j,
+// lane).  The key is A's bit pattern without the sign bit, the same 31 bits
+// the aggregation counted, so the histogram, the refinement and the
+// compaction agree on every key.
+//  1. The bin of the k-th largest key from the histogram (a prefix sum over
+//     the bins in descending order).
+//  2. The keys of that bin are copied into an LDS list (one LDS atomic per
+//     wavefront reserves its run).
+//  3. Two histogram passes over the list fix bits 19..9 and 8..0: the exact
+//     threshold key and how many keys equal to it are taken (ties to the
+//     lower block index).
+//  4. Ordered compaction: per load instruction, the kept lanes' positions
+//     are their rank in the wavefront's ballot plus the kept keys before
+//     them; the block ids go straight to the list in memory.
+// ---------------------------------------------------------------------------
+constexpr int kTkKeys = kTile / kTopkThreads;     // 32 keys per thread
+constexpr uint32_t kTkNone = 0x80000000u;          // no candidate: below every key as a signed int
+constexpr int kTkWaveKeys = kTile / kTopkWaves;   // 2048 keys per wavefront
+
+struct TileSmem {
+  uint32_t hist[kBins];
+  uint32_t wsum[kTopkWaves];
+  uint32_t wgt[kTopkWaves];
+  uint32_t weq[kTopkWaves];
+  uint32_t digit, above, n_list;
+  uint32_t list[kTile];
+};
+
+// Inclusive prefix sum over the wavefront on the DPP network: shifts by 1, 2,
+// 4 and 8 lanes inside each 16-lane row, then row 0 into row 1 and row 2 into
+// row 3 (row_bcast:15), then rows 0-1 into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast15, 0xa, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppBcast31, 0xc, 0xf, false);
+  return v;
+}
+
+// Makes the keys opaque to the compiler, so that the comparisons of a later
+// loop are recomputed instead of keeping 32 lane masks of an earlier one alive
+// in scalar registers.
+__device__ __forceinline__ void launder(uint32_t (&key)[kTkKeys]) {
+#pragma unroll
+  for (int j = 0; j < kTkKeys; ++j) asm volatile("" : "+v"(key[j]));
+}
+
+__device__ __forceinline__ uint32_t wave_total(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
+}
+
+// Bin of the krem-th largest key from counts in descending bin order (thread
+// t owns bins kBins-1-2t and kBins-2-2t); sets sm.digit and sm.above (keys in
+// the bins above it).  The counts must total at least krem.
+__device__ __forceinline__ void find_bin_dpp(uint32_t c0, uint32_t c1, uint32_t krem, TileSmem &sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(c0 + c1);
+  if (lane == 63) sm.wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - (c0 + c1);
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) before += (w < wave) ? sm.wsum[w] : 0u;
+  if (before < krem && krem <= before + c0) {
+    sm.digit = kBins - 1 - 2 * threadIdx.x;
+    sm.above = before;
+  } else if (before + c0 < krem && krem <= before + c0 + c1) {
+    sm.digit = kBins - 2 - 2 * threadIdx.x;
+    sm.above = before + c0;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk_tile(const float *__restrict__ A,
+                                                            const uint32_t *__restrict__ hist,
+                                                            int32_t *__restrict__ view_blocks, TopkMeta meta, int s0,
+                                                            int Hkv, int max_blocks, int n_list) {
+  __shared__ TileSmem sm;
+  const int sl = blockIdx.y;
+  const int s = s0 + sl;
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = meta.n_cand.v[sl], k = meta.k_eff.v[sl];
+  int32_t *out = view_blocks + ((size_t)s * Hkv + h) * n_list;
+
+  if (k > 0) {
+    const bool take_all = k >= nc;
+    const uint32_t *hc = hist + ((size_t)s * Hkv + h) * kSelBins;
+    const float *a = A + ((size_t)s * Hkv + h) * max_blocks;
+    // the counts first: the bin search needs only them and overlaps the keys
+    const uint32_t c0 = hc[kBins - 1 - 2 * tid];
+    const uint32_t c1 = hc[kBins - 2 - 2 * tid];
+    const int base = wave * kTkWaveKeys + lane;
+    uint32_t key[kTkKeys];
+#pragma unroll
+    for (int j = 0; j < kTkKeys; ++j) key[j] = __float_as_uint(a[min(base + 64 * j, nc - 1)]);
+
+    // taking every candidate: a threshold below every key (and no ties)
+    uint32_t thr = take_all ? 0xffffffffu : 0u, krem = 0, n_eq = 0;
+    // (unconditional, so the counts' loads stay ahead of the keys'; with
+    // every candidate taken it looks for no key and finds no bin)
+    if (tid == 0) sm.n_list = 0;
+    find_bin_dpp(c0, c1, take_all ? 0u : (uint32_t)k, sm);
+    const uint32_t b0 = sm.digit;
+    if (!take_all) krem = (uint32_t)k - sm.above;
+#pragma unroll
+    for (int j = 0; j < kTkKeys; ++j) key[j] = base + 64 * j < nc ? key[j] & 0x7fffffffu : kTkNone;
+    // per wavefront: keys above the threshold (cgt) and equal to it (ceq)
+    uint32_t cgt, ceq = 0;
+    if (take_all) {
+      cgt = (uint32_t)min(max(nc - wave * kTkWaveKeys, 0), kTkWaveKeys);
+    } else {
+      // keys of the bins above the boundary bin are kept whatever the
+      // refinement finds; the boundary bin's keys go into the list
+      const int above_key = (int)((b0 + 1) << kSelShift);
+      uint32_t c_in = 0, c_above = 0;
+#pragma unroll
+      for (int j = 0; j < kTkKeys; ++j) {
+        c_in += (key[j] >> kSelShift) == b0 ? 1u : 0u;
+        c_above += (int)key[j] >= above_key ? 1u : 0u;
+      }
+      const uint32_t both = wave_total((c_above << 16) | c_in);   // each at most 2048
+      const uint32_t cnt = both & 0xffffu;
+      cgt = both >> 16;
+      launder(key);
+      uint32_t run0 = 0;
+      if (lane == 0 && cnt) run0 = atomicAdd(&sm.n_list, cnt);
+      run0 = __builtin_amdgcn_readfirstlane(run0);
+      uint32_t run = run0;
+#pragma unroll
+      for (int j = 0; j < kTkKeys; ++j) {
+        const bool m = (key[j] >> kSelShift) == b0;
+        const uint64_t bm = __ballot(m);
+        if (m) sm.list[run + lane_rank(bm)] = key[j];
+        run += __popcll(bm);
+      }
+      for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0u;
+      __syncthreads();
+      const int nl = (int)sm.n_list;
+      // bits 19..9 of the listed keys
+      for (int i = tid; i < nl; i += kTopkThreads) atomicAdd(&sm.hist[(sm.list[i] >> 9) & (kBins - 1)], 1u);
+      __syncthreads();
+      find_bin_dpp(sm.hist[kBins - 1 - 2 * tid], sm.hist[kBins - 2 - 2 * tid], krem, sm);
+      const uint32_t b1 = sm.digit;
+      krem -= sm.above;
+      for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0u;
+      __syncthreads();
+      // bits 8..0 of the listed keys that share bits 19..9
+      for (int i = tid; i < nl; i += kTopkThreads) {
+        const uint32_t u = sm.list[i];
+        if (((u >> 9) & (kBins - 1)) == b1) atomicAdd(&sm.hist[u & 511u], 1u);
+      }
+      __syncthreads();
+      find_bin_dpp(sm.hist[kBins - 1 - 2 * tid], sm.hist[kBins - 2 - 2 * tid], krem, sm);
+      const uint32_t b2 = sm.digit;
+      krem -= sm.above;
+      thr = (b0 << kSelShift) | (b1 << 9) | b2;
+      n_eq = sm.hist[b2];
+      // this wavefront's listed keys above and equal to the threshold
+      uint32_t g = 0, e = 0;
+      for (uint32_t i = lane; i < cnt; i += 64) {
+        const uint32_t u = sm.list[run0 + i];
+        g += u > thr ? 1u : 0u;
+        e += u == thr ? 1u : 0u;
+      }
+      const uint32_t ge = wave_total((e << 16) | g);
+      cgt += ge & 0xffffu;
+      ceq = ge >> 16;
+    }
+    if (lane == 0) {
+      sm.wgt[wave] = cgt;
+      sm.weq[wave] = ceq;
+    }
+    __syncthreads();
+    uint32_t gt_before = 0, eq_before = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+      gt_before += (w < wave) ? sm.wgt[w] : 0u;
+      eq_before += (w < wave) ? sm.weq[w] : 0u;
+    }
+    launder(key);
+    uint32_t pos = gt_before + min(eq_before, krem);
+    char *outb = reinterpret_cast<char *>(out);
+    if (krem == n_eq) {
+      // every key equal to the threshold is kept: the keys at or above it
+      // (with every candidate taken, the threshold is -1 as a signed int)
+#pragma unroll
+      for (int j = 0; j < kTkKeys; ++j) {
+        const bool sel = (int)key[j] >= (int)thr;
+        const uint64_t ms = __ballot(sel);
+        const uint32_t p = pos + lane_rank(ms);
+        if (sel && p < (uint32_t)k) *reinterpret_cast<int32_t *>(outb + p * 4u) = base + 64 * j;
+        pos += __popcll(ms);
+      }
+    } else {
+      // only the first krem keys equal to the threshold, in block order
+      uint32_t eq_run = eq_before;
+#pragma unroll
+      for (int j = 0; j < kTkKeys; ++j) {
+        const bool gt = (int)key[j] > (int)thr;
+        const bool eq = key[j] == thr;
+        const uint64_t em = __ballot(eq);
+        const bool sel = gt || (eq && eq_run + lane_rank(em) < krem);
+        eq_run += __popcll(em);
+        const uint64_t ms = __ballot(sel);
+        const uint32_t p = pos + lane_rank(ms);
+        if (sel && p < (uint32_t)k) *reinterpret_cast<int32_t *>(outb + p * 4u) = base + 64 * j;
+        pos += __popcll(ms);
+      }
+    }
+  }
+  const int r0 = meta.r_start.v[sl], n_rec = meta.n_all.v[sl] - r0;
+  for (int j = tid; j < n_list - k; j += kTopkThreads) out[k + j] = (j < n_rec) ? r0 + j : -1;
+}
+
 __device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
   const float M = fmaxf(a.x, b.x);
   if (M == -INFINITY) return make_float2(-INFINITY, 0.f);
@@ -351,8 +577,14 @@ __global__ __launch_bounds__(kAggChunk) void k_aggregate(const float *__restrict
 hipError_t launch_topk(const float *A, const uint32_t *hist, int32_t *view_blocks, const TopkMeta &meta, int s0,
                        int n_sess, int Hkv, int max_blocks, int n_list, hipStream_t st) {
   dim3 grid((unsigned)Hkv, (unsigned)n_sess);
-  hipLaunchKernelGGL(k_topk, grid, dim3(kTopkThreads), 0, st, A, hist, view_blocks, meta, s0, Hkv, max_blocks,
-                     n_list);
+  int max_nc = 0;
+  for (int i = 0; i < n_sess; ++i) max_nc = meta.n_cand.v[i] > max_nc ? meta.n_cand.v[i] : max_nc;
+  if (hist != nullptr && max_nc <= kTile)
+    hipLaunchKernelGGL(k_topk_tile, grid, dim3(kTopkThreads), 0, st, A, hist, view_blocks, meta, s0, Hkv, max_blocks,
+                       n_list);
+  else
+    hipLaunchKernelGGL(k_topk, grid, dim3(kTopkThreads), 0, st, A, hist, view_blocks, meta, s0, Hkv, max_blocks,
+                       n_list);
   return hipGetLastError();
 }
 

@@ -160,7 +160,7 @@ SMALL = {
     # more candidates than one 32768-key register tile of the selection kernel
     "multi_tile_select": small_cfg("multi_tile_select", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 36000 + 9,),
                                    k=500, R=16, n_planted=300, seed=61),
-    # a list longer than the selection kernel's 16384-entry LDS window
+    # a list of more than 16384 entries
     "two_list_windows": small_cfg("two_list_windows", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 18000 + 7,),
                                   k=16_500, R=8, n_planted=100, seed=62),
 }
@@ -172,6 +172,45 @@ def test_small_parity(name):
     wl = make_workload(SMALL[name])
     certify(wl)
     _full_check(wl)
+
+
+# Exact ties in the aggregated scores: every block's keys are a copy of one of
+# four template blocks, so a head's index rows, scores and aggregated scores
+# take four values, identical bit for bit within a class on both sides, and the
+# budget cuts through a class: the kept blocks of that class are the ones with
+# the lowest block indices.  One case per selection kernel (up to one 32768-key
+# tile; more than that, with a list longer than the 16384 entries that kernel
+# stages at a time); the second session of "ties" keeps every candidate.
+TIES = {
+    "ties": small_cfg("ties", "bf16", S=2, Hq=16, Hkv=2, n_tokens=(32 * 3000 + 5, 32 * 700), k=1000, R=4,
+                      seed=63),
+    "ties_multi_tile": small_cfg("ties_multi_tile", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 34000 + 3,), k=17_000,
+                                 R=4, seed=64),
+}
+
+
+@pytest.mark.parametrize("name", list(TIES))
+def test_selection_exact_ties(name):
+    _need_gpu()
+    cfg = TIES[name]
+    wl = make_workload(cfg)
+    rng = np.random.default_rng(cfg.seed)
+    for s in range(cfg.n_sessions):
+        nb = int(wl.n_tokens[s]) // 32
+        cls = rng.integers(0, 4, nb)
+        cls[:4] = np.arange(4)
+        tmpl = wl.block_table[s, :4].copy()
+        for b in range(4, nb):
+            wl.k_pool[wl.block_table[s, b]] = wl.k_pool[tmpl[cls[b]]]
+    # the four classes must be well apart, so only the ties are at stake
+    ws = oracle_ws(wl)
+    for s in range(cfg.n_sessions):
+        index = [O.mean_k_index(ws, s, h) for h in range(cfg.n_kv_heads)]
+        _, A_all, _ = O.session_scores(ws, s, wl.q[s], wl.q_norm_w, cfg.eps, index, keep_scores=False)
+        for h in range(cfg.n_kv_heads):
+            v = np.sort(A_all[h][:4])
+            assert np.all(np.diff(v) > 1e-3 * v[1:]), (name, s, h, v)
+    _full_check(wl, check_scores=False)
 
 
 # Long query chunks (more than 32 query rows per KV head): the two-pass
