@@ -12,10 +12,10 @@
 //
 // One workgroup per (new token, session) covers every KV head: eight threads
 // per head, thread j owning dimension pairs (8j..8j+7, 64+8j..64+8j+7), so the
-// rotation needs no cross-lane data; the eight (cos, sin) pairs of a thread
-// are the same for every head.  The angle is formed in fp64 and reduced modulo
-// 2 pi as for the gather, so an appended token is bit-identical to the same
-// token gathered into that view position.
+// rotation needs no cross-lane data; the token's 64 (cos, sin) pairs are formed
+// once per workgroup and shared by every head.  The angles are formed exactly as the gather
+// forms them, so an appended token is bit-identical to the same token
+// gathered into that view position.
 #include "kvmem_internal.h"
 
 namespace kvmem {
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
                                                 T *__restrict__ vview, int32_t *dev_err, SessI32 n_tok,
                                                 SessI32 view_tok, int s0, int Hkv, int max_blocks, int n_pages,
                                                 int max_view, double theta) {
-  __shared__ double inv_freq[kD / 2];
+  __shared__ float2 cs_tok[kD / 2];   // (cos, sin) of the token's view position
   const int t = blockIdx.x;
   const int sl = blockIdx.y;
   const int s = s0 + sl;
@@ -49,11 +49,24 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
   const bool page_ok = page >= 0 && page < n_pages;
   if (!page_ok && threadIdx.x == 0) dev_flag(dev_err, 1);
 
-  if (threadIdx.x < kD / 2) inv_freq[threadIdx.x] = rope_inv_freq(threadIdx.x, theta);
+  // the angles of view position vpos = 32 (vpos / 32) + vpos % 32, composed
+  // as the gather composes them, once per frequency for every head
+  if (threadIdx.x < kD / 2) {
+    const double f = rope_inv_freq(threadIdx.x, theta);
+    double ca, sa;
+    rope_angle_f64((double)(vpos - vpos % kBT), f, ca, sa);
+    float cb, sb, c, sn;
+    rope_offset_pair(vpos % kBT, f, cb, sb);
+    rope_compose(ca, sa, cb, sb, c, sn);
+    cs_tok[threadIdx.x] = make_float2(c, sn);
+  }
   __syncthreads();
   float cs[8], sn[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) rope_cos_sin((double)vpos, inv_freq[8 * j + e], cs[e], sn[e]);
+  for (int e = 0; e < 8; ++e) {
+    cs[e] = cs_tok[8 * j + e].x;
+    sn[e] = cs_tok[8 * j + e].y;
+  }
 
   const int m = vpos / kBT;
   const int slot = v_slot(vpos % kBT);
@@ -75,10 +88,7 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
     Row8<T>::load(knew + src + 8 * j, x1);
     Row8<T>::load(knew + src + 64 + 8 * j, x2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
-      y2[e] = x2[e] * cs[e] + x1[e] * sn[e];
-    }
+    for (int e = 0; e < 8; ++e) rope_rotate(x1[e], x2[e], cs[e], sn[e], y1[e], y2[e]);
     T *kd = kview + (((size_t)s * Hkv + h) * max_view + vpos) * kD;
     Row8<T>::store(kd + 8 * j, y1);
     Row8<T>::store(kd + 64 + 8 * j, y2);

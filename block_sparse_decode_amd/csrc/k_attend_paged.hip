@@ -15,8 +15,11 @@
 // KV heads); wavefront w serves KV head 8 * group + w over the split's list
 // blocks.  Per block:
 //   * the 32 x 64 RoPE (cos, sin) table of the block's view positions is
-//     shared by the 8 heads through LDS (each thread forms 4 entries;
-//     double-buffered, one barrier per block);
+//     shared by the 8 heads through LDS (double-buffered, one barrier per
+//     block).  Its angles are composed from the block's 64 base angles
+//     (evaluated by one wavefront the block before) and the 32 x 64 in-block
+//     offsets (a table formed once per workgroup), exactly as the gather
+//     composes them;
 //   * S^T = K Q^T and the online softmax are those of the view attention (the
 //     K tile is loaded in the A-operand layout, where a dim and its +-64
 //     partner sit in one lane);
@@ -34,6 +37,14 @@ namespace {
 constexpr int kPgWaves = 8;
 constexpr int kPgPitch = kD + 8;   // padded token pitch (elements) of a wavefront's V tile
 
+// (cos, sin) of pos * inv_freq in fp64, kept out of line: inlined into the
+// block loop its temporaries push the kernel past its register budget
+__device__ __noinline__ double2 block_angle(double pos, double inv_freq) {
+  double c, s;
+  rope_angle_f64(pos, inv_freq, c, s);
+  return make_double2(c, s);
+}
+
 // token of k-slot e (0..7) of lane group qq: the S^T accumulator order
 __device__ __forceinline__ int pg_token(int qq, int e) { return e < 4 ? 4 * qq + e : 16 + 4 * qq + (e - 4); }
 
@@ -48,6 +59,8 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   // (cos, sin) of the current block's positions; rows padded by one pair so
   // that the 16 tokens one read instruction touches fall in different banks
   __shared__ float ktab[2][kBT][kD / 2 + 1][2];
+  __shared__ float2 offs[kBT][kD / 2];                   // in-block angles u * theta_i
+  __shared__ double2 base_cs[2][kD / 2];                 // block angles 32 m * theta_i
   __shared__ __align__(16) uint16_t vt[kPgWaves][kBT * kPgPitch];
 
   const int sl = blockIdx.z;
@@ -126,8 +139,22 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
       const int t = idx / (kD / 2), i = idx % (kD / 2);
       rope_cos_sin((double)(V + t), inv_freq[i], cs_tab[t][i][0], cs_tab[t][i][1]);
     }
+    for (int idx = tid; idx < kBT * (kD / 2); idx += 512) {
+      const int u = idx / (kD / 2), i = idx % (kD / 2);
+      float cb, sb;
+      rope_offset_pair(u, inv_freq[i], cb, sb);
+      offs[u][i] = make_float2(cb, sb);
+    }
+    if (tid < kD / 2) {
+#pragma unroll 1
+      for (int k = 0; k < 2; ++k) {
+        double c, sn;
+        rope_angle_f64((double)(kBT * (m0 + k)), inv_freq[tid], c, sn);
+        base_cs[k][tid] = make_double2(c, sn);
+      }
+    }
   }
-  __syncthreads();                                     // cs_tab
+  __syncthreads();                                     // cs_tab, offs, base_cs
   bf16x8 qhi[NT][4], qlo[NT][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) build_q_operands(x[nt], rvalid[nt], trow[nt], qq, qw, eps, cs_tab, qhi[nt], qlo[nt]);
@@ -145,10 +172,14 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 
   for (int m = m0; m < m1; ++m) {
     const int buf = (m - m0) & 1;
+#pragma unroll 1
     for (int idx = tid; idx < kBT * (kD / 2); idx += 512) {
       const int u = idx / (kD / 2), i = idx % (kD / 2);
-      rope_cos_sin((double)(kBT * m + u), inv_freq[i], ktab[buf][u][i][0], ktab[buf][u][i][1]);
+      const double2 a = base_cs[buf][i];
+      const float2 b = offs[u][i];
+      rope_compose(a.x, a.y, b.x, b.y, ktab[buf][u][i][0], ktab[buf][u][i][1]);
     }
+
     // this wavefront's V tile, token-major, into its own LDS tile
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -183,9 +214,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const int ip = 32 * c + 8 * qq + j + k;
-            const float cs = ktab[buf][u][ip][0], sn = ktab[buf][u][ip][1];
-            y1[k] = kv[c][j + k] * cs - kv[c + 2][j + k] * sn;
-            y2[k] = kv[c + 2][j + k] * cs + kv[c][j + k] * sn;
+            rope_rotate(kv[c][j + k], kv[c + 2][j + k], ktab[buf][u][ip][0], ktab[buf][u][ip][1], y1[k], y2[k]);
           }
           w[c][j / 2] = pack_bf16x2(y1[0], y1[1]);
           w[c + 2][j / 2] = pack_bf16x2(y2[0], y2[1]);
@@ -258,6 +287,10 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
         o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, o[nt][dt], 0, 0, 0);
       }
     }
+    // the base angles of block m + 2 into the buffer this block's table came
+    // from (every wavefront passed this block's barrier, so it is read out;
+    // block m + 1's barrier orders the write before block m + 2 reads it)
+    if (tid < kD / 2 && m + 2 < m1) base_cs[buf][tid] = block_angle((double)(kBT * (m + 2)), inv_freq[tid]);
     // one tile in flight per wavefront: the next tile's loads follow the
     // products (eight wavefronts per CU move 128 KiB per step between them)
     if (m + 1 < m1) {

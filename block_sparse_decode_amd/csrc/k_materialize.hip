@@ -5,8 +5,9 @@
 // stored un-rotated, so block m of the list lands at view positions 32m..32m+31
 // and is rotated there.  One workgroup per (session, view block) covers every KV
 // head: the 32 x 64 RoPE angles are the same for all heads, so each thread forms
-// its 8 (cos, sin) pairs once (fp64 angle and reduction, fp32 sin/cos) and
-// reuses them for every head.  Thread (u, j) owns token u and the dimension
+// its 8 (cos, sin) pairs once and reuses them for every head (the block's 64
+// base angles are evaluated once per workgroup, each thread's in-block offsets
+// itself, and the two composed as every kernel that touches view keys does).  Thread (u, j) owns token u and the dimension
 // pairs (8j..8j+7, 64+8j..64+8j+7), so each rotation needs no cross-lane data.
 // K rows are written token-major; each V block is transposed through LDS into
 // the dimension-major, slot-permuted layout that the attention kernel's
@@ -27,6 +28,7 @@ __global__ __launch_bounds__(256) void k_materialize(const T *__restrict__ kpool
                                                      SessI32 n_all, int s0, int Hkv, int max_blocks, int n_pages,
                                                      int n_list, int max_view, double theta) {
   __shared__ double inv_freq[kD / 2];
+  __shared__ double2 base_cs[kD / 2];   // (cos, sin) of the block angle 32 m * theta_i
   __shared__ T vt[kD * kVtPitch];
 
   const int sl = blockIdx.y;
@@ -38,13 +40,23 @@ __global__ __launch_bounds__(256) void k_materialize(const T *__restrict__ kpool
   const int t = threadIdx.x;
   const int u = t >> 3;
   const int j = t & 7;
-  if (t < kD / 2) inv_freq[t] = rope_inv_freq(t, theta);
+  if (t < kD / 2) {
+    const double f = rope_inv_freq(t, theta);
+    inv_freq[t] = f;
+    double c, sn;
+    rope_angle_f64((double)(kBT * m), f, c, sn);
+    base_cs[t] = make_double2(c, sn);
+  }
   __syncthreads();
 
   float cs[8], sn[8];
-  const double pos = (double)(kBT * m + u);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) rope_cos_sin(pos, inv_freq[8 * j + e], cs[e], sn[e]);
+  for (int e = 0; e < 8; ++e) {
+    float cb, sb;
+    rope_offset_pair(u, inv_freq[8 * j + e], cb, sb);
+    const double2 a = base_cs[8 * j + e];
+    rope_compose(a.x, a.y, cb, sb, cs[e], sn[e]);
+  }
 
   const int nall = n_all.v[sl];
   const size_t view_blocks_per_head = (size_t)(max_view / kBT);
@@ -68,10 +80,7 @@ __global__ __launch_bounds__(256) void k_materialize(const T *__restrict__ kpool
     }
     float y1[8], y2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
-      y2[e] = x2[e] * cs[e] + x1[e] * sn[e];
-    }
+    for (int e = 0; e < 8; ++e) rope_rotate(x1[e], x2[e], cs[e], sn[e], y1[e], y2[e]);
     T *kd = kview + (((size_t)s * Hkv + h) * max_view + (size_t)kBT * m + u) * kD;
     Row8<T>::store(kd + 8 * j, y1);
     Row8<T>::store(kd + 64 + 8 * j, y2);

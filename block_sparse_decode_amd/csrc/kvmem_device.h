@@ -166,6 +166,44 @@ __device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float 
   sincosf((float)r, &s, &c);
 }
 
+// fp64 sin and cos of pos * inv_freq, reduced modulo 2*pi as above.
+__device__ __forceinline__ void rope_angle_f64(double pos, double inv_freq, double &c, double &s) {
+  const double kTwoPiHi = 6.283185307179586232;
+  const double kTwoPiLo = 2.4492935982947064e-16;
+  const double kInvTwoPi = 0.15915494309189535;
+  const double phi = pos * inv_freq;
+  const double n = rint(phi * kInvTwoPi);
+  double r = fma(-n, kTwoPiHi, phi);
+  r = fma(-n, kTwoPiLo, r);
+  sincos(r, &s, &c);
+}
+
+// RoPE (cos, sin) of a key at view position p = 32 m + u.  The angle is split
+// into a block part 32 m * theta_i and an in-block part u * theta_i, each
+// formed and reduced in fp64 and evaluated with fp64 sin / cos; the in-block
+// pair is rounded to fp32 (kernels that reuse it across blocks keep a table of
+// the 32 x 64 pairs), and the two are combined with the angle-addition
+// identities in fp64 and rounded to fp32 once.  Every kernel that writes or
+// reads view keys forms their angles with these two functions, so gathered,
+// appended and paged keys agree bit for bit.
+__device__ __forceinline__ void rope_offset_pair(int u, double inv_freq, float &cb, float &sb) {
+  double c, s;
+  rope_angle_f64((double)u, inv_freq, c, s);
+  cb = (float)c;
+  sb = (float)s;
+}
+__device__ __forceinline__ void rope_compose(double ca, double sa, float cb, float sb, float &c, float &s) {
+  c = (float)fma(ca, (double)cb, -(sa * (double)sb));
+  s = (float)fma(sa, (double)cb, ca * (double)sb);
+}
+
+// The rotated pair (x1, x2) -> (x1 c - x2 s, x2 c + x1 s) with its fused
+// operations written out, so that every kernel rounds it the same way.
+__device__ __forceinline__ void rope_rotate(float x1, float x2, float c, float s, float &y1, float &y2) {
+  y1 = fmaf(x1, c, -(x2 * s));
+  y2 = fmaf(x2, c, x1 * s);
+}
+
 // Slot of token u inside a dimension-major 32-token V view block.
 __host__ __device__ __forceinline__ int v_slot(int u) {
   return 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3);
