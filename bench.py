@@ -8,12 +8,13 @@ no attention; the scorer is reported against the bf16 matrix-core peak.)
 
 One step is one pass of the whole path over the 1M-token workspace
 (1,048,576 tokens = 32,768 blocks; 64 query / 8 KV heads; d = 128; bf16):
-    kvmem_score_select -> kvmem_materialize -> kvmem_attend -> kvmem_build_index.
+    kvmem_score_select -> kvmem_build_index -> kvmem_materialize -> kvmem_attend.
 Two independent copies of the workspace are used in turn; a step scores,
-materialises and attends one copy and rebuilds the Mean-K index of the other,
-so each stage reads what the previous step wrote long before (the index a
-scorer reads was written one step earlier, with >3 GB of other traffic in
-between), as an incrementally maintained index would be.  Inputs are
+materialises and attends one copy and rebuilds the Mean-K index of the other
+between the scoring and the gather, so the index a scorer reads was written
+one step earlier with the gather and the attention (>3 GB of traffic, far
+beyond the 256 MB MALL) in between, as an incrementally maintained index
+would be read.  Inputs are
 resident in HBM before the timed region.
 
 Prints ONE JSON line.  `value` is blocks scored per second over whole steps
@@ -291,11 +292,11 @@ def main():
         # index already exceeds the 256 MB MALL)
         wl = make_workload(cfg, pools=False)
         wss = [DeviceWorkspace(wl, dev)]
-        stages = ["score_select", "materialize", "build_index"]
+        stages = ["score_select", "build_index", "materialize"]
     else:
         wl = make_workload(cfg)
         wss = [DeviceWorkspace(wl, dev), DeviceWorkspace(wl, dev)]
-        stages = ["score_select", "materialize", "attend", "build_index"]
+        stages = ["score_select", "build_index", "materialize", "attend"]
     print(f"[bench] workload {cfg.name} ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     for w in wss:

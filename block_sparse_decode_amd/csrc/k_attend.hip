@@ -719,6 +719,18 @@ __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict_
     m = mn;
   };
   int i = sg;
+  for (; i + 7 * kCombGroups < n; i += 8 * kCombGroups) {
+    float2 ml[8];
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t pidx = base + (size_t)(i + kCombGroups * u) * g.rows;
+      ml[u] = part_ml[pidx];
+      v[u] = reinterpret_cast<const float4 *>(part_o + pidx * kD)[slice];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) fold(ml[u], v[u]);
+  }
   for (; i + 3 * kCombGroups < n; i += 4 * kCombGroups) {
     float2 ml[4];
     float4 v[4];
