@@ -16,14 +16,15 @@
 //               form as the vector-ALU scorer, so the same aggregation kernel
 //               follows.
 // k_score_r8:   at most 8 query rows per KV head (the T = 1 decode step with
-//               G <= 8): one wavefront per index tile.  The 8 rows' hi and lo
-//               parts form one 16-column B operand (hi in columns 0..7, lo in
-//               8..15) and the two halves of the product are added with one
-//               DPP rotation, so a tile is 16 products.  Every wavefront asks
-//               for its whole 16 KiB tile at once and a launch keeps every
-//               tile of the index in flight (a plain 64 MiB stream measured
-//               fastest that way), where the vector-ALU GEMV for the same 8
-//               rows is bound by its FMAs and their overlap with the loads.
+//               G <= 8): one wavefront per run of up to four index tiles.  The
+//               8 rows' hi and lo parts form one 16-column B operand (hi in
+//               columns 0..7, lo in 8..15) and the two halves of the product
+//               are added with one DPP rotation, so a tile is 16 products.  A
+//               wavefront keeps two whole 16 KiB tiles in flight: the registers
+//               of a tile take the tile after next as soon as its products are
+//               issued, so the scoring of one tile overlaps the loads of the
+//               next two, where the vector-ALU GEMV for the same 8 rows is
+//               bound by its FMAs and their overlap with the loads.
 #include "kvmem_internal.h"
 
 namespace kvmem {
@@ -257,11 +258,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NTILE == 1 ?
   float x[4][8];
 #pragma unroll
   for (int c = 0; c < 4; ++c) load8(q + row_id * kD + 32 * c + 8 * qq, x[c]);
-  TileA a[NTILE];
+  constexpr int NB = NTILE < 2 ? NTILE : 2;   // tiles in flight
+  TileA a[NB];
   const uint16_t *tile0 = index + ((size_t)((size_t)s * g.Hkv + it.h) * g.n_tiles + it.t) * (size_t)(kIdxTile * kD);
+  // a tile past the history reads the first one (its scores are not used)
+  auto tile_ptr = [&](int k) { return b0 + k * kIdxTile < it.nb ? tile0 + (size_t)k * (kIdxTile * kD) : tile0; };
 #pragma unroll
-  for (int k = 0; k < NTILE; ++k)   // a tile past the history reads the first one (its scores are not used)
-    load_tile_a(a[k], b0 + k * kIdxTile < it.nb ? tile0 + (size_t)k * (kIdxTile * kD) : tile0, lane);
+  for (int k = 0; k < NB; ++k) load_tile_a(a[k], tile_ptr(k), lane);
 
   // q~ / sqrt(d): the row's sum of squares over the four lanes holding it
   float ss = 0.f;
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NTILE == 1 ?
       floatx4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[k].w[4 * m + c]), bq[c], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[k % NB].w[4 * m + c]), bq[c], d, 0, 0, 0);
       const int b = bt + 16 * m + 4 * qq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -318,6 +321,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NTILE == 1 ?
         }
       }
     }
+    // the freed registers take tile k + NB
+    if (k + NB < NTILE) load_tile_a(a[k % NB], tile_ptr(k + NB), lane);
     // the tile's softmax statistics per row: its maximum over the four lanes
     // holding the row, then one exponential per score (log2 units,
     // v_exp_f32), folded into the wavefront's running pair
@@ -359,12 +364,15 @@ hipError_t launch_score_r8(const void *index, const void *q, const float *qw, fl
   sp.rpg = kGemvMaxRows;
   sp.n_rg = 1;
   sp.ntl = idx_tiles(max_nb);
-  // two tiles per wavefront when they divide a head's tiles (a wavefront
-  // then never meets two keys)
-  sp.per = (sp.ntl % 2 == 0) ? 2 : 1;
+  // four (else two) tiles per wavefront when they divide a head's tiles (a
+  // wavefront then never meets two keys); two are in flight at a time
+  sp.per = (sp.ntl % 4 == 0) ? 4 : (sp.ntl % 2 == 0) ? 2 : 1;
   *split = sp;
   const int grid = n_sess * g.Hkv * sp.ntl / sp.per;
-  if (sp.per == 2)
+  if (sp.per == 4)
+    hipLaunchKernelGGL(k_score_r8<4>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const uint16_t *)q, qw,
+                       eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
+  else if (sp.per == 2)
     hipLaunchKernelGGL(k_score_r8<2>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const uint16_t *)q, qw,
                        eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
   else
