@@ -163,6 +163,12 @@ SMALL = {
     # a list of more than 16384 entries
     "two_list_windows": small_cfg("two_list_windows", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 18000 + 7,),
                                   k=16_500, R=8, n_planted=100, seed=62),
+    # exactly one full 32768-key selection tile (no padding keys), and one key
+    # more (the multi-tile selection kernel)
+    "full_select_tile": small_cfg("full_select_tile", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * (32768 + 4),),
+                                  k=3000, R=4, n_planted=200, seed=65),
+    "select_tile_plus_one": small_cfg("select_tile_plus_one", "bf16", S=1, Hq=4, Hkv=1,
+                                      n_tokens=(32 * (32769 + 4) + 1,), k=3000, R=5, n_planted=200, seed=66),
 }
 
 
