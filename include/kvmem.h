@@ -198,8 +198,13 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
  * block beta = view_blocks[s][h][m]:
  *   K_view[j] = round( RoPE(K[page(s,beta)][h][u], position j) )
  *   V_view[j] = V[page(s,beta)][h][u]        (bit copy)
- * RoPE rotates pairs (i, i + d/2) by angle j * theta^(-2i/d); the angle is
- * formed in fp64, the rotation in fp32, the result rounded to nearest even.
+ * RoPE rotates pairs (i, i + d/2) by angle j * theta^(-2i/d).  Its cosine and
+ * sine are formed from the block angle 32*m*theta_i and the in-block angle
+ * u*theta_i (each reduced modulo 2*pi and evaluated in fp64; the in-block pair
+ * rounded to fp32) by the angle-addition identities in fp64, rounded to fp32
+ * once; the rotation is in fp32 and the result rounded to nearest even.
+ * kvmem_append and kvmem_attend_paged form view keys the same way, bit for
+ * bit.
  * Slots j in [V, 32 * ceil(V/32)) are written as zeros; later slots are not
  * written.
  *
