@@ -230,8 +230,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 // of chunk c, the hi part for col < 8 and the lo part for col >= 8.  D[m]
 // holds, for lane (qq, col), blocks 16m + 4qq + i of column col; after adding
 // the rotation by 8 lanes, lanes col < 8 hold the full scores of row col.
-// All NTILE tiles are requested at once; the first is multiplied while the
-// others stream in.
+// Two tiles are in flight: the registers of a multiplied tile take the tile
+// after next.
 template <int NTILE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NTILE == 1 ? 4 : 2))) void k_score_r8(
     const uint16_t *__restrict__ index, const uint16_t *__restrict__ q, const float *__restrict__ qw, float eps,
