@@ -163,6 +163,11 @@ SMALL = {
     # a list of more than 16384 entries
     "two_list_windows": small_cfg("two_list_windows", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * 18000 + 7,),
                                   k=16_500, R=8, n_planted=100, seed=62),
+    # budget extremes: one block, and every candidate but one
+    "select_one": small_cfg("select_one", "bf16", S=2, Hq=16, Hkv=2, n_tokens=(32 * 400 + 9, 32 * 75),
+                            k=1, R=3, n_planted=1, seed=67),
+    "select_all_but_one": small_cfg("select_all_but_one", "bf16", S=1, Hq=16, Hkv=2, n_tokens=(32 * 60 + 3,),
+                                    k=58, R=2, n_planted=4, seed=68),
     # exactly one full 32768-key selection tile (no padding keys), and one key
     # more (the multi-tile selection kernel)
     "full_select_tile": small_cfg("full_select_tile", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * (32768 + 4),),
@@ -217,6 +222,36 @@ def test_selection_exact_ties(name):
             v = np.sort(A_all[h][:4])
             assert np.all(np.diff(v) > 1e-3 * v[1:]), (name, s, h, v)
     _full_check(wl, check_scores=False)
+
+
+# Every block's keys identical: all candidates tie, all of them fall into the
+# selection's boundary bin (the tile kernel's LDS list holds all 32768), and the
+# kept blocks are the lowest block indices.
+EQUAL = {
+    "all_equal_full_tile": small_cfg("all_equal_full_tile", "bf16", S=1, Hq=4, Hkv=1,
+                                     n_tokens=(32 * (32768 + 4),), k=20_000, R=4, seed=69),
+    "all_equal_two_sessions": small_cfg("all_equal_two_sessions", "bf16", S=2, Hq=16, Hkv=2,
+                                        n_tokens=(32 * 500 + 7, 32 * 90), k=77, R=3, seed=70),
+}
+
+
+@pytest.mark.parametrize("name", list(EQUAL))
+def test_selection_all_equal(name):
+    _need_gpu()
+    cfg = EQUAL[name]
+    wl = make_workload(cfg)
+    for s in range(cfg.n_sessions):
+        nb = int(wl.n_tokens[s]) // 32
+        tmpl = wl.block_table[s, 0]
+        for b in range(1, nb):
+            wl.k_pool[wl.block_table[s, b]] = wl.k_pool[tmpl]
+    res = _full_check(wl, check_scores=False)
+    for s in range(cfg.n_sessions):
+        nb = int(wl.n_tokens[s]) // 32
+        nc, _, _ = O.recent_split(int(wl.n_tokens[s]), cfg.n_recent)
+        k_eff = min(cfg.k_select, nc)
+        for h in range(cfg.n_kv_heads):
+            assert np.array_equal(res["vb"][s, h, :k_eff], np.arange(k_eff)), (name, s, h)
 
 
 # Long query chunks (more than 32 query rows per KV head): the two-pass
