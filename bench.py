@@ -120,8 +120,10 @@ def cpu_baseline(wl, heads=(0, 1, 2, 3)) -> dict:
     return {"value": nb / per_step, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
             "cpu": cpu_model(), "host_cpus_available": len(os.sched_getaffinity(0)),
             "sample": f"whole path (index, scores, selection, view, attention) for KV heads {list(heads)} of "
-                      f"{cfg.n_kv_heads} on the same workspace, {dt:.1f} s, scaled x{cfg.n_kv_heads / len(heads):.2f} "
-                      f"to one step; numpy float64, BLAS threads as 'cores', elementwise work single-threaded",
+                      f"{cfg.n_kv_heads}{' of session 0' if cfg.n_sessions > 1 else ''} on the same workspace, "
+                      f"{dt:.1f} s, scaled x{cfg.n_kv_heads / len(heads):.2f} to that session's step (blocks/s "
+                      f"of its {nb:,} blocks); numpy float64, BLAS threads as 'cores', elementwise work "
+                      f"single-threaded",
             "seconds_per_step": per_step}
 
 
@@ -138,7 +140,8 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
 
     cfg = wl.cfg
     wd = with_decode_capacity(wl, n_dec)
-    V0 = int(max(DeviceWorkspace.view_length_of(wd)))
+    V_start = DeviceWorkspace.view_length_of(wd)
+    V0 = int(max(V_start))
     dw = DeviceWorkspace(wd, dev, max_view=-(-(V0 + n_dec) // 32) * 32)
     kn, vn = draw_decode_tokens(cfg, 0, n_dec)
     kd, vd = to_device(kn, cfg.dtype, dev), to_device(vn, cfg.dtype, dev)
@@ -163,15 +166,16 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
     app = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
     step_us = att + app
     recall = ev[0].elapsed_time(ev[2]) * 1e3
-    blocks_done = [t for t in range(n_dec) if (int(wl.n_tokens[0]) + t + 1) % 32 == 0]
+    # steps at which some session's history completes a block (index rows added)
+    blocks_done = [t for t in range(n_dec) if any((int(n) + t + 1) % 32 == 0 for n in wl.n_tokens)]
     plain = [t for t in range(n_dec) if t not in blocks_done]
-    return {"tokens": n_dec, "view_tokens_start": V0,
+    return {"tokens": n_dec, "view_tokens_start": int(np.sum(V_start)),
             "step_us_median": round(float(np.median(step_us)), 2),
             "attend_us_median": round(float(np.median(att)), 2),
             "append_us_median": round(float(np.median(app[plain])), 2),
             "append_with_index_update_us_median": round(float(np.median(app[blocks_done])), 2) if blocks_done else None,
-            "attend_hbm_frac": round(2 * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4) * V0
-                                     / (np.median(att) * 1e-6) / HBM_PEAK, 4),
+            "attend_hbm_frac": round(2 * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+                                     * int(np.sum(V_start)) / (np.median(att) * 1e-6) / HBM_PEAK, 4),
             "recall_us": round(recall, 2),
             "tokens_per_s_view_reused": round(n_dec / ((recall + step_us.sum()) * 1e-6), 1),
             "tokens_per_s_reselect_each_token": round(1.0 / ((recall + float(np.median(att))) * 1e-6), 1)}
@@ -209,7 +213,7 @@ def paged_vs_view(wl, dev, stream, reps: int = 10) -> dict:
     t_mat = timed(dw.materialize)
     t_att = timed(dw.attend)
     t_pg = timed(lambda st: dw.attend_paged(stream=st))
-    V = int(dw.view_tokens[0])
+    V = int(np.sum(dw.view_tokens))
     nbytes = 2 * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4) * V
     breakeven = t_mat / (t_pg - t_att) if t_pg > t_att else None
     return {"paged_us": round(t_pg, 2), "paged_hbm_frac": round(nbytes / (t_pg * 1e-6) / HBM_PEAK, 4),
@@ -231,11 +235,11 @@ def mass_diagnostic(wl, dev, stream, reps: int = 5) -> dict:
     dw.build_index(stream)
     dw.score_select(stream)
     S, H, T, Hq = cfg.n_sessions, cfg.n_kv_heads, cfg.T, cfg.n_q_heads
-    n_tok = int(wl.n_tokens[0])
-    nb_all = -(-n_tok // 32)
-    r0 = max(0, nb_all - cfg.n_recent)
     rec = torch.full((S, H, dw.n_list), -1, dtype=torch.int32, device=dev)
-    rec[:, :, :nb_all - r0] = torch.arange(r0, nb_all, dtype=torch.int32, device=dev)
+    for s in range(S):                                  # each session's recent blocks, partial tail included
+        nb_all = -(-int(wl.n_tokens[s]) // 32)
+        r0 = max(0, nb_all - cfg.n_recent)
+        rec[s, :, :nb_all - r0] = torch.arange(r0, nb_all, dtype=torch.int32, device=dev)
     mass = torch.empty((S, T, Hq), device=dev)
     m_rec = torch.empty((S, T, Hq), device=dev)
     dw.attention_mass(mass, stream=stream)
@@ -251,7 +255,7 @@ def mass_diagnostic(wl, dev, stream, reps: int = 5) -> dict:
     dw.attention_mass(m_rec, view_blocks=rec, stream=stream)
     torch.cuda.synchronize()
     t = float(np.median(ts))
-    nbytes = n_tok * H * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+    nbytes = int(np.sum(wl.n_tokens)) * H * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
     return {"mass_selected_mean": round(float(mass.mean()), 4), "mass_selected_min": round(float(mass.min()), 4),
             "mass_recent_only_mean": round(float(m_rec.mean()), 4),
             "blocks_selected": cfg.k_select, "blocks_recent": cfg.n_recent,
@@ -334,8 +338,10 @@ def main():
             per[s].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
     mean = {s: float(np.mean(v)) for s, v in per.items()}
 
-    nb = int(wl.n_tokens[0]) // 32
-    V = int(wss[0].view_tokens[0])
+    # every session of the step: complete blocks scored, view tokens gathered
+    n_tok_all = int(np.sum(wl.n_tokens))
+    nb = int(np.sum(np.asarray(wl.n_tokens) // 32))
+    V = int(np.sum(wss[0].view_tokens))
     ab = alg_bytes(cfg, nb, V)
     stage_rep = {}
     for s in stages:
@@ -362,10 +368,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.n_sessions} session, {int(wl.n_tokens[0]):,} tokens "
-                               f"({nb:,} blocks of 32), {cfg.n_q_heads} q heads / {cfg.n_kv_heads} KV heads, "
-                               f"d={cfg.head_dim}, {cfg.dtype}, top-{cfg.k_select} + {cfg.n_recent} recent blocks "
-                               f"-> {V:,}-token view, T={cfg.T}",
+        "config": {"workload": f"{cfg.name}: {cfg.n_sessions} session{'s' if cfg.n_sessions > 1 else ''}, "
+                               f"{n_tok_all:,} tokens ({nb:,} blocks of 32), {cfg.n_q_heads} q heads / "
+                               f"{cfg.n_kv_heads} KV heads, d={cfg.head_dim}, {cfg.dtype}, top-{cfg.k_select} + "
+                               f"{cfg.n_recent} recent blocks per session -> {V:,} view tokens, T={cfg.T}",
                    "blocks": nb, "view_tokens": V, "query_tokens": cfg.T},
         "decode_step_latency_us": None,
         "recall_latency_us": round(stage_rep["score_select"]["us"] + stage_rep["materialize"]["us"], 2),
