@@ -765,13 +765,17 @@ __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict_
 
 }  // namespace
 
-int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view) {
-  // Aim for >= 2048 workgroups (8 per CU) at the largest view; 32..256 tokens
-  // per wavefront.
+int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view, int rows) {
+  // Up to 16 query rows per KV head (two workgroups per CU): aim for >= 2048
+  // workgroups at the largest view, 32..256 tokens per wavefront.  More rows
+  // (one workgroup per CU, whose prologue and merge are larger): >= 256
+  // workgroups, up to 512 tokens per wavefront (measured: 16 sessions of
+  // 4096-token views with 32 rows, 166 us at the first sizing, 80 us here).
+  const long target = rows <= 16 ? 2048L : 256L;
   const long work = (long)max_view * n_sessions * Hkv;
-  long tpw_blocks = (work + 2048L * 4 * kBT - 1) / (2048L * 4 * kBT);
+  long tpw_blocks = (work + target * 4 * kBT - 1) / (target * 4 * kBT);
   if (tpw_blocks < 1) tpw_blocks = 1;
-  if (tpw_blocks > 8) tpw_blocks = 8;
+  if (tpw_blocks > (rows <= 16 ? 8 : 16)) tpw_blocks = rows <= 16 ? 8 : 16;
   return (int)tpw_blocks * kBT;
 }
 

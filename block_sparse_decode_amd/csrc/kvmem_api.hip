@@ -91,7 +91,7 @@ struct AttendScratch {
 };
 AttendScratch attend_scratch(const kvmem_geom *g, int S, int T, int max_view) {
   AttendScratch r;
-  r.tpw = attend_tokens_per_wave(S, g->n_kv_heads, max_view);
+  r.tpw = attend_tokens_per_wave(S, g->n_kv_heads, max_view, T * (g->n_q_heads / g->n_kv_heads));
   r.max_splits = attend_max_splits(max_view, r.tpw);
   const size_t rows = (size_t)T * (g->n_q_heads / g->n_kv_heads);
   const size_t n = (size_t)S * g->n_kv_heads * r.max_splits * rows;

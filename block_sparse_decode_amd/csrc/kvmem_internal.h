@@ -133,7 +133,7 @@ hipError_t launch_append(int bf16, void *k_pool, void *v_pool, const int32_t *ta
 struct AttendGeom {
   int Tq, Hq, Hkv, G, rows, max_view, max_splits, tpw;
 };
-int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view);
+int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view, int rows);
 int attend_max_splits(int max_view, int tpw);
 
 hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
