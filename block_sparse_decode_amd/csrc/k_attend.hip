@@ -763,6 +763,60 @@ __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict_
   }
 }
 
+// At most kCombGroups splits per row (short views, or long runs per
+// wavefront): one thread per (query row, float4 slice of the row) folds the
+// row's splits in split order, kNarrowRows rows per workgroup.  The fold
+// order and arithmetic are those of k_attend_combine, whose split groups then
+// hold one split each, so both give the same bits.
+constexpr int kNarrowRows = 8;
+
+__global__ __launch_bounds__(256) void k_attend_combine_narrow(const float *__restrict__ part_o,
+                                                               const float2 *__restrict__ part_ml,
+                                                               float *__restrict__ out, SessI32 view_tok, int s0,
+                                                               AttendGeom g) {
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int row = blockIdx.x * kNarrowRows + (threadIdx.x >> 5);
+  const int slice = threadIdx.x & 31;                           // float4 slice of the row
+  if (row >= g.rows) return;
+  const int V = view_tok.v[sl];
+  const int split_tok = 4 * g.tpw;
+  const int n = (V + split_tok - 1) / split_tok;
+  if (n == 1) return;                     // written by the attention kernel itself
+  const int t = row / g.G, gg = row % g.G;
+  float4 *dst = reinterpret_cast<float4 *>(out + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD);
+  if (n == 0) {
+    dst[slice] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const size_t base = ((size_t)s * g.Hkv + h) * g.max_splits * g.rows + row;
+  float m = -INFINITY, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < n; i0 += 8) {
+    float2 ml[8];
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t pidx = base + (size_t)min(i0 + u, n - 1) * g.rows;
+      ml[u] = part_ml[pidx];
+      v[u] = reinterpret_cast<const float4 *>(part_o + pidx * kD)[slice];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u >= n || ml[u].x == -INFINITY) continue;
+      const float mn = fmaxf(m, ml[u].x);
+      const float a = exp2f(m - mn), b = exp2f(ml[u].x - mn);
+      l = l * a + ml[u].y * b;
+      acc.x = acc.x * a + v[u].x * b; acc.y = acc.y * a + v[u].y * b;
+      acc.z = acc.z * a + v[u].z * b; acc.w = acc.w * a + v[u].w * b;
+      m = mn;
+    }
+  }
+  const float inv = 1.0f / l;
+  dst[slice] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
 }  // namespace
 
 int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view, int rows) {
@@ -810,8 +864,16 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
 
 hipError_t launch_attend_combine(const float *part_o, const float2 *part_ml, float *out, const SessI32 &view_tok,
                                  int s0, int n_sess, const AttendGeom &g, hipStream_t st) {
-  dim3 cgrid((unsigned)(g.rows * kCombQuarters), (unsigned)g.Hkv, (unsigned)n_sess);
-  hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
+  int max_v = 0;
+  for (int i = 0; i < n_sess; ++i) max_v = view_tok.v[i] > max_v ? view_tok.v[i] : max_v;
+  const int n_max = (max_v + 4 * g.tpw - 1) / (4 * g.tpw);
+  if (n_max <= kCombGroups) {
+    dim3 cgrid((unsigned)((g.rows + kNarrowRows - 1) / kNarrowRows), (unsigned)g.Hkv, (unsigned)n_sess);
+    hipLaunchKernelGGL(k_attend_combine_narrow, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
+  } else {
+    dim3 cgrid((unsigned)(g.rows * kCombQuarters), (unsigned)g.Hkv, (unsigned)n_sess);
+    hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
+  }
   return hipGetLastError();
 }
 
