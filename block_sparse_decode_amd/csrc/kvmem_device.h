@@ -66,20 +66,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // fp64 -> bf16 bits with a single rounding (nearest, ties to even).  The
 // significand is rounded directly on the fp64 bit pattern to the 8 bits bf16
 // keeps, so no intermediate fp32 rounding can double-round.  Magnitudes below
-// the bf16 normal range use the fixed 2^-133 quantum of its subnormals.
+// the bf16 normal range use the fixed 2^-133 quantum of its subnormals.  Both
+// forms are evaluated and one is selected, so callers stay free of branches.
 __device__ __forceinline__ uint32_t f64_to_bf16(double x) {
-  if (!(fabs(x) >= 0x1p-126)) {
-    if (x != x) return 0x7fc0u;
-    const double y = rint(x * 0x1p133) * 0x1p-133;  // exact multiple of 2^-133
-    return __float_as_uint((float)y) >> 16;
-  }
+  const double ys = rint(x * 0x1p133) * 0x1p-133;               // exact multiple of 2^-133
+  const uint32_t small = x != x ? 0x7fc0u : __float_as_uint((float)ys) >> 16;
   const uint64_t b = (uint64_t)__double_as_longlong(x);
   const uint64_t half = 1ull << 44;
   const uint64_t rem = b & ((1ull << 45) - 1);
-  uint64_t keep = b >> 45;
-  if (rem > half || (rem == half && (keep & 1))) keep += 1;   // carry may bump the exponent
-  const double r = __longlong_as_double((long long)(keep << 45));
-  return __float_as_uint((float)r) >> 16;                      // exact, or +-inf
+  const uint64_t keep = b >> 45;
+  const uint64_t up = (rem > half || (rem == half && (keep & 1))) ? 1 : 0;   // carry may bump the exponent
+  const double r = __longlong_as_double((long long)((keep + up) << 45));
+  const uint32_t normal = __float_as_uint((float)r) >> 16;               // exact, or +-inf
+  return fabs(x) >= 0x1p-126 ? normal : small;
 }
 
 // ---------------------------------------------------------------------------
