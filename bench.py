@@ -8,7 +8,12 @@ no attention; the scorer is reported against the bf16 matrix-core peak.)
 
 One step is one pass of the whole path over the 1M-token workspace
 (1,048,576 tokens = 32,768 blocks; 64 query / 8 KV heads; d = 128; bf16):
-    kvmem_score_select -> kvmem_build_index -> kvmem_materialize -> kvmem_attend.
+    kvmem_score_select -> kvmem_build_index -> kvmem_materialize_attend
+(the gather + re-RoPE and the step's attention in one pass, which writes the
+same view as kvmem_materialize and returns the attention over it; with more
+than 16 query rows per KV head, kvmem_materialize -> kvmem_attend, which is
+faster there).  The step with the two separate calls is timed as well and
+reported under "separate_calls".
 Two independent copies of the workspace are used in turn; a step scores,
 materialises and attends one copy and rebuilds the Mean-K index of the other
 between the scoring and the gather, so the index a scorer reads was written
@@ -73,6 +78,8 @@ def alg_bytes(cfg, n_blocks: int, view_tokens: int) -> dict:
         "materialize": 4 * H * d * b * view_tokens,
         # read K and V of the view once
         "attend": 2 * H * d * b * view_tokens,
+        # the gather's bytes; the attention reads nothing more
+        "materialize_attend": 4 * H * d * b * view_tokens,
     }
 
 
@@ -213,12 +220,17 @@ def paged_vs_view(wl, dev, stream, reps: int = 10) -> dict:
     t_mat = timed(dw.materialize)
     t_att = timed(dw.attend)
     t_pg = timed(lambda st: dw.attend_paged(stream=st))
+    t_fu = timed(lambda st: dw.materialize_attend(stream=st))
     V = int(np.sum(dw.view_tokens))
     nbytes = 2 * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4) * V
     breakeven = t_mat / (t_pg - t_att) if t_pg > t_att else None
+    # n tokens over a view made in one pass: t_fu + (n - 1) t_att, against n t_pg
+    breakeven_fu = (t_fu - t_att) / (t_pg - t_att) if t_pg > t_att else None
     return {"paged_us": round(t_pg, 2), "paged_hbm_frac": round(nbytes / (t_pg * 1e-6) / HBM_PEAK, 4),
             "view_attend_us": round(t_att, 2), "materialize_us": round(t_mat, 2),
-            "tokens_per_view_breakeven": None if breakeven is None else round(breakeven, 1)}
+            "materialize_attend_us": round(t_fu, 2),
+            "tokens_per_view_breakeven": None if breakeven is None else round(breakeven, 1),
+            "tokens_per_view_breakeven_one_pass": None if breakeven_fu is None else round(breakeven_fu, 1)}
 
 
 def mass_diagnostic(wl, dev, stream, reps: int = 5) -> dict:
@@ -300,23 +312,26 @@ def main():
     else:
         wl = make_workload(cfg)
         wss = [DeviceWorkspace(wl, dev), DeviceWorkspace(wl, dev)]
-        stages = ["score_select", "build_index", "materialize", "attend"]
+        separate = ["score_select", "build_index", "materialize", "attend"]
+        one_pass = cfg.dtype == "bf16" and cfg.T * cfg.group <= 16
+        stages = ["score_select", "build_index", "materialize_attend"] if one_pass else separate
     print(f"[bench] workload {cfg.name} ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     for w in wss:
         w.build_index(stream)
     torch.cuda.synchronize()
 
-    def step(i, evs=None):
+    def step(i, evs=None, stage_list=None):
         a, b = wss[i % len(wss)], wss[(i + 1) % len(wss)]
         calls = {"score_select": a.score_select, "materialize": a.materialize, "attend": a.attend,
-                 "build_index": b.build_index}
-        for j, name in enumerate(stages):
+                 "build_index": b.build_index, "materialize_attend": lambda st: a.materialize_attend(stream=st)}
+        stage_list = stages if stage_list is None else stage_list
+        for j, name in enumerate(stage_list):
             if evs is not None:
                 evs[j].record(stream)
             calls[name](stream)
         if evs is not None:
-            evs[len(stages)].record(stream)
+            evs[len(stage_list)].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -331,6 +346,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    sep_rep = None
+    if not long_chunk and stages != separate:
+        # the same step with kvmem_materialize + kvmem_attend, for comparison
+        n_sep = max(10, args.steps // 5)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(separate) + 1)] for _ in range(n_sep)]
+        for i in range(3):
+            step(i, stage_list=separate)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(n_sep):
+            step(i, sev[i], stage_list=separate)
+        torch.cuda.synchronize()
+        wall_sep = time.perf_counter() - t1
+        sep_rep = {"ms_per_step": round(wall_sep / n_sep * 1e3, 4), "steps": n_sep}
+        for j, s in enumerate(separate):
+            sep_rep[s + "_us"] = round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in sev])) * 1e3, 2)
 
     per = {s: [] for s in stages}
     for ev in events:
@@ -374,10 +406,12 @@ def main():
                                f"{cfg.n_recent} recent blocks per session -> {V:,} view tokens, T={cfg.T}",
                    "blocks": nb, "view_tokens": V, "query_tokens": cfg.T},
         "decode_step_latency_us": None,
-        "recall_latency_us": round(stage_rep["score_select"]["us"] + stage_rep["materialize"]["us"], 2),
+        "recall_latency_us": round(stage_rep["score_select"]["us"] + stage_rep[stages[2]]["us"], 2),
         "blocks_scored_per_s_score_select": nb / mean["score_select"],
         "stages": stage_rep,
     }
+    if sep_rep is not None:
+        res["separate_calls"] = sep_rep
     if long_chunk:
         # prefill-style chunk: the scorer is a matrix-core contraction
         res["roofline"] = {"bound": "mfma", "kernel": "score_select", "achieved": round(fl / mean["score_select"] / 1e12, 2),

@@ -32,6 +32,7 @@ EXPORTED = [
     "kvmem_append",
     "kvmem_attend_paged_scratch_bytes",
     "kvmem_attend_paged",
+    "kvmem_materialize_attend",
     "kvmem_attention_mass_scratch_bytes",
     "kvmem_attention_mass",
     "kvmem_status_string",
@@ -104,6 +105,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_attend_paged.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
                                        c_void_p, c_int32, c_void_p, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.kvmem_attend_paged.restype = c_int32
+    lib.kvmem_materialize_attend.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
+                                             c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.kvmem_materialize_attend.restype = c_int32
     lib.kvmem_attention_mass_scratch_bytes.argtypes = [POINTER(Geom), c_int32, c_int32, c_int32]
     lib.kvmem_attention_mass_scratch_bytes.restype = c_size_t
     lib.kvmem_attention_mass.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
@@ -256,6 +261,19 @@ def kvmem_attend_paged(geom: Geom, ws: Workspace, q, T: int, q_norm_w, eps: floa
                                    scratch_bytes, _stream(stream))
     if check:
         _check(st, "kvmem_attend_paged")
+    return st
+
+
+def kvmem_materialize_attend(geom: Geom, ws: Workspace, q, T: int, q_norm_w, eps: float, view_blocks, n_list: int,
+                             view_tokens_host: np.ndarray, max_view: int, rope_theta: float, k_view, v_view, out,
+                             scratch=None, scratch_bytes: int | None = None, stream=None, check: bool = True) -> int:
+    if scratch_bytes is None:
+        scratch_bytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    st = load().kvmem_materialize_attend(ctypes.byref(geom), ctypes.byref(ws), _p(q), T, _p(q_norm_w), eps,
+                                         _p(view_blocks), n_list, _p(view_tokens_host), max_view, rope_theta,
+                                         _p(k_view), _p(v_view), _p(out), _p(scratch), scratch_bytes, _stream(stream))
+    if check:
+        _check(st, "kvmem_materialize_attend")
     return st
 
 

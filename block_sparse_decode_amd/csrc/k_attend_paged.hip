@@ -48,12 +48,13 @@ __device__ __noinline__ double2 block_angle(double pos, double inv_freq) {
 // token of k-slot e (0..7) of lane group qq: the S^T accumulator order
 __device__ __forceinline__ int pg_token(int qq, int e) { return e < 4 ? 4 * qq + e : 16 + 4 * qq + (e - 4); }
 
-template <int NT>
+template <int NT, bool WV>
 __global__ __launch_bounds__(512) void k_attend_paged_bf16(
     const uint16_t *__restrict__ q, const float *__restrict__ qw, float eps, const uint16_t *__restrict__ kpool,
     const uint16_t *__restrict__ vpool, const int32_t *__restrict__ table, const int32_t *__restrict__ vblocks,
     float *__restrict__ part_o, float2 *__restrict__ part_ml, float *__restrict__ out, int32_t *dev_err,
-    SessI32 view_tok, SessI32 n_all, int s0, PagedGeom g, double theta) {
+    SessI32 view_tok, SessI32 n_all, int s0, PagedGeom g, double theta, uint16_t *__restrict__ kview,
+    uint16_t *__restrict__ vview, int max_view) {
   __shared__ double inv_freq[kD / 2];
   __shared__ float cs_tab[kQprepMaxT][kD / 2][2];        // query positions V + t
   // (cos, sin) of the current block's positions; rows padded by one pair so
@@ -180,13 +181,15 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
       rope_compose(a.x, a.y, b.x, b.y, ktab[buf][u][i][0], ktab[buf][u][i][1]);
     }
 
-    // this wavefront's V tile, token-major, into its own LDS tile
+    // this wavefront's V tile, token-major, into its own LDS tile (tokens at
+    // or past V are zeros, as the gather writes them; their weights are 0)
+    const int tb = kBT * m;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<uint4 *>(myv + (16 * tt + col) * kPgPitch + 32 * c + 8 * qq) =
-            ok ? vr[tt][c] : make_uint4(0, 0, 0, 0);
+            ok && tb + 16 * tt + col < V ? vr[tt][c] : make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     // K rotated at view positions 32m + u and rounded to bf16: A operands
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
       float kv[4][8];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 r = ok ? kr[tt][c] : make_uint4(0, 0, 0, 0);
+        const uint4 r = ok && tb + u < V ? kr[tt][c] : make_uint4(0, 0, 0, 0);
         const uint32_t e[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -221,9 +224,14 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
         }
 #pragma unroll
       for (int c = 0; c < 4; ++c) ka[tt][c] = as_bf16x8(make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]));
+      if (WV && head_ok) {   // the view's K row of token u: dims 32c + 8qq .. + 7 from this lane
+        uint16_t *row = kview + (((size_t)s * g.Hkv + h) * max_view + tb + u) * kD + 8 * qq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          store_nt16(row + 32 * c, make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]));
+      }
     }
 
-    const int tb = kBT * m;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       floatx4 sc[2];
@@ -282,6 +290,9 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
           w[k] = (uint32_t)myv[pg_token(qq, 2 * k) * kPgPitch + dim] |
                  ((uint32_t)myv[pg_token(qq, 2 * k + 1) * kPgPitch + dim] << 16);
         const bf16x8 va = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        if (WV && nt == 0 && head_ok)   // the lane's 8 tokens of dim are slots 8qq .. 8qq + 7 of the view's V
+          store_nt16(vview + ((((size_t)s * g.Hkv + h) * (max_view / kBT) + m) * kD + dim) * kBT + 8 * qq,
+                     make_uint4(w[0], w[1], w[2], w[3]));
         o[nt][dt] *= alpha;
         o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, o[nt][dt], 0, 0, 0);
         o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, o[nt][dt], 0, 0, 0);
@@ -346,20 +357,24 @@ int paged_blocks_per_split(int n_sessions, int Hkv, int n_list) {
 hipError_t launch_attend_paged(const void *q, const float *qw, float eps, const void *k_pool, const void *v_pool,
                                const int32_t *table, const int32_t *view_blocks, float *part_o, float2 *part_ml,
                                float *out, int32_t *dev_err, const SessI32 &view_tok, const SessI32 &n_all, int s0,
-                               int n_sess, const PagedGeom &g, double theta, hipStream_t st) {
+                               int n_sess, const PagedGeom &g, double theta, void *k_view, void *v_view, int max_view,
+                               hipStream_t st) {
   int max_v = 0;
   for (int i = 0; i < n_sess; ++i) max_v = view_tok.v[i] > max_v ? view_tok.v[i] : max_v;
   const int splits = (max_v + kBT * g.bps - 1) / (kBT * g.bps);
   if (splits > 0) {
     dim3 grid((unsigned)splits, (unsigned)((g.Hkv + kPgWaves - 1) / kPgWaves), (unsigned)n_sess);
-    if (g.rows <= 16)
-      hipLaunchKernelGGL(k_attend_paged_bf16<1>, grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,
-                         (const uint16_t *)k_pool, (const uint16_t *)v_pool, table, view_blocks, part_o, part_ml, out,
-                         dev_err, view_tok, n_all, s0, g, theta);
-    else
-      hipLaunchKernelGGL(k_attend_paged_bf16<2>, grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,
-                         (const uint16_t *)k_pool, (const uint16_t *)v_pool, table, view_blocks, part_o, part_ml, out,
-                         dev_err, view_tok, n_all, s0, g, theta);
+#define KVMEM_PAGED(NT, WV)                                                                                     \
+  hipLaunchKernelGGL((k_attend_paged_bf16<NT, WV>), grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,          \
+                     (const uint16_t *)k_pool, (const uint16_t *)v_pool, table, view_blocks, part_o, part_ml, out, \
+                     dev_err, view_tok, n_all, s0, g, theta, (uint16_t *)k_view, (uint16_t *)v_view, max_view)
+    const bool wv = k_view != nullptr;
+    if (g.rows <= 16) {
+      if (wv) KVMEM_PAGED(1, true); else KVMEM_PAGED(1, false);
+    } else {
+      if (wv) KVMEM_PAGED(2, true); else KVMEM_PAGED(2, false);
+    }
+#undef KVMEM_PAGED
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -312,21 +312,27 @@ size_t kvmem_attend_paged_scratch_bytes(const kvmem_geom *geom, int32_t n_sessio
   return paged_scratch(geom, n_sessions, T, n_list).total;
 }
 
-kvmem_status kvmem_attend_paged(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
-                                const float *q_norm_w, float eps, const int32_t *view_blocks, int32_t n_list,
-                                const int32_t *view_tokens_host, float rope_theta, float *out, void *scratch,
-                                size_t scratch_bytes, void *stream) {
+// Attention from the pages; with k_view / v_view also the view's K and V
+// (max_view is then the view's capacity).
+static kvmem_status paged_attend(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
+                                 const float *q_norm_w, float eps, const int32_t *view_blocks, int32_t n_list,
+                                 const int32_t *view_tokens_host, float rope_theta, float *out, void *scratch,
+                                 size_t scratch_bytes, void *stream, void *k_view, void *v_view, int32_t max_view) {
   kvmem_status st = check_geom(geom);
   if (st != KVMEM_OK) return st;
   if ((st = check_ws(ws, true)) != KVMEM_OK) return st;
   if (!q || !q_norm_w || !out || !view_tokens_host || T <= 0 || n_list < 0 || (n_list > 0 && !view_blocks))
     return KVMEM_E_ARG;
   if (!(eps >= 0.f) || !isfinite(eps) || !(rope_theta > 1.0f) || !isfinite(rope_theta)) return KVMEM_E_ARG;
+  const bool wv = k_view != nullptr || v_view != nullptr;
+  if (wv && (!k_view || !v_view || max_view <= 0 || max_view % kBT != 0)) return KVMEM_E_ARG;
   const int G = geom->n_q_heads / geom->n_kv_heads;
   if (geom->kv_dtype != KVMEM_BF16 || (long)T * G > kMfmaMaxRows) return KVMEM_E_UNSUPPORTED;
   const int S = ws->n_sessions;
-  for (int s = 0; s < S; ++s)
-    if (view_tokens_host[s] < 0 || (long)view_tokens_host[s] > (long)kBT * n_list) return KVMEM_E_ARG;
+  for (int s = 0; s < S; ++s) {
+    const int V = view_tokens_host[s];
+    if (V < 0 || (long)V > (long)kBT * n_list || (wv && V > max_view)) return KVMEM_E_ARG;
+  }
   if ((long)S * geom->n_kv_heads * n_list >= (1L << 31)) return KVMEM_E_UNSUPPORTED;
   const PagedScratch sc = paged_scratch(geom, S, T, n_list > 0 ? n_list : 1);
   if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
@@ -353,10 +359,29 @@ kvmem_status kvmem_attend_paged(const kvmem_geom *geom, const kvmem_workspace *w
     }
     st = hip_status(launch_attend_paged(q, q_norm_w, eps, ws->k_pool, ws->v_pool, ws->block_table, view_blocks,
                                         (float *)(base + sc.part_o), (float2 *)(base + sc.part_ml), out,
-                                        ws->dev_error, vt, na, s0, n, g, (double)rope_theta, (hipStream_t)stream));
+                                        ws->dev_error, vt, na, s0, n, g, (double)rope_theta, wv ? k_view : nullptr,
+                                        wv ? v_view : nullptr, wv ? max_view : 0, (hipStream_t)stream));
     if (st != KVMEM_OK) return st;
   }
   return KVMEM_OK;
+}
+
+kvmem_status kvmem_attend_paged(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
+                                const float *q_norm_w, float eps, const int32_t *view_blocks, int32_t n_list,
+                                const int32_t *view_tokens_host, float rope_theta, float *out, void *scratch,
+                                size_t scratch_bytes, void *stream) {
+  return paged_attend(geom, ws, q, T, q_norm_w, eps, view_blocks, n_list, view_tokens_host, rope_theta, out, scratch,
+                      scratch_bytes, stream, nullptr, nullptr, 0);
+}
+
+kvmem_status kvmem_materialize_attend(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
+                                      const float *q_norm_w, float eps, const int32_t *view_blocks, int32_t n_list,
+                                      const int32_t *view_tokens_host, int32_t max_view, float rope_theta,
+                                      void *k_view, void *v_view, float *out, void *scratch, size_t scratch_bytes,
+                                      void *stream) {
+  if (!k_view || !v_view) return KVMEM_E_ARG;
+  return paged_attend(geom, ws, q, T, q_norm_w, eps, view_blocks, n_list, view_tokens_host, rope_theta, out, scratch,
+                      scratch_bytes, stream, k_view, v_view, max_view);
 }
 
 size_t kvmem_attention_mass_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T, int32_t max_blocks) {

@@ -155,7 +155,8 @@ int paged_blocks_per_split(int n_sessions, int Hkv, int n_list);
 hipError_t launch_attend_paged(const void *q, const float *qw, float eps, const void *k_pool, const void *v_pool,
                                const int32_t *table, const int32_t *view_blocks, float *part_o, float2 *part_ml,
                                float *out, int32_t *dev_err, const SessI32 &view_tok, const SessI32 &n_all, int s0,
-                               int n_sess, const PagedGeom &g, double theta, hipStream_t st);
+                               int n_sess, const PagedGeom &g, double theta, void *k_view, void *v_view, int max_view,
+                               hipStream_t st);
 
 // --- selection-quality diagnostic ------------------------------------------------
 struct MassGeom {

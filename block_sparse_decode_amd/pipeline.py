@@ -167,6 +167,17 @@ class DeviceWorkspace:
                              self.n_list, self.view_tokens, self.theta, self.out if out is None else out,
                              scratch=self.paged_scratch, stream=stream)
 
+    def materialize_attend(self, out=None, stream=None):
+        """kvmem_materialize and kvmem_attend in one pass over the selected
+        blocks: the view is written and the step's attention computed."""
+        if not hasattr(self, "paged_scratch"):
+            nbytes = L.kvmem_attend_paged_scratch_bytes(self.geom, self.S, self.T, max(1, self.n_list))
+            self.paged_scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        L.kvmem_materialize_attend(self.geom, self.ws, self.q, self.T, self.q_norm_w, self.eps, self.view_blocks,
+                                   self.n_list, self.view_tokens, self.max_view, self.theta, self.k_view,
+                                   self.v_view, self.out if out is None else out, scratch=self.paged_scratch,
+                                   stream=stream)
+
     # --- selection-quality diagnostic ---------------------------------------
     def attention_mass(self, mass, lse=None, view_blocks=None, n_list=None, stream=None):
         """Share of full attention over the history that the listed blocks

@@ -282,6 +282,30 @@ kvmem_status kvmem_attend_paged(const kvmem_geom *geom, const kvmem_workspace *w
                                 void *scratch, size_t scratch_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * Gather + re-RoPE and the step's attention in one pass ([REVIEW 'Summary']:
+ * the selected blocks are restored with position-consistent re-RoPE into the
+ * bounded view; [README 'Local reproduction']: attention over that view).
+ *
+ * Writes k_view and v_view exactly as kvmem_materialize does (same bits, same
+ * zeros past V), and computes into out the attention kvmem_attend computes
+ * over them, reading each selected K/V block once: the attention is that of
+ * kvmem_attend_paged (its keys are the view's keys, bit for bit).  The view is
+ * then ready for kvmem_attend / kvmem_append over the step's later tokens.
+ * Slots at or past 32 * ceil(V/32) are not written.
+ *
+ * Arguments as for kvmem_attend_paged, plus max_view, k_view, v_view as for
+ * kvmem_materialize (V <= max_view).  scratch: at least
+ * kvmem_attend_paged_scratch_bytes() bytes.  bf16 workspaces only
+ * (KVMEM_E_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+kvmem_status kvmem_materialize_attend(const kvmem_geom *geom, const kvmem_workspace *ws,
+                                      const void *q, int32_t T, const float *q_norm_w, float eps,
+                                      const int32_t *view_blocks, int32_t n_list,
+                                      const int32_t *view_tokens_host, int32_t max_view,
+                                      float rope_theta, void *k_view, void *v_view, float *out,
+                                      void *scratch, size_t scratch_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Step-level view reuse ([REVIEW 'Scope & Claims']: recall is scheduled per
  * agent step; [REVIEW 'Strengths']: attention is stable within a step and
  * shifts across step boundaries).  The view selected and materialised at a

@@ -152,6 +152,31 @@ def test_attend_rejects(lib):
     assert call(geom=_geom(bt=64)) == L.KVMEM_E_UNSUPPORTED
 
 
+def test_materialize_attend_rejects(lib):
+    ws, n = _ws()
+    g = _geom()
+    vt = np.array([64, 96], np.int32)
+    need = L.kvmem_attend_paged_scratch_bytes(g, 2, 1, 4)
+    assert need > 0
+    call = lambda **kw: L.kvmem_materialize_attend(**{**dict(
+        geom=g, ws=ws, q=0x10, T=1, q_norm_w=0x20, eps=1e-6, view_blocks=0x30, n_list=4, view_tokens_host=vt,
+        max_view=128, rope_theta=1e6, k_view=0x40, v_view=0x50, out=0x60, scratch=0x70, scratch_bytes=need,
+        check=False), **kw})
+    assert call(k_view=None) == L.KVMEM_E_ARG
+    assert call(v_view=None) == L.KVMEM_E_ARG
+    assert call(max_view=100) == L.KVMEM_E_ARG             # not a multiple of 32
+    assert call(max_view=64) == L.KVMEM_E_ARG              # shorter than a view
+    assert call(n_list=2) == L.KVMEM_E_ARG                 # view longer than the list allows
+    assert call(view_blocks=None) == L.KVMEM_E_ARG
+    assert call(T=0) == L.KVMEM_E_ARG
+    assert call(q=None) == L.KVMEM_E_ARG
+    assert call(out=None) == L.KVMEM_E_ARG
+    assert call(rope_theta=1.0) == L.KVMEM_E_ARG
+    assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
+    assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head
+    assert call(geom=_geom("f32")) == L.KVMEM_E_UNSUPPORTED  # bf16 workspaces only
+
+
 def test_update_index_rejects(lib):
     g = _geom()
     ws, n = _ws()

@@ -1,6 +1,9 @@
 """GPU parity of attention straight from the pages (kvmem_attend_paged)
 against the oracle's gather + attention and against the library's own view
-attention, through the C ABI.
+attention, through the C ABI; and of the one-pass gather + attention
+(kvmem_materialize_attend), whose view must equal kvmem_materialize's bit for
+bit (slots past the last view block untouched) and whose output must equal
+kvmem_attend_paged's bit for bit (same kernel, same keys, same order).
 
 Bars: the attention bar against the oracle (2e-2 max-abs for bf16); against
 kvmem_materialize + kvmem_attend on the same lists <= 5e-5 max-abs: the same
@@ -45,6 +48,23 @@ def _run(wl, heads=None):
     assert int(dw.dev_error.item()) == 0
     d = float(np.abs(out_paged - out_view).max())
     assert d <= 5e-5, (cfg.name, "paged vs view", d)
+
+    # one pass: the view as the gather writes it, the output as the paged attention's
+    k_ref, v_ref = dw.k_view.clone(), dw.v_view.clone()
+    sentinel = 0x5A5A
+    dw.k_view.view(torch.int16).fill_(sentinel)
+    dw.v_view.view(torch.int16).fill_(sentinel)
+    out_f = torch.full_like(dw.out, float("nan"))
+    dw.materialize_attend(out=out_f)
+    torch.cuda.synchronize()
+    assert int(dw.dev_error.item()) == 0
+    assert torch.equal(out_f.view(torch.int32), out_p.view(torch.int32)), (cfg.name, "fused vs paged output")
+    for s in range(cfg.n_sessions):
+        nb = (int(dw.view_tokens[s]) + 31) // 32
+        kf, vf = dw.k_view[s].view(torch.int16), dw.v_view[s].view(torch.int16)
+        assert torch.equal(kf[:, :32 * nb], k_ref[s].view(torch.int16)[:, :32 * nb]), (cfg.name, s, "fused K view")
+        assert torch.equal(vf[:, :nb], v_ref[s].view(torch.int16)[:, :nb]), (cfg.name, s, "fused V view")
+        assert bool((kf[:, 32 * nb:] == sentinel).all()) and bool((vf[:, nb:] == sentinel).all()), (cfg.name, s)
     ws = oracle_ws(wl)
     G = cfg.group
     vb = dw.view_blocks.cpu().numpy()
@@ -60,7 +80,8 @@ def _run(wl, heads=None):
             err = float(np.abs(out_paged[s, :, h * G:(h + 1) * G] - o_ref).max())
             worst = max(worst, err)
             assert err <= ATT_TOL[cfg.dtype], (cfg.name, s, h, err)
-    print(f"[gpu] paged {cfg.name}: |paged - view| {d:.2e}, |paged - oracle| {worst:.2e}", flush=True)
+    print(f"[gpu] paged {cfg.name}: |paged - view| {d:.2e}, |paged - oracle| {worst:.2e}; one-pass view and output"
+          " bit-identical", flush=True)
 
 
 @pytest.mark.parametrize("name", list(CASES))
