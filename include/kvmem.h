@@ -3,7 +3,7 @@
  *
  * KVMem keeps a long agent history as paged KV and runs each step over a
  * bounded, query-selected execution view.  The library implements the
- * data-parallel path of that method as four calls:
+ * data-parallel path of that method as these calls:
  *
  *   kvmem_build_index    Mean-K index: mean of each 32-token block's pre-RoPE
  *                        keys, per KV head.
@@ -15,6 +15,9 @@
  *   kvmem_attend         decode attention of the step's queries over the view.
  *   kvmem_attend_paged   the same attention computed straight from the pages
  *                        through the view lists (no materialised view).
+ *   kvmem_materialize_attend  the gather and the attention in one pass: the
+ *                        view as kvmem_materialize writes it, and the
+ *                        attention over it, reading each selected block once.
  *
  * and, for decoding many tokens over one view (step-level reuse):
  *
