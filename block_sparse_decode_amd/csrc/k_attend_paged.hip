@@ -28,6 +28,15 @@
 //     tile and reads the operand from there.
 // Split partials have the view attention's layout and are merged by
 // k_attend_combine.
+//
+// With WV (kvmem_materialize_attend) the kernel also writes the view, which
+// makes it the gather and the attention in one pass: a lane's rotated K
+// operand for token u is a 16-byte run of the view's K row, and its V^T
+// operand (8 tokens of one dimension, in the accumulator's token order) is
+// exactly 8 consecutive slots of that dimension in the view's V layout, so
+// both go out as 16-byte stores with no extra data movement.  Tokens at or
+// past V are zeroed before the rotation and the staging, as the gather writes
+// them.
 #include "attend_common.h"
 
 namespace kvmem {
