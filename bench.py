@@ -3,30 +3,30 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
 
 (--workload c5 times the 10M-token, 512-token-chunk stress instead: one
-workspace drawn on the device, score_select -> materialize -> build_index,
+workspace drawn on the device, score_select -> update_index -> materialize,
 no attention; the scorer is reported against the bf16 matrix-core peak.)
 
-One step is one pass of the whole path over the 1M-token workspace
+One step is one recall step of the method over the 1M-token workspace
 (1,048,576 tokens = 32,768 blocks; 64 query / 8 KV heads; d = 128; bf16):
-    kvmem_score_select -> kvmem_build_index -> kvmem_materialize_attend
-(the gather + re-RoPE and the step's attention in one pass, which writes the
-same view as kvmem_materialize and returns the attention over it; with more
-than 16 query rows per KV head, kvmem_materialize -> kvmem_attend, which is
-faster there).  The step with the two separate calls is timed as well and
-reported under "separate_calls".
-Two independent copies of the workspace are used in turn; a step scores,
-materialises and attends one copy and rebuilds the Mean-K index of the other
-between the scoring and the gather, so the index a scorer reads was written
-one step earlier with the gather and the attention (>3 GB of traffic, far
-beyond the 256 MB MALL) in between, as an incrementally maintained index
-would be read.  Inputs are
-resident in HBM before the timed region.
+    kvmem_score_select -> kvmem_update_index -> kvmem_materialize_attend
+i.e. scoring and selection, the Mean-K index maintenance a step does (the
+rows of the newest complete block), and the gather + re-RoPE with the step's
+attention in one pass (it writes the same view as kvmem_materialize and
+returns the attention over it; with more than 16 query rows per KV head,
+kvmem_materialize -> kvmem_attend, which is faster there).  The step with the
+two separate calls is timed as well ("separate_calls"), and so is a full
+index build (stage "build_index_full", outside the steps).
+Two independent copies of the workspace are used in turn, so the index a
+scorer reads was last touched two steps earlier, with the gathers and
+attentions of both copies (>4 GB of traffic, far beyond the 256 MB MALL) in
+between.  Inputs are resident in HBM before the timed region.
 
-Prints ONE JSON line.  `value` is blocks scored per second over whole steps
-(32,768 blocks per step / step time).  Per-stage times come from HIP events
-recorded on the stream the library launches on; `roofline` reports the
-dominant stage against the 8 TB/s HBM peak using the algorithmic bytes of the
-method; `cpu_baseline` times the CPU oracle on a bounded sample.
+Prints ONE JSON line.  `value` is blocks scored per second: the workspace's
+complete blocks over the mean time of kvmem_score_select (HIP events recorded
+on the stream the library launches on); whole-step throughput is
+`step_blocks_per_s`.  `roofline` reports the dominant stage against the 8 TB/s
+HBM peak using the algorithmic bytes of the method; `cpu_baseline` times the
+CPU oracle stage by stage on a bounded sample.
 """
 from __future__ import annotations
 
@@ -72,6 +72,9 @@ def alg_bytes(cfg, n_blocks: int, view_tokens: int) -> dict:
     return {
         # read 32 keys, write one index row, per (block, KV head)
         "build_index": (32 + 1) * H * d * b * n_blocks,
+        "build_index_full": (32 + 1) * H * d * b * n_blocks,
+        # the newest complete block of every session
+        "update_index": (32 + 1) * H * d * b * cfg.n_sessions,
         # read the index row of every (block, KV head), write A
         "score_select": (H * d * b + H * 4) * n_blocks,
         # read K and V of the selected tokens, write both into the view
@@ -99,39 +102,88 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, heads=(0, 1, 2, 3)) -> dict:
-    """The oracle as it stands, timed on a sample: the whole path for a few of
-    the 8 KV heads of the workspace, scaled to the full workload."""
+def _oracle_stages(wl, heads, threads=None) -> dict:
+    """Seconds per stage of the oracle for the given KV heads of session 0
+    (index, score + select, materialize, attend), BLAS threads limited to
+    `threads` when given."""
+    import contextlib
+
     from oracle import kvmem_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        lim = threadpool_limits(threads) if threads else contextlib.nullcontext()
+    except Exception:  # pragma: no cover
+        lim = contextlib.nullcontext()
+    cfg = wl.cfg
+    ws = O.Workspace(wl.k_pool, wl.v_pool, wl.block_table, wl.n_tokens, cfg.dtype, cfg.n_q_heads,
+                     cfg.n_kv_heads, cfg.head_dim)
+    G = cfg.group
+    n_tok = int(wl.n_tokens[0])
+    t = {"index": 0.0, "score_select": 0.0, "materialize": 0.0, "attend": 0.0}
+    with lim:
+        qn = O.q_rmsnorm(O.decode(wl.q[0], cfg.dtype), wl.q_norm_w, cfg.eps)
+        for h in heads:
+            t0 = time.perf_counter()
+            idx = O.mean_k_index(ws, 0, h)
+            t1 = time.perf_counter()
+            A = O.head_aggregate(qn[:, h * G:(h + 1) * G], idx)
+            lst, V = O.view_list(A, n_tok, cfg.k_select, cfg.n_recent)
+            t2 = time.perf_counter()
+            kv, vv = O.materialize(ws, 0, h, lst, V, cfg.rope_theta)
+            t3 = time.perf_counter()
+            O.attend(qn[:, h * G:(h + 1) * G], kv, vv, cfg.rope_theta)
+            t4 = time.perf_counter()
+            for k, a, b in (("index", t0, t1), ("score_select", t1, t2), ("materialize", t2, t3),
+                            ("attend", t3, t4)):
+                t[k] += b - a
+    return t
+
+
+def cpu_baseline(wl, heads=(0, 1, 2, 3), small=("c1", "c2")) -> dict:
+    """The oracle as it stands, timed stage by stage on a sample: the whole
+    path for a few of the KV heads of session 0, with all BLAS threads and
+    with one, scaled to the full workload; the same for the small workloads
+    (all heads of c1, two of c2)."""
+    from workloads import CONFIGS, make_workload
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
     cfg = wl.cfg
-    ws = O.Workspace(wl.k_pool, wl.v_pool, wl.block_table, wl.n_tokens, cfg.dtype, cfg.n_q_heads,
-                     cfg.n_kv_heads, cfg.head_dim)
-    G = cfg.group
-    t0 = time.perf_counter()
-    qn = O.q_rmsnorm(O.decode(wl.q[0], cfg.dtype), wl.q_norm_w, cfg.eps)
-    n_tok = int(wl.n_tokens[0])
-    for h in heads:
-        idx = O.mean_k_index(ws, 0, h)
-        A = O.head_aggregate(qn[:, h * G:(h + 1) * G], idx)
-        lst, V = O.view_list(A, n_tok, cfg.k_select, cfg.n_recent)
-        kv, vv = O.materialize(ws, 0, h, lst, V, cfg.rope_theta)
-        O.attend(qn[:, h * G:(h + 1) * G], kv, vv, cfg.rope_theta)
-    dt = time.perf_counter() - t0
-    per_step = dt * cfg.n_kv_heads / len(heads)
-    nb = n_tok // 32
-    return {"value": nb / per_step, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
+    scale = cfg.n_kv_heads / len(heads)
+    nb = int(wl.n_tokens[0]) // 32
+    t_all = _oracle_stages(wl, heads)
+    t_one = _oracle_stages(wl, heads, threads=1)
+    per_all = {k: round(v * scale, 4) for k, v in t_all.items()}
+    per_one = {k: round(v * scale, 4) for k, v in t_one.items()}
+    sample_s = sum(t_all.values()) + sum(t_one.values())
+    others = {}
+    for name in small:
+        c = CONFIGS[name]
+        if c.name == cfg.name:
+            continue
+        w2 = make_workload(c)
+        hs = tuple(range(min(2, c.n_kv_heads)))
+        sc = c.n_kv_heads / len(hs)
+        a = _oracle_stages(w2, hs)
+        o = _oracle_stages(w2, hs, threads=1)
+        sample_s += sum(a.values()) + sum(o.values())
+        nb2 = int(w2.n_tokens[0]) // 32
+        others[c.name] = {"seconds_per_stage": {k: round(v * sc, 5) for k, v in a.items()},
+                          "seconds_per_stage_1_thread": {k: round(v * sc, 5) for k, v in o.items()},
+                          "blocks_scored_per_s": round(nb2 / (a["score_select"] * sc), 1),
+                          "heads_sampled": list(hs)}
+    return {"value": nb / per_all["score_select"], "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
             "cpu": cpu_model(), "host_cpus_available": len(os.sched_getaffinity(0)),
-            "sample": f"whole path (index, scores, selection, view, attention) for KV heads {list(heads)} of "
-                      f"{cfg.n_kv_heads}{' of session 0' if cfg.n_sessions > 1 else ''} on the same workspace, "
-                      f"{dt:.1f} s, scaled x{cfg.n_kv_heads / len(heads):.2f} to that session's step (blocks/s "
-                      f"of its {nb:,} blocks); numpy float64, BLAS threads as 'cores', elementwise work "
-                      f"single-threaded",
-            "seconds_per_step": per_step}
+            "sample": f"oracle stages (index, score + select, view, attention) for KV heads {list(heads)} of "
+                      f"{cfg.n_kv_heads} of session 0, with {threads} BLAS threads and with 1, scaled "
+                      f"x{scale:.2f}; value = complete blocks / (score + select seconds per step) with all "
+                      f"threads; numpy float64, elementwise work single-threaded; plus {', '.join(others)} "
+                      f"({sample_s:.1f} s of CPU work in all)",
+            "seconds_per_stage": per_all, "seconds_per_stage_1_thread": per_one,
+            "blocks_scored_per_s_1_thread": nb / per_one["score_select"],
+            "seconds_per_step": round(sum(per_all.values()), 4), "other_workloads": others}
 
 
 def decode_loop(wl, dev, stream, n_dec: int) -> dict:
@@ -308,23 +360,27 @@ def main():
         # index already exceeds the 256 MB MALL)
         wl = make_workload(cfg, pools=False)
         wss = [DeviceWorkspace(wl, dev)]
-        stages = ["score_select", "build_index", "materialize"]
+        stages = ["score_select", "update_index", "materialize"]
     else:
         wl = make_workload(cfg)
         wss = [DeviceWorkspace(wl, dev), DeviceWorkspace(wl, dev)]
-        separate = ["score_select", "build_index", "materialize", "attend"]
+        separate = ["score_select", "update_index", "materialize", "attend"]
         one_pass = cfg.dtype == "bf16" and cfg.T * cfg.group <= 16
-        stages = ["score_select", "build_index", "materialize_attend"] if one_pass else separate
+        stages = ["score_select", "update_index", "materialize_attend"] if one_pass else separate
     print(f"[bench] workload {cfg.name} ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     for w in wss:
         w.build_index(stream)
     torch.cuda.synchronize()
 
+    # the per-step index maintenance: rows of each session's newest complete block
+    newest = np.maximum(np.asarray(wl.n_tokens) // 32 - 1, 0).astype(np.int32)
+
     def step(i, evs=None, stage_list=None):
-        a, b = wss[i % len(wss)], wss[(i + 1) % len(wss)]
+        a = wss[i % len(wss)]
         calls = {"score_select": a.score_select, "materialize": a.materialize, "attend": a.attend,
-                 "build_index": b.build_index, "materialize_attend": lambda st: a.materialize_attend(stream=st)}
+                 "update_index": lambda st: a.update_index(newest, st),
+                 "materialize_attend": lambda st: a.materialize_attend(stream=st)}
         stage_list = stages if stage_list is None else stage_list
         for j, name in enumerate(stage_list):
             if evs is not None:
@@ -346,6 +402,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    # the full Mean-K index build (done once per workspace, not per step),
+    # the copies alternating
+    n_full = 10 if not long_chunk else 2
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_full)]
+    for i in range(n_full):
+        fev[i][0].record(stream)
+        wss[i % len(wss)].build_index(stream)
+        fev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_full = [e[0].elapsed_time(e[1]) * 1e-3 for e in fev]
 
     sep_rep = None
     if not long_chunk and stages != separate:
@@ -382,6 +449,12 @@ def main():
                         "us_p10": round(float(np.percentile(per[s], 10)) * 1e6, 2),
                         "us_p90": round(float(np.percentile(per[s], 90)) * 1e6, 2), "alg_bytes": int(ab[s]),
                         "GB/s": round(gbs, 1), "hbm_frac": round(gbs * 1e9 / HBM_PEAK, 4)}
+    mf = float(np.mean(t_full))
+    stage_rep["build_index_full"] = {"us": round(mf * 1e6, 2), "us_median": round(float(np.median(t_full)) * 1e6, 2),
+                                     "launches": n_full, "alg_bytes": int(ab["build_index_full"]),
+                                     "GB/s": round(ab["build_index_full"] / mf / 1e9, 1),
+                                     "hbm_frac": round(ab["build_index_full"] / mf / HBM_PEAK, 4),
+                                     "note": "outside the steps: the whole index of a copy, once per workspace"}
     fl = alg_flops(cfg, nb)
     stage_rep["score_select"]["alg_flops"] = fl
     stage_rep["score_select"]["TFLOP/s"] = round(fl / mean["score_select"] / 1e12, 2)
@@ -389,7 +462,7 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     res = {
         "metric": METRIC,
-        "value": nb / (wall / args.steps),
+        "value": nb / mean["score_select"],
         "unit": "blocks/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -407,7 +480,8 @@ def main():
                    "blocks": nb, "view_tokens": V, "query_tokens": cfg.T},
         "decode_step_latency_us": None,
         "recall_latency_us": round(stage_rep["score_select"]["us"] + stage_rep[stages[2]]["us"], 2),
-        "blocks_scored_per_s_score_select": nb / mean["score_select"],
+        "step_blocks_per_s": nb / (wall / args.steps),
+        "score_select_hbm_frac": stage_rep["score_select"]["hbm_frac"],
         "stages": stage_rep,
     }
     if sep_rep is not None:

@@ -35,6 +35,7 @@ EXPORTED = [
     "kvmem_materialize_attend",
     "kvmem_attention_mass_scratch_bytes",
     "kvmem_attention_mass",
+    "kvmem_view_tokens",
     "kvmem_status_string",
     "kvmem_version",
 ]
@@ -114,6 +115,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_attention_mass.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
                                          c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.kvmem_attention_mass.restype = c_int32
+    lib.kvmem_view_tokens.argtypes = [c_int32, c_void_p, c_int32, c_int32, c_void_p]
+    lib.kvmem_view_tokens.restype = c_int32
     lib.kvmem_status_string.argtypes = [c_int32]
     lib.kvmem_status_string.restype = ctypes.c_char_p
     lib.kvmem_version.argtypes = []
@@ -292,6 +295,17 @@ def kvmem_attention_mass(geom: Geom, ws: Workspace, q, T: int, q_norm_w, eps: fl
     if check:
         _check(st, "kvmem_attention_mass")
     return st
+
+
+def kvmem_view_tokens(n_tokens_host: np.ndarray, k_select: int, n_recent: int, check: bool = True) -> np.ndarray:
+    """View lengths kvmem_score_select will report for these history lengths
+    (host only); returns them as a new int32 array."""
+    n = np.ascontiguousarray(n_tokens_host, dtype=np.int32)
+    out = np.zeros(max(1, len(n)), np.int32)
+    st = load().kvmem_view_tokens(len(n), _p(n), k_select, n_recent, _p(out))
+    if check:
+        _check(st, "kvmem_view_tokens")
+    return out[:len(n)]
 
 
 def kvmem_version() -> int:

@@ -48,6 +48,15 @@ Split recent_split(int n_tok, int n_recent) {
   return r;
 }
 
+// View tokens of a history of n_tok tokens: k_eff selected whole blocks plus
+// the recent range (its partial tail block counts its valid tokens only).
+int view_length(int n_tok, int k_select, int n_recent) {
+  const Split sp = recent_split(n_tok, n_recent);
+  const int k_eff = k_select < sp.n_cand ? k_select : sp.n_cand;
+  const long tail = (long)n_tok - (long)kBT * sp.r_start;
+  return kBT * k_eff + (int)(tail > 0 ? tail : 0);
+}
+
 // Steps with many query rows per KV head (bf16) take the two-pass long-chunk
 // scorer, which never stores the score matrix.
 bool long_chunk(const kvmem_geom *g, int T) {
@@ -117,6 +126,15 @@ const char *kvmem_status_string(kvmem_status st) {
 }
 
 int32_t kvmem_version(void) { return 300; }
+
+kvmem_status kvmem_view_tokens(int32_t n_sessions, const int32_t *n_tokens_host, int32_t k_select,
+                               int32_t n_recent, int32_t *view_tokens_host) {
+  if (n_sessions <= 0 || !n_tokens_host || !view_tokens_host || k_select < 0 || n_recent < 0) return KVMEM_E_ARG;
+  for (int s = 0; s < n_sessions; ++s)
+    if (n_tokens_host[s] < 0) return KVMEM_E_ARG;
+  for (int s = 0; s < n_sessions; ++s) view_tokens_host[s] = view_length(n_tokens_host[s], k_select, n_recent);
+  return KVMEM_OK;
+}
 
 size_t kvmem_index_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t max_blocks) {
   if (check_geom(geom) != KVMEM_OK || n_sessions <= 0 || max_blocks <= 0) return 0;
@@ -215,12 +233,7 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
   const ScoreScratch sc = score_scratch(geom, S, ws->max_blocks, T);
   if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
 
-  for (int s = 0; s < S; ++s) {
-    const Split sp = recent_split(ws->n_tokens_host[s], n_recent);
-    const int k_eff = k_select < sp.n_cand ? k_select : sp.n_cand;
-    const long tail = (long)ws->n_tokens_host[s] - (long)kBT * sp.r_start;
-    view_tokens_host[s] = kBT * k_eff + (int)(tail > 0 ? tail : 0);
-  }
+  for (int s = 0; s < S; ++s) view_tokens_host[s] = view_length(ws->n_tokens_host[s], k_select, n_recent);
 
   char *base = (char *)scratch;
   float *scores = scores_opt ? scores_opt : (float *)(base + sc.scores);

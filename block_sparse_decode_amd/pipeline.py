@@ -22,14 +22,6 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
     return t.to(device)
 
 
-def view_length(n_tok: int, k_select: int, n_recent: int) -> int:
-    """View tokens of a session (what kvmem_score_select reports), used to size buffers."""
-    nb_full, nb_all = n_tok // BLOCK, -(-n_tok // BLOCK)
-    r0 = max(0, nb_all - n_recent)
-    nc = min(nb_full, r0)
-    return BLOCK * min(k_select, nc) + max(0, n_tok - BLOCK * r0)
-
-
 def v_view_token_major(v_view: torch.Tensor) -> torch.Tensor:
     """[S][Hkv][nblk][d][32 slots] dimension-major V view -> [S][Hkv][nblk*32][d]
     token-major (inverse of the slot order documented in kvmem.h)."""
@@ -60,7 +52,8 @@ def index_rows(index: torch.Tensor, max_blocks: int) -> torch.Tensor:
 class DeviceWorkspace:
     """Inputs of a workload on the GPU plus every buffer the four calls use."""
 
-    def __init__(self, wl, device="cuda", k_select=None, n_recent=None, max_view=None, with_v=True):
+    def __init__(self, wl, device="cuda", k_select=None, n_recent=None, max_view=None, with_v=True,
+                 device_pools=None):
         cfg = wl.cfg
         self.cfg = cfg
         self.device = torch.device(device)
@@ -71,7 +64,9 @@ class DeviceWorkspace:
         self.T = cfg.T
         S, H, d = cfg.n_sessions, cfg.n_kv_heads, cfg.head_dim
         self.S, self.H, self.d = S, H, d
-        if wl.k_pool is not None:
+        if device_pools is not None:           # pools the caller has already put on the device
+            self.k_pool, self.v_pool = device_pools
+        elif wl.k_pool is not None:
             self.k_pool = to_device(wl.k_pool, cfg.dtype, self.device)
             self.v_pool = to_device(wl.v_pool, cfg.dtype, self.device) if with_v else None
         else:                                   # pools too large for the host: drawn chunk by chunk
@@ -93,7 +88,7 @@ class DeviceWorkspace:
         self.n_list = self.k_select + self.n_recent
         self.view_blocks = torch.empty((S, H, max(1, self.n_list)), dtype=torch.int32, device=self.device)
         self.view_tokens = np.zeros(S, np.int32)
-        need = max(view_length(int(n), self.k_select, self.n_recent) for n in self.n_tokens)
+        need = int(L.kvmem_view_tokens(self.n_tokens, self.k_select, self.n_recent).max())
         mv = max(BLOCK, -(-need // BLOCK) * BLOCK)
         self.max_view = mv if max_view is None else max_view
         self.k_view = torch.empty((S, H, self.max_view, d), dtype=self.tdtype, device=self.device)
@@ -108,10 +103,10 @@ class DeviceWorkspace:
 
     @staticmethod
     def view_length_of(wl, k_select=None, n_recent=None) -> list:
-        """View tokens of every session of a workload (host arithmetic on the lengths)."""
+        """View tokens of every session of a workload (the library's host-side query)."""
         k = wl.cfg.k_select if k_select is None else k_select
         r = wl.cfg.n_recent if n_recent is None else n_recent
-        return [view_length(int(n), k, r) for n in wl.n_tokens]
+        return [int(v) for v in L.kvmem_view_tokens(wl.n_tokens, k, r)]
 
     def _stream_pool(self, wl, which: str) -> torch.Tensor:
         from workloads import pool_chunks
@@ -126,6 +121,11 @@ class DeviceWorkspace:
     # --- the four calls ---------------------------------------------------
     def build_index(self, stream=None):
         L.kvmem_build_index(self.geom, self.ws, self.index, stream)
+
+    def update_index(self, first_block: np.ndarray, stream=None):
+        """Index rows of blocks first_block[s] .. of every session (host array)."""
+        L.kvmem_update_index(self.geom, self.ws, np.ascontiguousarray(first_block, dtype=np.int32), self.index,
+                             stream)
 
     def score_select(self, stream=None, scores=None, agg=None):
         L.kvmem_score_select(self.geom, self.ws, self.index, self.q, self.T, self.q_norm_w, self.eps,

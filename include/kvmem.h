@@ -181,6 +181,18 @@ kvmem_status kvmem_update_index(const kvmem_geom *geom, const kvmem_workspace *w
  * scratch      : device buffer of at least kvmem_score_select_scratch_bytes().
  * Requires T >= 1, k_select >= 0, n_recent >= 0.
  * ------------------------------------------------------------------------- */
+/* The view lengths kvmem_score_select will report, computed on the host
+ * from the history lengths alone (the selection always fills its budget up to
+ * the candidates there are), for sizing the view buffers before the first
+ * selection.  For each session s < n_sessions, with N = n_tokens_host[s] and
+ * r0, nc, k_eff as above:
+ *   view_tokens_host[s] = 32 * k_eff + max(0, N - 32 * r0).
+ * Enqueues nothing and touches no device memory.  KVMEM_E_ARG for
+ * n_sessions <= 0, a NULL array, k_select < 0, n_recent < 0 or a negative
+ * length.                                                                  */
+kvmem_status kvmem_view_tokens(int32_t n_sessions, const int32_t *n_tokens_host, int32_t k_select,
+                               int32_t n_recent, int32_t *view_tokens_host);
+
 size_t kvmem_score_select_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions,
                                         int32_t max_blocks, int32_t T);
 kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *ws,

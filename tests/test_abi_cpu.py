@@ -213,3 +213,58 @@ def test_append_rejects(lib):
     ws_nov = L.Workspace(0x1000, None, 0x3000, n.ctypes.data, 2, 64, 70, None)
     assert bad(ws_=ws_nov, v_pool=None) == L.KVMEM_E_ARG  # V pool required
     assert bad(T_new=0) == L.KVMEM_OK                     # nothing to do, nothing enqueued
+
+
+def test_view_tokens_query(lib):
+    """The host-only view-length query equals the oracle's view length (the
+    selected whole blocks plus the recent range, partial tail included)."""
+    from oracle import kvmem_oracle as O
+    rng = np.random.default_rng(12)
+    n = np.concatenate([[0, 1, 31, 32, 33, 64, 32 * 100 + 7], rng.integers(0, 32 * 5000, 40)]).astype(np.int32)
+    for k, r in ((0, 0), (8, 8), (7936, 256), (3, 0), (0, 5), (10_000, 2), (1, 1000)):
+        got = L.kvmem_view_tokens(n, k, r)
+        want = [O.view_tokens(int(x), k, r) for x in n]
+        assert got.tolist() == want, (k, r)
+    out = np.zeros(2, np.int32)
+    q = L.load().kvmem_view_tokens
+    nn = np.array([64, 100], np.int32)
+    assert q(0, nn.ctypes.data, 1, 1, out.ctypes.data) == L.KVMEM_E_ARG
+    assert q(2, None, 1, 1, out.ctypes.data) == L.KVMEM_E_ARG
+    assert q(2, nn.ctypes.data, 1, 1, None) == L.KVMEM_E_ARG
+    assert q(2, nn.ctypes.data, -1, 1, out.ctypes.data) == L.KVMEM_E_ARG
+    assert q(2, nn.ctypes.data, 1, -1, out.ctypes.data) == L.KVMEM_E_ARG
+    neg = np.array([64, -1], np.int32)
+    assert q(2, neg.ctypes.data, 1, 1, out.ctypes.data) == L.KVMEM_E_ARG
+
+
+def test_attention_mass_rejects(lib):
+    ws, n = _ws()
+    g = _geom()
+    need = L.kvmem_attention_mass_scratch_bytes(g, 2, 1, 64)
+    assert need > 0 and need % 256 == 0
+    assert L.kvmem_attention_mass_scratch_bytes(g, 0, 1, 64) == 0
+    assert L.kvmem_attention_mass_scratch_bytes(g, 2, 0, 64) == 0
+    assert L.kvmem_attention_mass_scratch_bytes(_geom(d=64), 2, 1, 64) == 0
+    call = lambda **kw: L.kvmem_attention_mass(**{**dict(
+        geom=g, ws=ws, q=0x10, T=1, q_norm_w=0x20, eps=1e-6, view_blocks=0x30, n_list=4, rope_theta=1e6,
+        mass=0x40, lse=None, scratch=0x50, scratch_bytes=need, check=False), **kw})
+    assert call(q=None) == L.KVMEM_E_ARG
+    assert call(q_norm_w=None) == L.KVMEM_E_ARG
+    assert call(mass=None) == L.KVMEM_E_ARG
+    assert call(T=0) == L.KVMEM_E_ARG
+    assert call(n_list=-1) == L.KVMEM_E_ARG
+    assert call(view_blocks=None) == L.KVMEM_E_ARG          # a list of 4 entries without a buffer
+    assert call(eps=float("nan")) == L.KVMEM_E_ARG
+    assert call(eps=-1.0) == L.KVMEM_E_ARG
+    assert call(rope_theta=1.0) == L.KVMEM_E_ARG
+    assert call(rope_theta=float("inf")) == L.KVMEM_E_ARG
+    assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
+    assert call(scratch=None) == L.KVMEM_E_WORKSPACE
+    assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head
+    assert call(geom=_geom("f32")) == L.KVMEM_E_UNSUPPORTED  # bf16 workspaces only
+    assert call(geom=_geom(d=64)) == L.KVMEM_E_UNSUPPORTED
+    ws2, n2 = _ws(n_tok=(100, 64 * 32 + 1))                  # longer than the table
+    assert call(ws=ws2) == L.KVMEM_E_ARG
+    st = L.load().kvmem_attention_mass(ctypes.byref(g), None, 0x10, 1, 0x20, 1e-6, 0x30, 4, 1e6, 0x40, None,
+                                       0x50, need, None)
+    assert st == L.KVMEM_E_ARG

@@ -6,7 +6,7 @@ history-block and view-block boundaries, the third does not) each followed by
 attention.  Bars:
 pools bit-exact (every page, spare pages included), index rows bit-exact, V
 view bit-exact, K view within one bf16 ulp (the gather's bar), the view's tail
-slots zero, attention within the attention bar.
+slots zero, attention within the attention bar and the regression bar.
 """
 from __future__ import annotations
 
@@ -17,7 +17,7 @@ import torch
 from oracle import kvmem_oracle as O
 from tests.certify import certify
 from tests.helpers import make_workload, oracle_ws, small_cfg
-from tests.test_gpu_parity import ATT_TOL, _bits_to_f64
+from tests.test_gpu_parity import ATT_TOL, _bits_to_f64, reg_bar
 from workloads import draw_decode_tokens, with_decode_capacity
 
 pytestmark = pytest.mark.gpu
@@ -109,4 +109,5 @@ def test_append_parity(name):
                 o_ref = O.attend(qn[:, h * G:(h + 1) * G], kv, vv, cfg.rope_theta)
                 err = float(np.abs(out[s, :, h * G:(h + 1) * G] - o_ref).max())
                 assert err <= ATT_TOL[cfg.dtype], (name, step, s, h, "attend", err)
+                assert err <= reg_bar(o_ref), (name, step, s, h, "attend regression bar", err, reg_bar(o_ref))
     assert int(dw.dev_error.item()) == 0

@@ -6,7 +6,8 @@ Bars (from the scope of the hot path):
   * aggregated scores A     : |d| <= 1e-3 * A_ref
   * selected blocks, view   : bit-exact (inputs certified with a 1e-3 cut margin)
   * V view                  : bit-exact;  K view: <= 1 bf16 ulp / 2e-6 relative fp32
-  * attention output        : <= 2e-2 max-abs for bf16, <= 1e-4 for fp32
+  * attention output        : <= 2e-2 max-abs for bf16, <= 1e-4 for fp32, and
+                              the regression bar below
 """
 from __future__ import annotations
 
@@ -24,6 +25,22 @@ from workloads import CONFIGS
 pytestmark = pytest.mark.gpu
 
 ATT_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+# Regression bar, applied beside ATT_TOL to every attention output of a (session,
+# KV head): |o_gpu - o_ref| <= REG_REL * max|o_ref| + REG_ABS.  The kernels form
+# each logit from bf16 hi + lo query operands (~2^-16 relative) and accumulate
+# every product, exponential and weighted sum in fp32; their keys differ from the
+# oracle's by one bf16 ulp only on the elements whose exact rotated value lies
+# within the fp32 rotation error of a rounding boundary (a fraction ~1e-5 of
+# them).  Together that moves an output, a convex combination of value rows,
+# by far less than 1e-3 of its largest coordinate, while a 32-token tile that a
+# kernel drops or counts twice in a diffuse 262,144-token view moves it by about
+# p_tile * |v_tile - o| ~ 1.2e-4 * 0.5, several times the bar there.
+REG_REL, REG_ABS = 1e-3, 2e-6
+
+
+def reg_bar(o_ref: np.ndarray) -> float:
+    return REG_REL * (float(np.abs(o_ref).max()) if o_ref.size else 0.0) + REG_ABS
 
 
 def _need_gpu():
@@ -117,8 +134,10 @@ def check_session(wl, res, s, heads=None, att_heads=None, check_scores=True, tag
         o_ref = O.attend(qn[:, h * G:(h + 1) * G], kv, vv, cfg.rope_theta)
         o_gpu = res["out"][s, :, h * G:(h + 1) * G]
         err = float(np.abs(o_gpu - o_ref).max()) if V else float(np.abs(o_gpu).max())
-        worst_att = max(worst_att, err)
+        bar = reg_bar(o_ref)
+        worst_att = max(worst_att, err / bar)
         assert err <= ATT_TOL[cfg.dtype], (tag, s, h, "attend", err)
+        assert err <= bar, (tag, s, h, "attend regression bar", err, bar)
     return worst_att
 
 
@@ -128,7 +147,7 @@ def _full_check(wl, attend=True, **kw):
     worst = 0.0
     for s in range(wl.cfg.n_sessions):
         worst = max(worst, check_session(wl, res, s, tag=wl.cfg.name, **kw))
-    print(f"[gpu] {wl.cfg.name}: worst attention |err| = {worst:.3e}", flush=True)
+    print(f"[gpu] {wl.cfg.name}: worst attention |err| / regression bar = {worst:.3f}", flush=True)
     return res
 
 
@@ -394,26 +413,73 @@ def test_c4_full():
 C5_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "c5_10m_golden.npz")
 
 
+def _c5_device_pools_and_views(wl, lists, cfg):
+    """Draws the K and V pools chunk by chunk straight onto the device and,
+    from the same chunks, the oracle's view of every listed block (its keys
+    rotated at the view positions and rounded, its values as stored), plus the
+    oracle's index rows of a sample of chunks.  Returns the device pools, the
+    expected views [H][V][d] (float32, exact bf16 values) and the sampled rows."""
+    from block_sparse_decode_amd.pipeline import to_device
+    from tests.certify import chunk_workspace
+    from workloads import pool_chunks
+    H, d = cfg.n_kv_heads, cfg.head_dim
+    n_tok = int(wl.n_tokens[0])
+    last = -(-n_tok // 32)
+    V = 32 * lists.shape[1]
+    shape = (wl.n_pages, H, 32, d)
+    exp = {"k": np.full((H, V, d), np.nan, np.float32), "v": np.full((H, V, d), np.nan, np.float32)}
+    sample = {0, ((last - 1) // 1024) * 1024, (int(lists[0, 0]) // 1024) * 1024, 100 * 1024, 200 * 1024}
+    rows = {}
+    pools = {}
+    for which in ("k", "v"):
+        pool = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        for _, b0, pages, x in pool_chunks(wl, which):
+            idx = torch.from_numpy(np.ascontiguousarray(pages, dtype=np.int64)).to("cuda")
+            pool[idx] = to_device(x, "bf16", "cuda")
+            cws = chunk_workspace(wl, 0, b0, x)
+            b1 = b0 + x.shape[0]
+            if which == "k" and b0 in sample:
+                n = min(b1, n_tok // 32) - b0
+                rows[b0] = [O.mean_k_rows(cws, 0, h, range(n)) for h in range(H)]
+            for h in range(H):
+                ms = np.nonzero((lists[h] >= b0) & (lists[h] < b1))[0]
+                if len(ms) == 0:
+                    continue
+                toks = O.block_tokens_of(cws, cws.k_pool, 0, h, [int(lists[h, m]) - b0 for m in ms])  # [n][32][d]
+                if which == "k":
+                    pos = (32 * ms[:, None] + np.arange(32)[None, :]).reshape(-1)
+                    rot = O.round_store(O.rope(toks.reshape(-1, d), pos, cfg.rope_theta), "bf16")
+                    exp["k"][h, pos] = rot.astype(np.float32)
+                else:
+                    pos = (32 * ms[:, None] + np.arange(32)[None, :]).reshape(-1)
+                    exp["v"][h, pos] = toks.reshape(-1, d).astype(np.float32)
+        pools[which] = pool
+        print(f"[gpu] c5: {which.upper()} pool drawn on the device, views of its listed blocks computed", flush=True)
+    return (pools["k"], pools["v"]), exp, rows
+
+
 def test_c5_full():
     """10,000,000 tokens (312,500 blocks), a 512-token query chunk x 64 heads,
     top-2048 per KV head, 65,536-token view: the two-pass matrix-core scorer
-    at full size.  The oracle at this size takes minutes, so its results (the
-    certified view lists, A on every selected block and on a sample of the
-    others, and the key repair log the certification made) come from
-    tests/golden/make_c5_golden.py; index rows and view blocks of two pool
-    chunks are recomputed here from redrawn chunks."""
+    at full size.  The oracle's scoring at this size takes minutes, so its
+    results (the certified view lists, A on every selected block and on a
+    sample of the others, and the key repair log the certification made) come
+    from tests/golden/make_c5_golden.py.  The pools are drawn here chunk by
+    chunk, and from the same chunks the oracle gives every listed block's view
+    (all 16,384 view blocks are compared) and the index rows of a sample of
+    chunks."""
     _need_gpu()
     from block_sparse_decode_amd.pipeline import DeviceWorkspace, index_rows, v_view_token_major
-    from tests.certify import chunk_workspace
-    from workloads import pool_chunks
     if not os.path.exists(C5_GOLDEN):
         pytest.skip("tests/golden/c5_10m_golden.npz not generated")
     g = np.load(C5_GOLDEN)
     repairs = [(int(a), int(b), int(c), int(d), float(e)) for a, b, c, d, e in g["repairs"]]
     cfg = CONFIGS["c5"]
     wl = make_workload(cfg, pools=False, repairs=repairs)
+    lists = g["lists"]
     print(f"[gpu] c5: drawing {wl.n_pages} pages of K and V on the device ({len(repairs)} key repairs)", flush=True)
-    dw = DeviceWorkspace(wl, "cuda")
+    pools, exp, rows = _c5_device_pools_and_views(wl, lists, cfg)
+    dw = DeviceWorkspace(wl, "cuda", device_pools=pools)
     H, G, mb = cfg.n_kv_heads, cfg.group, dw.max_blocks
     ag = torch.full((1, H, mb), float("nan"), device="cuda")
     dw.build_index()
@@ -425,7 +491,7 @@ def test_c5_full():
     nc, _, _ = O.recent_split(n_tok, cfg.n_recent)
     # selection (bit-exact) and view length
     vb = dw.view_blocks.cpu().numpy()[0]
-    assert np.array_equal(vb, g["lists"])
+    assert np.array_equal(vb, lists)
     V = int(dw.view_tokens[0])
     assert V == int(g["view_tokens"]) == 65536
     # aggregated scores on the sampled blocks; every head's A sums to T * G
@@ -436,36 +502,22 @@ def test_c5_full():
         assert np.all(np.abs(a_gpu - a_ref) <= 1e-3 * a_ref + 1e-30), (h, "A")
         assert abs(A[h, :nc].sum() - g["a_sums"][h]) <= 1e-3 * g["a_sums"][h], (h, "sum A")
         assert abs(g["a_sums"][h] - cfg.T * G) <= 1e-6 * cfg.T * G
-    # index rows and view blocks of two redrawn chunks (one holding head 0's
-    # first selected block, and the last chunk)
-    lists = g["lists"]
-    last = -(-n_tok // 32)
-    starts = sorted({(int(lists[0, 0]) // 1024) * 1024, ((last - 1) // 1024) * 1024})
-    jobs = [(0, b0, min(b0 + 1024, last)) for b0 in starts]
-    kch = {b0: x for _, b0, _, x in pool_chunks(wl, "k", jobs=jobs)}
-    vch = {b0: x for _, b0, _, x in pool_chunks(wl, "v", jobs=jobs)}
+    # index rows of the sampled chunks
     idx_dev = index_rows(dw.index, mb)
-    vview = v_view_token_major(dw.v_view)
-    n_view_checked = 0
-    for (_, b0, b1) in jobs:
-        kws = chunk_workspace(wl, 0, b0, kch[b0])
-        vws = chunk_workspace(wl, 0, b0, vch[b0])
-        n = min(b1, n_tok // 32) - b0
+    for b0, want in rows.items():
+        n = want[0].shape[0]
         for h in range(H):
             got = _bits_to_f64(idx_dev[0, h, b0:b0 + n].contiguous(), "bf16")
-            assert np.array_equal(got, O.mean_k_rows(kws, 0, h, range(n))), (b0, h, "index")
-            for m in np.nonzero((lists[h] >= b0) & (lists[h] < b1))[0]:
-                beta = int(lists[h, m]) - b0
-                pos = 32 * int(m) + np.arange(32)
-                kv = O.round_store(O.rope(O.block_tokens_of(kws, kws.k_pool, 0, h, [beta])[0], pos,
-                                          cfg.rope_theta), "bf16")
-                vv = O.block_tokens_of(vws, vws.k_pool, 0, h, [beta])[0]
-                kg = _bits_to_f64(dw.k_view[0, h, pos[0]:pos[0] + 32].contiguous(), "bf16")
-                vg = _bits_to_f64(vview[0, h, pos[0]:pos[0] + 32].contiguous(), "bf16")
-                ulp = np.ldexp(1.0, np.frexp(np.abs(kv))[1] - 8)
-                rot = 1e-6 * np.abs(kv).max(axis=-1, keepdims=True)
-                assert np.all(np.abs(kg - kv) <= ulp + rot), (h, int(m), "K view")
-                assert np.array_equal(vg, vv), (h, int(m), "V view")
-                n_view_checked += 1
-    print(f"[gpu] c5: selection, A samples, index rows and {n_view_checked} view blocks match", flush=True)
-    assert n_view_checked > 0
+            assert np.array_equal(got, want[h]), (b0, h, "index")
+    # every view block: V bit for bit, K within one bf16 ulp
+    kg = _bits_to_f64(dw.k_view[0, :, :V].contiguous(), "bf16")
+    vg = _bits_to_f64(v_view_token_major(dw.v_view)[0, :, :V].contiguous(), "bf16")
+    kv = exp["k"].astype(np.float64)
+    assert not np.isnan(kv).any() and not np.isnan(exp["v"]).any()
+    assert np.array_equal(vg, exp["v"].astype(np.float64)), "V view"
+    ulp = np.ldexp(1.0, np.frexp(np.abs(kv))[1] - 8)
+    rot = 1e-6 * np.abs(kv).max(axis=-1, keepdims=True)
+    bad = np.abs(kg - kv) > ulp + rot
+    assert not bad.any(), ("K view", np.argwhere(bad)[:4])
+    print(f"[gpu] c5: selection, A samples, index rows of {len(rows)} chunks and all "
+          f"{H * V // 32} view blocks match", flush=True)

@@ -209,6 +209,28 @@ def test_softmax_against_scipy_and_mass():
     np.testing.assert_allclose(O.softmax_blocks(s + rng.standard_normal((3, 8, 1)) * 50), p, rtol=1e-12)
 
 
+@pytest.mark.parametrize("T,t_chunk,G,nb", [(7, 3, 4, 50), (512, 16, 8, 96), (5, 1, 2, 7), (9, 20, 8, 33),
+                                            (6, 6, 3, 40)])
+def test_head_aggregate_chunked(T, t_chunk, G, nb):
+    """The chunked aggregation (it wrote the 10M-token golden, 16 query tokens
+    at a time) against scipy's softmax over the same scores, summed over all
+    tokens and heads, for chunk sizes that do and do not divide T; and the
+    closed form sum_beta A = T * G."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(T * 1000 + t_chunk)
+    d = 128
+    qg = rng.standard_normal((T, G, d)) * 3
+    index = rng.standard_normal((nb, d))
+    s = np.einsum("tgi,bi->tgb", qg, index) / math.sqrt(d)
+    want = softmax(s, axis=-1).sum(axis=(0, 1))
+    got = O.head_aggregate(qg, index, t_chunk)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-300)
+    assert abs(got.sum() - T * G) <= 1e-10 * T * G
+    # a chunk that the loop dropped or counted twice changes the sum by G * t_chunk
+    if 0 < t_chunk < T:
+        assert abs(O.head_aggregate(qg[:T - 1], index, t_chunk).sum() - (T - 1) * G) <= 1e-10 * T * G
+
+
 # ---------------------------------------------------------------------------
 # O6/O7 selection
 # ---------------------------------------------------------------------------
