@@ -28,6 +28,7 @@ EXPORTED = [
     "kvmem_materialize",
     "kvmem_attend_scratch_bytes",
     "kvmem_attend",
+    "kvmem_attend_noalloc",
     "kvmem_update_index",
     "kvmem_append",
     "kvmem_attend_paged_scratch_bytes",
@@ -96,6 +97,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_attend.argtypes = [POINTER(Geom), c_int32, c_void_p, c_int32, c_void_p, c_float, c_void_p,
                                  c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.kvmem_attend.restype = c_int32
+    lib.kvmem_attend_noalloc.argtypes = [POINTER(Geom), c_int32, c_void_p, c_int32, c_void_p, c_float, c_void_p,
+                                         c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p]
+    lib.kvmem_attend_noalloc.restype = c_int32
     lib.kvmem_update_index.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p, c_void_p]
     lib.kvmem_update_index.restype = c_int32
     lib.kvmem_append.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
@@ -224,6 +228,20 @@ def kvmem_attend(geom: Geom, n_sessions: int, q, T: int, q_norm_w, eps: float, k
                              scratch_bytes, _stream(stream))
     if check:
         _check(st, "kvmem_attend")
+    return st
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # KVMEM_NOALLOC_SCRATCH_BYTES
+
+
+def kvmem_attend_noalloc(geom: Geom, n_sessions: int, q, T: int, q_norm_w, eps: float, k_view, v_view,
+                         view_tokens_host: np.ndarray, max_view: int, rope_theta: float, out, stream=None,
+                         check: bool = True) -> int:
+    st = load().kvmem_attend_noalloc(ctypes.byref(geom), n_sessions, _p(q), T, _p(q_norm_w), eps, _p(k_view),
+                                     _p(v_view), _p(view_tokens_host), max_view, rope_theta, _p(out),
+                                     _stream(stream))
+    if check:
+        _check(st, "kvmem_attend_noalloc")
     return st
 
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/kvmem.h"
 #include "kvmem_internal.h"
 
@@ -110,7 +112,31 @@ AttendScratch attend_scratch(const kvmem_geom *g, int S, int T, int max_view) {
   return r;
 }
 
+// Scratch of kvmem_attend_noalloc: the library's own device array, one per
+// GPU (each device holds its own copy of a __device__ variable), kept until
+// the process ends.  Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress, looked up once per device on
+// the first call made with that device current, and cached here.
+constexpr size_t kNoAllocBytes = KVMEM_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoAllocDevices = 64;
+std::atomic<void *> g_noalloc_ptr[kNoAllocDevices];
+
 }  // namespace
+
+static __device__ __align__(256) unsigned char kvmem_noalloc_scratch[kNoAllocBytes];
+
+// Device address of the current device's copy of kvmem_noalloc_scratch.
+static kvmem_status noalloc_scratch(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocDevices) return KVMEM_E_HIP;
+  void *p = g_noalloc_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(kvmem_noalloc_scratch)) != hipSuccess || p == nullptr) return KVMEM_E_HIP;
+    g_noalloc_ptr[dev].store(p, std::memory_order_release);   // the same address if two threads race here
+  }
+  *ptr = p;
+  return KVMEM_OK;
+}
 
 extern "C" {
 
@@ -482,10 +508,12 @@ size_t kvmem_attend_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, in
   return attend_scratch(geom, n_sessions, T, max_view).total;
 }
 
-kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,
-                          const float *q_norm_w, float eps, const void *k_view, const void *v_view,
-                          const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
-                          void *scratch, size_t scratch_bytes, void *stream) {
+// Argument checks of kvmem_attend (all of them, before any HIP call); on
+// success *sc holds the scratch layout the call needs.
+static kvmem_status attend_check(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,
+                                 const float *q_norm_w, float eps, const void *k_view, const void *v_view,
+                                 const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
+                                 AttendScratch *sc) {
   kvmem_status st = check_geom(geom);
   if (st != KVMEM_OK) return st;
   if (n_sessions <= 0 || !q || !q_norm_w || !k_view || !v_view || !view_tokens_host || !out || T <= 0)
@@ -496,32 +524,66 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions, const void
   for (int s = 0; s < n_sessions; ++s)
     if (view_tokens_host[s] < 0 || view_tokens_host[s] > max_view) return KVMEM_E_ARG;
   const int bf16 = geom->kv_dtype == KVMEM_BF16;
-  const int G = geom->n_q_heads / geom->n_kv_heads;
-  const long rows = (long)T * G;
+  const long rows = (long)T * (geom->n_q_heads / geom->n_kv_heads);
   if ((bf16 && rows > 32) || (!bf16 && rows > 64)) return KVMEM_E_UNSUPPORTED;
-  const AttendScratch sc = attend_scratch(geom, n_sessions, T, max_view);
-  if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
+  *sc = attend_scratch(geom, n_sessions, T, max_view);
+  return KVMEM_OK;
+}
+
+// The launches of kvmem_attend over a checked call, with its scratch at `base`.
+static kvmem_status attend_launch(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,
+                                  const float *q_norm_w, float eps, const void *k_view, const void *v_view,
+                                  const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
+                                  const AttendScratch &sc, char *base, void *stream) {
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
   AttendGeom g;
   g.Tq = T;
   g.Hq = geom->n_q_heads;
   g.Hkv = geom->n_kv_heads;
-  g.G = G;
-  g.rows = (int)rows;
+  g.G = g.Hq / g.Hkv;
+  g.rows = T * g.G;
   g.max_view = max_view;
   g.max_splits = sc.max_splits;
   g.tpw = sc.tpw;
-  char *base = (char *)scratch;
   for (int s0 = 0; s0 < n_sessions; s0 += kMaxSess) {
     const int n = n_sessions - s0 < kMaxSess ? n_sessions - s0 : kMaxSess;
     SessI32 vt;
     memset(&vt, 0, sizeof(vt));
     for (int i = 0; i < n; ++i) vt.v[i] = view_tokens_host[s0 + i];
-    st = hip_status(launch_attend(bf16, q, q_norm_w, eps, k_view, v_view, (float *)(base + sc.part_o),
-                                  (float2 *)(base + sc.part_ml), out, vt, s0, n, g,
-                                  (double)rope_theta, (hipStream_t)stream));
+    const kvmem_status st = hip_status(launch_attend(bf16, q, q_norm_w, eps, k_view, v_view,
+                                                     (float *)(base + sc.part_o), (float2 *)(base + sc.part_ml),
+                                                     out, vt, s0, n, g, (double)rope_theta, (hipStream_t)stream));
     if (st != KVMEM_OK) return st;
   }
   return KVMEM_OK;
+}
+
+kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,
+                          const float *q_norm_w, float eps, const void *k_view, const void *v_view,
+                          const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
+                          void *scratch, size_t scratch_bytes, void *stream) {
+  AttendScratch sc;
+  const kvmem_status st = attend_check(geom, n_sessions, q, T, q_norm_w, eps, k_view, v_view, view_tokens_host,
+                                       max_view, rope_theta, out, &sc);
+  if (st != KVMEM_OK) return st;
+  if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
+  return attend_launch(geom, n_sessions, q, T, q_norm_w, eps, k_view, v_view, view_tokens_host, max_view,
+                       rope_theta, out, sc, (char *)scratch, stream);
+}
+
+kvmem_status kvmem_attend_noalloc(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,
+                                  const float *q_norm_w, float eps, const void *k_view, const void *v_view,
+                                  const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
+                                  void *stream) {
+  AttendScratch sc;
+  kvmem_status st = attend_check(geom, n_sessions, q, T, q_norm_w, eps, k_view, v_view, view_tokens_host, max_view,
+                                 rope_theta, out, &sc);
+  if (st != KVMEM_OK) return st;
+  if (sc.total > kNoAllocBytes) return KVMEM_E_WORKSPACE;
+  void *base = nullptr;
+  if ((st = noalloc_scratch(&base)) != KVMEM_OK) return st;
+  return attend_launch(geom, n_sessions, q, T, q_norm_w, eps, k_view, v_view, view_tokens_host, max_view,
+                       rope_theta, out, sc, (char *)base, stream);
 }
 
 }  // extern "C"

@@ -268,6 +268,33 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions,
                           void *scratch, size_t scratch_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * kvmem_attend for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no scratch argument and calls no allocating routine; otherwise it is
+ * kvmem_attend (same checks, same kernels, the same output bits).
+ *
+ * Its scratch is the library's own device array of
+ * KVMEM_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends.  A
+ * call that needs more (kvmem_attend_scratch_bytes() above the constant, e.g.
+ * more than four sessions of 262,144-token views at 64 query / 8 KV heads)
+ * returns KVMEM_E_WORKSPACE and enqueues nothing.  The call runs on the
+ * current device (stream must belong to it).  The array's device address is
+ * looked up once per device, on the first call made with that device
+ * current: make one call before capturing a graph.  Every call on a GPU
+ * shares that GPU's array and leaves its partial results there; nothing in
+ * it needs to start at zero (a call reads only partials it wrote itself), but
+ * calls that overlap on one GPU (other streams, other host threads) race:
+ * serialise them, e.g. on one stream.  KVMEM_E_HIP if the device or the
+ * array's address cannot be obtained.
+ * ------------------------------------------------------------------------- */
+#define KVMEM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+kvmem_status kvmem_attend_noalloc(const kvmem_geom *geom, int32_t n_sessions,
+                                  const void *q, int32_t T, const float *q_norm_w, float eps,
+                                  const void *k_view, const void *v_view,
+                                  const int32_t *view_tokens_host, int32_t max_view,
+                                  float rope_theta, float *out, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Attention straight from the paged history ([README 'Core equation']: the
  * address space and the execution window are separate; [REVIEW 'Summary']:
  * the view is the selected blocks re-RoPE'd to contiguous positions).

@@ -268,3 +268,31 @@ def test_attention_mass_rejects(lib):
     st = L.load().kvmem_attention_mass(ctypes.byref(g), None, 0x10, 1, 0x20, 1e-6, 0x30, 4, 1e6, 0x40, None,
                                        0x50, need, None)
     assert st == L.KVMEM_E_ARG
+
+
+def test_attend_noalloc_rejects(lib):
+    """The scratch-free attention checks its arguments like kvmem_attend and
+    refuses a call whose scratch would exceed its array, all before any HIP
+    call."""
+    g = _geom()
+    vt = np.array([64, 96], np.int32)
+    call = lambda **kw: L.kvmem_attend_noalloc(**{**dict(geom=g, n_sessions=2, q=0x10, T=1, q_norm_w=0x20,
+                                                         eps=1e-6, k_view=0x30, v_view=0x40, view_tokens_host=vt,
+                                                         max_view=128, rope_theta=1e6, out=0x50, check=False),
+                                                  **kw})
+    assert call(T=0) == L.KVMEM_E_ARG
+    assert call(n_sessions=0) == L.KVMEM_E_ARG
+    assert call(out=None) == L.KVMEM_E_ARG
+    assert call(q=None) == L.KVMEM_E_ARG
+    assert call(view_tokens_host=np.array([64, 160], np.int32)) == L.KVMEM_E_ARG
+    assert call(max_view=100) == L.KVMEM_E_ARG
+    assert call(eps=float("nan")) == L.KVMEM_E_ARG
+    assert call(rope_theta=1.0) == L.KVMEM_E_ARG
+    assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head in bf16
+    assert call(geom=_geom(bt=64)) == L.KVMEM_E_UNSUPPORTED
+    # beyond the array: eight sessions of 262,144-token views
+    S, mv = 8, 262144
+    assert L.kvmem_attend_scratch_bytes(g, S, 1, mv) > L.NOALLOC_SCRATCH_BYTES
+    big = np.full(S, mv, np.int32)
+    assert call(n_sessions=S, view_tokens_host=big, max_view=mv) == L.KVMEM_E_WORKSPACE
+    assert L.kvmem_attend_scratch_bytes(g, 1, 1, mv) <= L.NOALLOC_SCRATCH_BYTES
