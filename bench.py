@@ -285,6 +285,75 @@ def paged_vs_view(wl, dev, stream, reps: int = 10) -> dict:
             "tokens_per_view_breakeven_one_pass": None if breakeven_fu is None else round(breakeven_fu, 1)}
 
 
+HOST_LINK_PEAK = 64.0e9   # B/s per direction, PCIe Gen5 x16 (the MI355X host interface)
+
+
+def host_tier(wl, dev, stream, reps: int = 5) -> dict:
+    """Host-tier paging: the K/V pools in pinned host memory (read by the GPU
+    in place), the Mean-K index built from them into HBM, then per recall step
+    score_select -> kvmem_stage_view (the listed tiles over the host link into
+    an HBM staging pool) -> the one-pass gather + attention on the staged pool.
+    Reports the staged bytes per second against the link's peak, and the copy
+    overlapped with decode attention of a device-resident copy of the
+    workspace on another stream (normal priority) against the two back to
+    back."""
+    import torch
+
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace, StagedView
+
+    cfg = wl.cfg
+    dw = DeviceWorkspace(wl, dev, host_pools=True)
+
+    def timed(fn, n=reps):
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    t_idx = timed(lambda: dw.build_index(stream), 2)
+    t_ss = timed(lambda: dw.score_select(stream))
+    st = StagedView(dw)
+    t_st = timed(lambda: dw.stage(st, stream))
+    t_ma = timed(lambda: dw.materialize_attend_staged(st, stream=stream))
+    b = 2 if cfg.dtype == "bf16" else 4
+    V = int(np.sum(dw.view_tokens))
+    staged = 2 * cfg.n_kv_heads * cfg.head_dim * b * V
+    idx_bytes = 32 * cfg.n_kv_heads * cfg.head_dim * b * int(np.sum(np.asarray(wl.n_tokens) // 32))
+    # overlap: decode attention of a device-resident copy on another stream
+    hb = DeviceWorkspace(wl, dev)
+    hb.build_index(stream)
+    hb.score_select(stream)
+    hb.materialize(stream)
+    torch.cuda.synchronize()
+    t_att = timed(lambda: hb.attend(stream))
+    n_att = max(1, int(t_st / t_att))
+    t_atts = timed(lambda: [hb.attend(stream) for _ in range(n_att)], 3)
+    s2 = torch.cuda.Stream(dev)
+    tog = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        dw.stage(st, s2)
+        for _ in range(n_att):
+            hb.attend(stream)
+        torch.cuda.synchronize()
+        tog.append((time.perf_counter() - a) * 1e6)
+    return {"stage_us": round(t_st, 1), "staged_bytes": staged, "staged_GB/s": round(staged / t_st / 1e3, 2),
+            "link_peak_GB/s": HOST_LINK_PEAK / 1e9, "link_frac": round(staged / (t_st * 1e-6) / HOST_LINK_PEAK, 4),
+            "index_build_from_host_us": round(t_idx, 1),
+            "index_build_from_host_GB/s": round(idx_bytes / t_idx / 1e3, 2),
+            "score_select_us": round(t_ss, 2), "materialize_attend_staged_us": round(t_ma, 2),
+            "recall_from_host_us": round(t_ss + t_st + t_ma, 1),
+            "overlap": {"decode_attentions": n_att, "attention_us": round(t_att, 2),
+                        "stage_alone_us": round(t_st, 1), "attentions_alone_us": round(t_atts, 1),
+                        "back_to_back_us": round(t_st + t_atts, 1), "together_us": round(float(np.median(tog)), 1)}}
+
+
 def mass_diagnostic(wl, dev, stream, reps: int = 5) -> dict:
     """Selection-quality diagnostic: share of full attention over the history
     that the selected blocks carry, and that the recent-only control (the
@@ -335,6 +404,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-diagnostic", action="store_true",
                     help="skip the selection-quality diagnostic after the timed steps")
+    ap.add_argument("--no-host-tier", action="store_true",
+                    help="skip the host-tier paging measurement after the timed steps")
     ap.add_argument("--decode-tokens", type=int, default=256,
                     help="decode steps over one reused view after the timed steps (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -503,6 +574,11 @@ def main():
         dec = decode_loop(wl, dev, stream, args.decode_tokens)
         res["decode"] = dec
         res["decode_step_latency_us"] = dec["step_us_median"]
+    if not long_chunk and not args.no_host_tier:
+        print("[bench] host-tier paging (pinned host pools, staging over the host link) ...", file=sys.stderr,
+              flush=True)
+        res["host_tier"] = host_tier(wl, dev, stream)
+        torch.cuda.empty_cache()
     if not long_chunk and not args.no_diagnostic:
         print("[bench] attention from the pages vs gather + view attention ...", file=sys.stderr, flush=True)
         res["paged_attend"] = paged_vs_view(wl, dev, stream)

@@ -26,6 +26,7 @@ EXPORTED = [
     "kvmem_score_select_scratch_bytes",
     "kvmem_score_select",
     "kvmem_materialize",
+    "kvmem_stage_view",
     "kvmem_attend_scratch_bytes",
     "kvmem_attend",
     "kvmem_attend_noalloc",
@@ -92,6 +93,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_materialize.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p,
                                       c_int32, c_float, c_void_p, c_void_p, c_void_p]
     lib.kvmem_materialize.restype = c_int32
+    lib.kvmem_stage_view.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.kvmem_stage_view.restype = c_int32
     lib.kvmem_attend_scratch_bytes.argtypes = [POINTER(Geom), c_int32, c_int32, c_int32]
     lib.kvmem_attend_scratch_bytes.restype = c_size_t
     lib.kvmem_attend.argtypes = [POINTER(Geom), c_int32, c_void_p, c_int32, c_void_p, c_float, c_void_p,
@@ -211,6 +215,16 @@ def kvmem_materialize(geom: Geom, ws: Workspace, view_blocks, n_list: int, view_
                                   _stream(stream))
     if check:
         _check(st, "kvmem_materialize")
+    return st
+
+
+def kvmem_stage_view(geom: Geom, ws: Workspace, view_blocks, n_list: int, view_tokens_host: np.ndarray, stage_k,
+                     stage_v, stage_table, stage_list, stream=None, check: bool = True) -> int:
+    st = load().kvmem_stage_view(ctypes.byref(geom), ctypes.byref(ws), _p(view_blocks), n_list,
+                                 _p(view_tokens_host), _p(stage_k), _p(stage_v), _p(stage_table), _p(stage_list),
+                                 _stream(stream))
+    if check:
+        _check(st, "kvmem_stage_view")
     return st
 
 

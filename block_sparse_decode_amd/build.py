@@ -29,7 +29,7 @@ FLAGS = [
 ]
 SOURCES = ["kvmem_api.hip", "k_index.hip", "k_score.hip", "k_score_mfma.hip", "k_score_long.hip", "k_select.hip", "k_materialize.hip",
            "k_attend.hip", "k_append.hip",
-           "k_attend_paged.hip"]
+           "k_attend_paged.hip", "k_stage.hip"]
 
 
 def hipcc() -> str:

@@ -38,6 +38,19 @@ kvmem_status check_ws(const kvmem_workspace *w, bool need_v) {
 
 kvmem_status hip_status(hipError_t e) { return e == hipSuccess ? KVMEM_OK : KVMEM_E_HIP; }
 
+// True when the GPU can read p at address p: device memory, or pinned host
+// memory mapped into the device's address space (hipHostMalloc).  A pointer
+// HIP does not know (pageable memory) is refused; its lookup error is cleared
+// so that it does not surface at a later launch check.
+bool gpu_addressable(const void *p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return a.devicePointer == p;
+}
+
 struct Split {
   int n_cand, r_start, n_all, n_full;
 };
@@ -464,6 +477,43 @@ kvmem_status kvmem_attention_mass(const kvmem_geom *geom, const kvmem_workspace 
     for (int i = 0; i < n; ++i) nt.v[i] = ws->n_tokens_host[s0 + i];
     st = hip_status(launch_mass(q, q_norm_w, eps, ws->k_pool, ws->block_table, view_blocks, (float4 *)scratch, mass,
                                 lse_opt, ws->dev_error, nt, s0, n, g, (double)rope_theta, (hipStream_t)stream));
+    if (st != KVMEM_OK) return st;
+  }
+  return KVMEM_OK;
+}
+
+kvmem_status kvmem_stage_view(const kvmem_geom *geom, const kvmem_workspace *ws, const int32_t *view_blocks,
+                              int32_t n_list, const int32_t *view_tokens_host, void *stage_k, void *stage_v,
+                              int32_t *stage_table, int32_t *stage_list, void *stream) {
+  kvmem_status st = check_geom(geom);
+  if (st != KVMEM_OK) return st;
+  if ((st = check_ws(ws, true)) != KVMEM_OK) return st;
+  if (!view_tokens_host || !stage_k || !stage_v || !stage_table || !stage_list || n_list <= 0) return KVMEM_E_ARG;
+  bool any = false;
+  for (int s = 0; s < ws->n_sessions; ++s) {
+    const int V = view_tokens_host[s];
+    if (V < 0 || (long)V > (long)kBT * n_list) return KVMEM_E_ARG;
+    any = any || V > 0;
+  }
+  if (any && !view_blocks) return KVMEM_E_ARG;
+  // staged pages and list entries are indexed in 32 bits
+  if ((long)ws->n_sessions * n_list * geom->n_kv_heads >= (1L << 31)) return KVMEM_E_UNSUPPORTED;
+  // the kernel reads the pools in place: they must be device memory or host
+  // memory mapped for the GPU at the same address (pageable memory would fault)
+  if (!gpu_addressable(ws->k_pool) || !gpu_addressable(ws->v_pool)) return KVMEM_E_ARG;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  for (int s0 = 0; s0 < ws->n_sessions; s0 += kMaxSess) {
+    const int n = ws->n_sessions - s0 < kMaxSess ? ws->n_sessions - s0 : kMaxSess;
+    SessI32 vt, na;
+    memset(&vt, 0, sizeof(vt));
+    memset(&na, 0, sizeof(na));
+    for (int i = 0; i < n; ++i) {
+      vt.v[i] = view_tokens_host[s0 + i];
+      na.v[i] = (ws->n_tokens_host[s0 + i] + kBT - 1) / kBT;
+    }
+    st = hip_status(launch_stage(bf16, ws->k_pool, ws->v_pool, ws->block_table, view_blocks, stage_k, stage_v,
+                                 stage_table, stage_list, ws->dev_error, vt, na, s0, n, geom->n_kv_heads,
+                                 ws->max_blocks, ws->n_pages, n_list, (hipStream_t)stream));
     if (st != KVMEM_OK) return st;
   }
   return KVMEM_OK;

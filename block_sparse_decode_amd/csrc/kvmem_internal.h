@@ -121,6 +121,15 @@ hipError_t launch_materialize(int bf16, const void *k_pool, const void *v_pool, 
                               int Hkv, int max_blocks, int n_pages, int n_list, int max_view,
                               double theta, hipStream_t st);
 
+// --- host-tier staging ------------------------------------------------------------
+// The listed (block, KV head) tiles of every session's view, read from the
+// pools (pinned host memory or HBM) into staged page s * n_list + m, with the
+// staged block table and identity list (see k_stage.hip).
+hipError_t launch_stage(int bf16, const void *k_pool, const void *v_pool, const int32_t *table,
+                        const int32_t *view_blocks, void *stage_k, void *stage_v, int32_t *stage_table,
+                        int32_t *stage_list, int32_t *dev_err, const SessI32 &view_tok, const SessI32 &n_all,
+                        int s0, int n_sess, int Hkv, int max_blocks, int n_pages, int n_list, hipStream_t st);
+
 // --- append ---------------------------------------------------------------------
 // Writes T_new new tokens per session into the pools at history positions
 // n_tok + t and into the view at positions view_tok + t (K re-RoPE'd there).

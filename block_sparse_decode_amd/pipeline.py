@@ -53,7 +53,7 @@ class DeviceWorkspace:
     """Inputs of a workload on the GPU plus every buffer the four calls use."""
 
     def __init__(self, wl, device="cuda", k_select=None, n_recent=None, max_view=None, with_v=True,
-                 device_pools=None):
+                 device_pools=None, host_pools=False):
         cfg = wl.cfg
         self.cfg = cfg
         self.device = torch.device(device)
@@ -66,6 +66,9 @@ class DeviceWorkspace:
         self.S, self.H, self.d = S, H, d
         if device_pools is not None:           # pools the caller has already put on the device
             self.k_pool, self.v_pool = device_pools
+        elif host_pools:                        # the host tier: pinned host memory the GPU reads in place
+            self.k_pool = to_device(wl.k_pool, cfg.dtype, "cpu").pin_memory()
+            self.v_pool = to_device(wl.v_pool, cfg.dtype, "cpu").pin_memory() if with_v else None
         elif wl.k_pool is not None:
             self.k_pool = to_device(wl.k_pool, cfg.dtype, self.device)
             self.v_pool = to_device(wl.v_pool, cfg.dtype, self.device) if with_v else None
@@ -178,6 +181,23 @@ class DeviceWorkspace:
                                    self.v_view, self.out if out is None else out, scratch=self.paged_scratch,
                                    stream=stream)
 
+    # --- host-tier paging ----------------------------------------------------
+    def stage(self, staged: "StagedView", stream=None):
+        """Copy the current lists' blocks from this workspace's pools (pinned
+        host memory for the host tier) into the staging pool."""
+        L.kvmem_stage_view(self.geom, self.ws, self.view_blocks, self.n_list, self.view_tokens, staged.k, staged.v,
+                           staged.table, staged.list, stream)
+
+    def materialize_attend_staged(self, staged: "StagedView", out=None, stream=None):
+        """kvmem_materialize_attend over the staged pool (its identity list)."""
+        if not hasattr(self, "paged_scratch"):
+            nbytes = L.kvmem_attend_paged_scratch_bytes(self.geom, self.S, self.T, max(1, self.n_list))
+            self.paged_scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        L.kvmem_materialize_attend(self.geom, staged.ws, self.q, self.T, self.q_norm_w, self.eps, staged.list,
+                                   self.n_list, self.view_tokens, self.max_view, self.theta, self.k_view,
+                                   self.v_view, self.out if out is None else out, scratch=self.paged_scratch,
+                                   stream=stream)
+
     # --- selection-quality diagnostic ---------------------------------------
     def attention_mass(self, mass, lse=None, view_blocks=None, n_list=None, stream=None):
         """Share of full attention over the history that the listed blocks
@@ -195,3 +215,19 @@ class DeviceWorkspace:
         self.score_select(stream)
         self.materialize(stream)
         self.attend(stream)
+
+
+class StagedView:
+    """Device staging pool of a workspace's views (kvmem_stage_view): page
+    s * n_list + m holds every KV head's m-th listed block; with its block
+    table and identity list it is a workspace whose history is the view."""
+
+    def __init__(self, dw: DeviceWorkspace):
+        S, H, d, n = dw.S, dw.H, dw.d, max(1, dw.n_list)
+        self.k = torch.empty((S * n, H, BLOCK, d), dtype=dw.tdtype, device=dw.device)
+        self.v = torch.empty((S * n, H, BLOCK, d), dtype=dw.tdtype, device=dw.device)
+        self.table = torch.empty((S, n), dtype=torch.int32, device=dw.device)
+        self.list = torch.empty((S, H, n), dtype=torch.int32, device=dw.device)
+        # the staged history lengths are the view lengths (the array the
+        # selection writes in place)
+        self.ws = L.make_workspace(self.k, self.v, self.table, dw.view_tokens, dw.dev_error)

@@ -25,6 +25,11 @@
  *   kvmem_update_index   Mean-K rows of the blocks completed since the last
  *                        index build.
  *
+ * and, for workspaces whose pages live in pinned host memory:
+ *
+ *   kvmem_stage_view     the listed blocks of every view, copied over the
+ *                        host link into a device staging pool in view order.
+ *
  * and a selection-quality diagnostic:
  *
  *   kvmem_attention_mass share of full attention over the whole history that
@@ -239,6 +244,45 @@ kvmem_status kvmem_materialize(const kvmem_geom *geom, const kvmem_workspace *ws
                                const int32_t *view_blocks, int32_t n_list,
                                const int32_t *view_tokens_host, int32_t max_view,
                                float rope_theta, void *k_view, void *v_view, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-tier paging ([README 'Background and main changes']: the history is
+ * kept as paged KV across GPU memory, host memory and NVMe, and the selected
+ * blocks are brought into the bounded view on demand; [REVIEW 'Summary']).
+ *
+ * The workspace's K/V pools may be pinned host memory (hipHostMalloc, e.g.
+ * torch's pinned allocator: the GPU reads it in place over the host link;
+ * memory merely registered with hipHostRegister is not supported) or device
+ * memory; the Mean-K index, built by kvmem_build_index from either, stays in
+ * device memory, so kvmem_score_select never touches the host tier.  After a
+ * selection, this call copies exactly the listed (block, KV head) tiles of
+ * every session's view into a device staging pool laid out in view order:
+ *   stage page s * n_list + m, KV head h  <-  K and V of head h's m-th listed
+ *                                             block, view_blocks[s][h][m]
+ * and writes the staged workspace's block table and list:
+ *   stage_table[s][m]   = s * n_list + m   for m < ceil(V/32), else -1
+ *   stage_list[s][h][m] = m                for m < ceil(V/32), else -1
+ * A workspace { stage_k, stage_v, stage_table, view_tokens_host (as history
+ * lengths), n_sessions, n_list (as max_blocks), n_sessions * n_list pages }
+ * with stage_list as its view list then gives kvmem_materialize,
+ * kvmem_materialize_attend and kvmem_attend_paged exactly the view and the
+ * attention the original workspace gives with view_blocks (a view position
+ * depends only on the list slot).  Tokens past V in the last block are not
+ * read and are zero in the staged pool; a bad list entry or page sets the
+ * KVMEM_DEVERR_* bit and is staged as a zero tile, as the gather writes it.
+ * KVMEM_E_ARG (checked last, with HIP's pointer query) if a pool is not
+ * readable by the GPU at its own address (e.g. pageable host memory).
+ *
+ * view_blocks, n_list, view_tokens_host : as for kvmem_materialize.
+ * stage_k, stage_v : device, [n_sessions * n_list][Hkv][32][d] in kv_dtype.
+ * stage_table      : device int32 [n_sessions][n_list].
+ * stage_list       : device int32 [n_sessions][Hkv][n_list].
+ * ------------------------------------------------------------------------- */
+kvmem_status kvmem_stage_view(const kvmem_geom *geom, const kvmem_workspace *ws,
+                              const int32_t *view_blocks, int32_t n_list,
+                              const int32_t *view_tokens_host,
+                              void *stage_k, void *stage_v, int32_t *stage_table,
+                              int32_t *stage_list, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Decode attention over the view ([README 'Local reproduction']: attention

@@ -296,3 +296,25 @@ def test_attend_noalloc_rejects(lib):
     big = np.full(S, mv, np.int32)
     assert call(n_sessions=S, view_tokens_host=big, max_view=mv) == L.KVMEM_E_WORKSPACE
     assert L.kvmem_attend_scratch_bytes(g, 1, 1, mv) <= L.NOALLOC_SCRATCH_BYTES
+
+
+def test_stage_view_rejects(lib):
+    ws, n = _ws()
+    g = _geom()
+    vt = np.array([64, 96], np.int32)
+    call = lambda **kw: L.kvmem_stage_view(**{**dict(geom=g, ws=ws, view_blocks=0x10, n_list=4,
+                                                    view_tokens_host=vt, stage_k=0x20, stage_v=0x30,
+                                                    stage_table=0x40, stage_list=0x50, check=False), **kw})
+    assert call(stage_k=None) == L.KVMEM_E_ARG
+    assert call(stage_v=None) == L.KVMEM_E_ARG
+    assert call(stage_table=None) == L.KVMEM_E_ARG
+    assert call(stage_list=None) == L.KVMEM_E_ARG
+    assert call(n_list=0) == L.KVMEM_E_ARG
+    assert call(n_list=2) == L.KVMEM_E_ARG                 # a view longer than the list allows
+    assert call(view_blocks=None) == L.KVMEM_E_ARG
+    assert call(view_tokens_host=np.array([-1, 0], np.int32)) == L.KVMEM_E_ARG
+    assert call(geom=_geom(d=64)) == L.KVMEM_E_UNSUPPORTED
+    ws_nov = L.Workspace(0x1000, None, 0x3000, n.ctypes.data, 2, 64, 70, None)
+    assert call(ws=ws_nov) == L.KVMEM_E_ARG                # V pool needed
+    ws2, n2 = _ws(n_tok=(100, 64 * 32 + 1))                  # longer than the table
+    assert call(ws=ws2) == L.KVMEM_E_ARG
