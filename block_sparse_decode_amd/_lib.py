@@ -68,7 +68,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("KVMEM_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with `python -m block_sparse_decode_amd.build`")
     # PyTorch wheels bring their own HIP runtime.  Loading it first makes the

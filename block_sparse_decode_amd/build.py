@@ -1,9 +1,16 @@
 """Build the HIP library libkvmem.so in-tree for gfx950.
 
-    python -m block_sparse_decode_amd.build
+    python -m block_sparse_decode_amd.build              # libkvmem.so next to this file
+    python -m block_sparse_decode_amd.build --sanitize   # _build/sanitize/libkvmem.so
 
-compiles every kernel source under csrc/ with hipcc into one shared library
-next to this file.  Sources are compiled in parallel, then linked.
+compiles every kernel source under csrc/ with hipcc into one shared library.
+Sources are compiled in parallel, then linked.  --sanitize builds the host
+code with AddressSanitizer and UndefinedBehaviorSanitizer (the device code is
+built as usual; sanitizers apply to the host side only), for running the
+CPU-only ABI tests against the argument checking and scratch layout code:
+
+    ASAN_OPTIONS=detect_leaks=0 LD_PRELOAD=<clang's libclang_rt.asan-x86_64.so> \
+        KVMEM_LIB=_build/sanitize/libkvmem.so python -m pytest tests/test_abi_cpu.py
 """
 from __future__ import annotations
 
@@ -39,9 +46,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime (to LD_PRELOAD)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    p = r.stdout.strip()
+    if not os.path.isabs(p) or not os.path.exists(p):
+        import glob
+        found = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        p = found[-1] if found else ""
+    return p
+
+
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+    cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -51,20 +73,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    out_dir = os.path.join(BUILD, "sanitize") if sanitize else BUILD
+    lib = os.path.join(out_dir, "libkvmem.so") if sanitize else LIB
+    extra = SANITIZE if sanitize else ()
+    os.makedirs(out_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda src: _compile(src, out_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-shared-libsan"] if sanitize else []
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])
