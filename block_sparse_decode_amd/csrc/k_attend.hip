@@ -631,6 +631,113 @@ __global__ __launch_bounds__(512) void k_mass_bf16(const uint16_t *__restrict__ 
 
 // One wavefront per (session, KV head, query row): folds the chunks' partials
 // (lane c takes chunks c, c + 64, ...; then a fixed butterfly order).
+// fp32 workspaces: a vector-ALU kernel with the same chunks and partials.  One
+// 256-thread workgroup per (session, chunk of history blocks, KV head); each
+// history key is rotated at its own position in fp32 (the angle reduced in
+// fp64, its sine and cosine in fp32, as the query angles), which is the fp32
+// storage rounding, and the logits are the view attention's fp32 dot products.
+__global__ __launch_bounds__(256) void k_mass_f32(const float *__restrict__ q, const float *__restrict__ qw,
+                                                  float eps, const float *__restrict__ kpool,
+                                                  const int32_t *__restrict__ table,
+                                                  const int32_t *__restrict__ vblocks, float4 *__restrict__ part,
+                                                  int32_t *dev_err, SessI32 n_tok, int s0, MassGeom g,
+                                                  double theta) {
+  __shared__ double inv_freq[kD / 2];
+  __shared__ float qs[kF32MaxRows][kD + 1];
+  __shared__ float ks[kBT][kD + 1];
+  __shared__ float lg[kF32MaxRows][kBT + 1];
+  __shared__ float srs[kF32MaxRows];
+  __shared__ uint8_t listed[kMassMaxChunk];
+  __shared__ int s_page;
+
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N = n_tok.v[sl];
+  const int n_all = (N + kBT - 1) / kBT;
+  const int b0 = chunk * g.chunk;
+  if (b0 >= n_all) return;                             // uniform over the workgroup
+  const int b1 = min(n_all, b0 + g.chunk);
+  const int R = g.rows;
+  if (tid < kD / 2) inv_freq[tid] = rope_inv_freq(tid, theta);
+  if (tid < R) {
+    const int t = tid / g.G, gg = tid % g.G;
+    const float *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
+    float ss = 0.f;
+    for (int e = 0; e < kD; ++e) ss += src[e] * src[e];
+    srs[tid] = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  }
+  for (int i = tid; i < kMassMaxChunk; i += 256) listed[i] = 0;
+  __syncthreads();
+  {
+    const int32_t *lst = vblocks + ((size_t)s * g.Hkv + h) * g.n_list;
+    for (int idx = tid; idx < g.n_list; idx += 256) {
+      const int v = lst[idx];
+      if (v >= b0 && v < b1) listed[v - b0] = 1;
+    }
+  }
+  for (int idx = tid; idx < R * kD; idx += 256) {       // q~ rotated at N + t, in log2 units
+    const int r = idx >> 7, dim = idx & (kD - 1);
+    const int t = r / g.G, gg = r % g.G;
+    const float *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
+    const int i = dim & 63;
+    const int pd = dim < 64 ? dim + 64 : dim - 64;
+    const float x = src[dim] * srs[r] * qw[dim];
+    const float px = src[pd] * srs[r] * qw[pd];
+    float c, sn;
+    rope_cos_sin((double)(N + t), inv_freq[i], c, sn);
+    qs[r][dim] = (dim < 64 ? x * c - px * sn : x * c + px * sn) * kLog2eRsqrtD;
+  }
+  float m_all = -INFINITY, l_all = 0.f, m_sel = -INFINITY, l_sel = 0.f;   // row tid's statistics
+  for (int beta = b0; beta < b1; ++beta) {
+    if (tid == 0) {
+      const int page = table[(size_t)s * g.max_blocks + beta];
+      const bool ok = page >= 0 && page < g.n_pages;
+      if (!ok) dev_flag(dev_err, 1);
+      s_page = ok ? page : -1;
+    }
+    __syncthreads();
+    const int page = s_page;
+    if (page < 0) continue;                            // uniform: a bad page is skipped
+    const size_t src = ((size_t)page * g.Hkv + h) * (size_t)(kBT * kD);
+    for (int idx = tid; idx < kBT * (kD / 2); idx += 256) {
+      const int u = idx / (kD / 2), i = idx % (kD / 2);
+      const int pos = kBT * beta + u;
+      const bool have = pos < N;
+      const float x1 = have ? kpool[src + (size_t)u * kD + i] : 0.f;
+      const float x2 = have ? kpool[src + (size_t)u * kD + 64 + i] : 0.f;
+      float c, sn, y1, y2;
+      rope_cos_sin((double)pos, inv_freq[i], c, sn);
+      rope_rotate(x1, x2, c, sn, y1, y2);
+      ks[u][i] = y1;
+      ks[u][64 + i] = y2;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < R * kBT; idx += 256) {
+      const int r = idx / kBT, u = idx % kBT;
+      float a = -INFINITY;
+      if (kBT * beta + u < N) {
+        a = 0.f;
+        for (int e = 0; e < kD; ++e) a = fmaf(qs[r][e], ks[u][e], a);
+      }
+      lg[r][u] = a;
+    }
+    __syncthreads();
+    if (tid < R) {
+      float bm = -INFINITY;
+      for (int j = 0; j < kBT; ++j) bm = fmaxf(bm, lg[tid][j]);
+      float bl = 0.f;
+      for (int j = 0; j < kBT; ++j) bl += exp2f(lg[tid][j] - bm);
+      mass_fold(m_all, l_all, bm, bl);
+      if (listed[beta - b0]) mass_fold(m_sel, l_sel, bm, bl);
+    }
+    __syncthreads();
+  }
+  if (tid < R) part[(((size_t)s * g.Hkv + h) * g.n_chunks + chunk) * g.rows + tid] = make_float4(m_all, l_all, m_sel, l_sel);
+}
+
 __global__ __launch_bounds__(64) void k_mass_combine(const float4 *__restrict__ part, float *__restrict__ mass,
                                                      float *__restrict__ lse, SessI32 n_tok, int s0, MassGeom g) {
   const int sl = blockIdx.z;
@@ -881,7 +988,7 @@ hipError_t launch_attend_combine(const float *part_o, const float2 *part_ml, flo
 
 namespace kvmem {
 
-hipError_t launch_mass(const void *q, const float *qw, float eps, const void *k_pool, const int32_t *table,
+hipError_t launch_mass(int bf16, const void *q, const float *qw, float eps, const void *k_pool, const int32_t *table,
                        const int32_t *view_blocks, float4 *part, float *mass, float *lse, int32_t *dev_err,
                        const SessI32 &n_tok, int s0, int n_sess, const MassGeom &g, double theta, hipStream_t st) {
   int max_all = 0;
@@ -890,7 +997,13 @@ hipError_t launch_mass(const void *q, const float *qw, float eps, const void *k_
     max_all = n > max_all ? n : max_all;
   }
   const int groups = (g.Hkv + kMassWaves - 1) / kMassWaves;
-  if (max_all > 0) {
+  if (max_all > 0 && !bf16) {
+    const dim3 grid((unsigned)((max_all + g.chunk - 1) / g.chunk), (unsigned)g.Hkv, (unsigned)n_sess);
+    hipLaunchKernelGGL(k_mass_f32, grid, dim3(256), 0, st, (const float *)q, qw, eps, (const float *)k_pool, table,
+                       view_blocks, part, dev_err, n_tok, s0, g, theta);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (max_all > 0) {
     dim3 grid((unsigned)((max_all + g.chunk - 1) / g.chunk), (unsigned)groups, (unsigned)n_sess);
     if (g.rows <= 16)
       hipLaunchKernelGGL(k_mass_bf16<1>, grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,

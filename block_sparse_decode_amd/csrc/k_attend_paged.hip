@@ -27,7 +27,8 @@
 //     tokens of one dimension: the wavefront stages its V tile in its own LDS
 //     tile and reads the operand from there.
 // Split partials have the view attention's layout and are merged by
-// k_attend_combine.
+// k_attend_combine.  fp32 workspaces take a vector-ALU kernel
+// (k_attend_paged_f32, below) with the same splits and partials.
 //
 // With WV (kvmem_materialize_attend) the kernel also writes the view, which
 // makes it the gather and the attention in one pass: a lane's rotated K
@@ -347,6 +348,170 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   }
 }
 
+// fp32 workspaces: a vector-ALU kernel with the same split structure and
+// partial layout.  One 256-thread workgroup per (session, split of the list,
+// KV head).  Per listed block the workgroup rotates the block's keys at their
+// view positions with the gather's angle composition and rotation (so the
+// keys are the view's, bit for bit), stages K and V in LDS, and runs the fp32
+// logits, online softmax and weighted sum of the view attention over them.
+// With WV it also writes the view exactly as the gather does (K rotated,
+// token-major; V copied into its slot; zeros past V in the last block).
+constexpr int kPgF32MaxRows = 64;
+
+template <bool WV>
+__global__ __launch_bounds__(256) void k_attend_paged_f32(
+    const float *__restrict__ q, const float *__restrict__ qw, float eps, const float *__restrict__ kpool,
+    const float *__restrict__ vpool, const int32_t *__restrict__ table, const int32_t *__restrict__ vblocks,
+    float *__restrict__ part_o, float2 *__restrict__ part_ml, float *__restrict__ out, int32_t *dev_err,
+    SessI32 view_tok, SessI32 n_all, int s0, PagedGeom g, double theta, float *__restrict__ kview,
+    float *__restrict__ vview, int max_view) {
+  __shared__ double inv_freq[kD / 2];
+  __shared__ double2 base_cs[kD / 2];                  // block angles 32 m * theta_i
+  __shared__ float2 offs[kBT][kD / 2];                 // in-block angles u * theta_i
+  __shared__ float qs[kPgF32MaxRows][kD + 1];
+  __shared__ float ks[kBT][kD + 1];
+  __shared__ float vs[kBT][kD];
+  __shared__ float lg[kPgF32MaxRows][kBT + 1];
+  __shared__ float srs[kPgF32MaxRows], smx[kPgF32MaxRows], slsum[kPgF32MaxRows], salpha[kPgF32MaxRows];
+  __shared__ int s_page;
+
+  const int sl = blockIdx.z;
+  const int s = s0 + sl;
+  const int h = blockIdx.y;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int V = view_tok.v[sl];
+  const int m0 = split * g.bps;
+  if (kBT * m0 >= V) return;
+  const int m1 = min((V + kBT - 1) / kBT, m0 + g.bps);
+  const int n_splits = (V + kBT * g.bps - 1) / (kBT * g.bps);
+  const int R = g.rows;
+  if (tid < kD / 2) inv_freq[tid] = rope_inv_freq(tid, theta);
+  if (tid < R) {
+    const int t = tid / g.G, gg = tid % g.G;
+    const float *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
+    float ss = 0.f;
+    for (int e = 0; e < kD; ++e) ss += src[e] * src[e];
+    srs[tid] = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+    smx[tid] = -INFINITY;
+    slsum[tid] = 0.f;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kBT * (kD / 2); idx += 256) {
+    float cb, sb;
+    rope_offset_pair(idx / (kD / 2), inv_freq[idx % (kD / 2)], cb, sb);
+    offs[idx / (kD / 2)][idx % (kD / 2)] = make_float2(cb, sb);
+  }
+  for (int idx = tid; idx < R * kD; idx += 256) {       // q~ rotated at V + t, in log2 units
+    const int r = idx >> 7, dim = idx & (kD - 1);
+    const int t = r / g.G, gg = r % g.G;
+    const float *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD;
+    const int i = dim & 63;
+    const int pd = dim < 64 ? dim + 64 : dim - 64;
+    const float x = src[dim] * srs[r] * qw[dim];
+    const float px = src[pd] * srs[r] * qw[pd];
+    float c, sn;
+    rope_cos_sin((double)(V + t), inv_freq[i], c, sn);
+    qs[r][dim] = (dim < 64 ? x * c - px * sn : x * c + px * sn) * kLog2eRsqrtD;
+  }
+
+  const int32_t *lst = vblocks + ((size_t)s * g.Hkv + h) * g.n_list;
+  const int dim = tid & (kD - 1);
+  const int rh = tid >> 7;                             // rows rh, rh + 2, ...
+  float acc[kPgF32MaxRows / 2];
+#pragma unroll
+  for (int k = 0; k < kPgF32MaxRows / 2; ++k) acc[k] = 0.f;
+
+  for (int m = m0; m < m1; ++m) {
+    const int tb = kBT * m;
+    if (tid < kD / 2) {
+      double c, sn;
+      rope_angle_f64((double)tb, inv_freq[tid], c, sn);
+      base_cs[tid] = make_double2(c, sn);
+    }
+    if (tid == 0) {                                    // a bad entry or page is a zero block
+      const int beta = lst[m];
+      const bool beta_ok = beta >= 0 && beta < n_all.v[sl];
+      const int page = beta_ok ? table[(size_t)s * g.max_blocks + beta] : -1;
+      const bool ok = beta_ok && page >= 0 && page < g.n_pages;
+      if (!ok) dev_flag(dev_err, beta_ok ? 1 : 2);
+      s_page = ok ? page : -1;
+    }
+    __syncthreads();
+    const int page = s_page;
+    const size_t src = ((size_t)(page >= 0 ? page : 0) * g.Hkv + h) * (size_t)(kBT * kD);
+    for (int idx = tid; idx < kBT * (kD / 2); idx += 256) {
+      const int u = idx / (kD / 2), i = idx % (kD / 2);
+      const bool have = page >= 0 && tb + u < V;
+      const float x1 = have ? kpool[src + (size_t)u * kD + i] : 0.f;
+      const float x2 = have ? kpool[src + (size_t)u * kD + 64 + i] : 0.f;
+      float c, sn, y1, y2;
+      rope_compose(base_cs[i].x, base_cs[i].y, offs[u][i].x, offs[u][i].y, c, sn);
+      rope_rotate(x1, x2, c, sn, y1, y2);
+      ks[u][i] = y1;
+      ks[u][64 + i] = y2;
+      if (WV) {
+        float *row = kview + (((size_t)s * g.Hkv + h) * max_view + tb + u) * kD;
+        row[i] = y1;
+        row[64 + i] = y2;
+      }
+    }
+    for (int idx = tid; idx < kBT * kD; idx += 256) {
+      const int u = idx >> 7, d = idx & (kD - 1);
+      const float v = page >= 0 && tb + u < V ? vpool[src + idx] : 0.f;
+      vs[u][d] = v;
+      if (WV) vview[((((size_t)s * g.Hkv + h) * (max_view / kBT) + m) * kD + d) * kBT + v_slot(u)] = v;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < R * kBT; idx += 256) {
+      const int r = idx / kBT, u = idx % kBT;
+      float a = -INFINITY;
+      if (tb + u < V) {
+        a = 0.f;
+        for (int e = 0; e < kD; ++e) a = fmaf(qs[r][e], ks[u][e], a);
+      }
+      lg[r][u] = a;
+    }
+    __syncthreads();
+    if (tid < R) {
+      float bm = -INFINITY;
+      for (int j = 0; j < kBT; ++j) bm = fmaxf(bm, lg[tid][j]);
+      const float mn = fmaxf(smx[tid], bm);
+      const float alpha = exp2f(smx[tid] - mn);
+      float ps = 0.f;
+      for (int j = 0; j < kBT; ++j) {
+        const float p = exp2f(lg[tid][j] - mn);
+        lg[tid][j] = p;
+        ps += p;
+      }
+      slsum[tid] = slsum[tid] * alpha + ps;
+      smx[tid] = mn;
+      salpha[tid] = alpha;
+    }
+    __syncthreads();
+    for (int k = 0; k < kPgF32MaxRows / 2; ++k) {
+      const int r = rh + 2 * k;
+      if (r >= R) break;
+      float a = acc[k] * salpha[r];
+      for (int j = 0; j < kBT; ++j) a = fmaf(lg[r][j], vs[j][dim], a);
+      acc[k] = a;
+    }
+    __syncthreads();
+  }
+  for (int k = 0; k < kPgF32MaxRows / 2; ++k) {
+    const int r = rh + 2 * k;
+    if (r >= R) break;
+    if (n_splits == 1) {
+      const int t = r / g.G, gg = r % g.G;
+      out[(((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + dim] = acc[k] / slsum[r];
+    } else {
+      const size_t pidx = (((size_t)s * g.Hkv + h) * g.max_splits + split) * g.rows + r;
+      part_o[pidx * kD + dim] = acc[k];
+      if (dim == 0) part_ml[pidx] = make_float2(smx[r], slsum[r]);
+    }
+  }
+}
+
 }  // namespace
 
 int paged_blocks_per_split(int n_sessions, int Hkv, int n_list) {
@@ -358,15 +523,27 @@ int paged_blocks_per_split(int n_sessions, int Hkv, int n_list) {
   return (int)b;
 }
 
-hipError_t launch_attend_paged(const void *q, const float *qw, float eps, const void *k_pool, const void *v_pool,
-                               const int32_t *table, const int32_t *view_blocks, float *part_o, float2 *part_ml,
-                               float *out, int32_t *dev_err, const SessI32 &view_tok, const SessI32 &n_all, int s0,
-                               int n_sess, const PagedGeom &g, double theta, void *k_view, void *v_view, int max_view,
-                               hipStream_t st) {
+hipError_t launch_attend_paged(int bf16, const void *q, const float *qw, float eps, const void *k_pool,
+                               const void *v_pool, const int32_t *table, const int32_t *view_blocks, float *part_o,
+                               float2 *part_ml, float *out, int32_t *dev_err, const SessI32 &view_tok,
+                               const SessI32 &n_all, int s0, int n_sess, const PagedGeom &g, double theta,
+                               void *k_view, void *v_view, int max_view, hipStream_t st) {
   int max_v = 0;
   for (int i = 0; i < n_sess; ++i) max_v = view_tok.v[i] > max_v ? view_tok.v[i] : max_v;
   const int splits = (max_v + kBT * g.bps - 1) / (kBT * g.bps);
-  if (splits > 0) {
+  if (splits > 0 && !bf16) {
+    const dim3 grid((unsigned)splits, (unsigned)g.Hkv, (unsigned)n_sess);
+    if (k_view != nullptr)
+      hipLaunchKernelGGL(k_attend_paged_f32<true>, grid, dim3(256), 0, st, (const float *)q, qw, eps,
+                         (const float *)k_pool, (const float *)v_pool, table, view_blocks, part_o, part_ml, out,
+                         dev_err, view_tok, n_all, s0, g, theta, (float *)k_view, (float *)v_view, max_view);
+    else
+      hipLaunchKernelGGL(k_attend_paged_f32<false>, grid, dim3(256), 0, st, (const float *)q, qw, eps,
+                         (const float *)k_pool, (const float *)v_pool, table, view_blocks, part_o, part_ml, out,
+                         dev_err, view_tok, n_all, s0, g, theta, nullptr, nullptr, max_view);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (splits > 0) {
     dim3 grid((unsigned)splits, (unsigned)((g.Hkv + kPgWaves - 1) / kPgWaves), (unsigned)n_sess);
 #define KVMEM_PAGED(NT, WV)                                                                                     \
   hipLaunchKernelGGL((k_attend_paged_bf16<NT, WV>), grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,          \

@@ -379,7 +379,8 @@ static kvmem_status paged_attend(const kvmem_geom *geom, const kvmem_workspace *
   const bool wv = k_view != nullptr || v_view != nullptr;
   if (wv && (!k_view || !v_view || max_view <= 0 || max_view % kBT != 0)) return KVMEM_E_ARG;
   const int G = geom->n_q_heads / geom->n_kv_heads;
-  if (geom->kv_dtype != KVMEM_BF16 || (long)T * G > kMfmaMaxRows) return KVMEM_E_UNSUPPORTED;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  if ((long)T * G > (bf16 ? kMfmaMaxRows : kF32PagedMaxRows)) return KVMEM_E_UNSUPPORTED;
   const int S = ws->n_sessions;
   for (int s = 0; s < S; ++s) {
     const int V = view_tokens_host[s];
@@ -409,7 +410,7 @@ static kvmem_status paged_attend(const kvmem_geom *geom, const kvmem_workspace *
       vt.v[i] = view_tokens_host[s0 + i];
       na.v[i] = (ws->n_tokens_host[s0 + i] + kBT - 1) / kBT;
     }
-    st = hip_status(launch_attend_paged(q, q_norm_w, eps, ws->k_pool, ws->v_pool, ws->block_table, view_blocks,
+    st = hip_status(launch_attend_paged(bf16, q, q_norm_w, eps, ws->k_pool, ws->v_pool, ws->block_table, view_blocks,
                                         (float *)(base + sc.part_o), (float2 *)(base + sc.part_ml), out,
                                         ws->dev_error, vt, na, s0, n, g, (double)rope_theta, wv ? k_view : nullptr,
                                         wv ? v_view : nullptr, wv ? max_view : 0, (hipStream_t)stream));
@@ -454,7 +455,8 @@ kvmem_status kvmem_attention_mass(const kvmem_geom *geom, const kvmem_workspace 
   if (!q || !q_norm_w || !mass || T <= 0 || n_list < 0 || (n_list > 0 && !view_blocks)) return KVMEM_E_ARG;
   if (!(eps >= 0.f) || !isfinite(eps) || !(rope_theta > 1.0f) || !isfinite(rope_theta)) return KVMEM_E_ARG;
   const int G = geom->n_q_heads / geom->n_kv_heads;
-  if (geom->kv_dtype != KVMEM_BF16 || (long)T * G > kMfmaMaxRows) return KVMEM_E_UNSUPPORTED;
+  const int bf16 = geom->kv_dtype == KVMEM_BF16;
+  if ((long)T * G > (bf16 ? kMfmaMaxRows : kF32PagedMaxRows)) return KVMEM_E_UNSUPPORTED;
   const int S = ws->n_sessions;
   if ((long)S * geom->n_kv_heads * n_list >= (1L << 31)) return KVMEM_E_UNSUPPORTED;
   const size_t need = kvmem_attention_mass_scratch_bytes(geom, S, T, ws->max_blocks);
@@ -475,7 +477,7 @@ kvmem_status kvmem_attention_mass(const kvmem_geom *geom, const kvmem_workspace 
     SessI32 nt;
     memset(&nt, 0, sizeof(nt));
     for (int i = 0; i < n; ++i) nt.v[i] = ws->n_tokens_host[s0 + i];
-    st = hip_status(launch_mass(q, q_norm_w, eps, ws->k_pool, ws->block_table, view_blocks, (float4 *)scratch, mass,
+    st = hip_status(launch_mass(bf16, q, q_norm_w, eps, ws->k_pool, ws->block_table, view_blocks, (float4 *)scratch, mass,
                                 lse_opt, ws->dev_error, nt, s0, n, g, (double)rope_theta, (hipStream_t)stream));
     if (st != KVMEM_OK) return st;
   }

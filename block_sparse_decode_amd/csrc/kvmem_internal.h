@@ -155,17 +155,20 @@ hipError_t launch_attend_combine(const float *part_o, const float2 *part_ml, flo
                                  int s0, int n_sess, const AttendGeom &g, hipStream_t st);
 
 // --- attention straight from the pages ------------------------------------------
+// query rows per KV head of the fp32 kernels (attention from the pages, the
+// one-pass call and the diagnostic on fp32 workspaces)
+constexpr int kF32PagedMaxRows = 64;
 struct PagedGeom {
   int Tq, Hq, Hkv, G, rows, max_blocks, n_pages, n_list;
   int bps;          // list blocks per split
   int max_splits;   // split slots per (session, head) in the partials
 };
 int paged_blocks_per_split(int n_sessions, int Hkv, int n_list);
-hipError_t launch_attend_paged(const void *q, const float *qw, float eps, const void *k_pool, const void *v_pool,
-                               const int32_t *table, const int32_t *view_blocks, float *part_o, float2 *part_ml,
-                               float *out, int32_t *dev_err, const SessI32 &view_tok, const SessI32 &n_all, int s0,
-                               int n_sess, const PagedGeom &g, double theta, void *k_view, void *v_view, int max_view,
-                               hipStream_t st);
+hipError_t launch_attend_paged(int bf16, const void *q, const float *qw, float eps, const void *k_pool,
+                               const void *v_pool, const int32_t *table, const int32_t *view_blocks, float *part_o,
+                               float2 *part_ml, float *out, int32_t *dev_err, const SessI32 &view_tok,
+                               const SessI32 &n_all, int s0, int n_sess, const PagedGeom &g, double theta,
+                               void *k_view, void *v_view, int max_view, hipStream_t st);
 
 // --- selection-quality diagnostic ------------------------------------------------
 struct MassGeom {
@@ -174,7 +177,7 @@ struct MassGeom {
   int n_chunks;   // chunk slots per (session, head) in the partials
 };
 int mass_chunk(int n_sessions, int Hkv, int max_blocks);
-hipError_t launch_mass(const void *q, const float *qw, float eps, const void *k_pool, const int32_t *table,
+hipError_t launch_mass(int bf16, const void *q, const float *qw, float eps, const void *k_pool, const int32_t *table,
                        const int32_t *view_blocks, float4 *part, float *mass, float *lse, int32_t *dev_err,
                        const SessI32 &n_tok, int s0, int n_sess, const MassGeom &g, double theta, hipStream_t st);
 

@@ -355,9 +355,9 @@ kvmem_status kvmem_attend_noalloc(const kvmem_geom *geom, int32_t n_sessions,
  *
  * view_blocks, n_list : as written by kvmem_score_select.
  * view_tokens_host    : HOST [n_sessions] view lengths V (<= 32 * n_list).
- * q, q_norm_w, eps, out, rope_theta : as for kvmem_attend (T * G <= 32).
+ * q, q_norm_w, eps, out, rope_theta : as for kvmem_attend (T * G <= 32 for
+ *                       bf16, <= 64 for fp32; KVMEM_E_UNSUPPORTED beyond).
  * scratch             : at least kvmem_attend_paged_scratch_bytes() bytes.
- * bf16 workspaces only (KVMEM_E_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------- */
 size_t kvmem_attend_paged_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T,
                                         int32_t n_list);
@@ -381,8 +381,7 @@ kvmem_status kvmem_attend_paged(const kvmem_geom *geom, const kvmem_workspace *w
  *
  * Arguments as for kvmem_attend_paged, plus max_view, k_view, v_view as for
  * kvmem_materialize (V <= max_view).  scratch: at least
- * kvmem_attend_paged_scratch_bytes() bytes.  bf16 workspaces only
- * (KVMEM_E_UNSUPPORTED otherwise).
+ * kvmem_attend_paged_scratch_bytes() bytes.
  * ------------------------------------------------------------------------- */
 kvmem_status kvmem_materialize_attend(const kvmem_geom *geom, const kvmem_workspace *ws,
                                       const void *q, int32_t T, const float *q_norm_w, float eps,
@@ -450,11 +449,11 @@ kvmem_status kvmem_append(const kvmem_geom *geom, const kvmem_workspace *ws,
  * empty history or list.  Pass the selection's list for the method's mass and
  * a list of the recent blocks only for the recent-only control.
  *
- * q, q_norm_w, eps : as for kvmem_score_select (T * G <= 32).
+ * q, q_norm_w, eps : as for kvmem_score_select (T * G <= 32 for bf16, <= 64
+ *                    for fp32; KVMEM_E_UNSUPPORTED beyond).
  * mass, lse_opt    : [n_sessions][T][Hq] fp32 (lse_opt may be NULL).
  * scratch          : at least kvmem_attention_mass_scratch_bytes() bytes.
- * Reads the K pool only (v_pool may be NULL).  bf16 workspaces only
- * (KVMEM_E_UNSUPPORTED otherwise).
+ * Reads the K pool only (v_pool may be NULL).
  * ------------------------------------------------------------------------- */
 size_t kvmem_attention_mass_scratch_bytes(const kvmem_geom *geom, int32_t n_sessions, int32_t T,
                                           int32_t max_blocks);

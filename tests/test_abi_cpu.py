@@ -174,7 +174,9 @@ def test_materialize_attend_rejects(lib):
     assert call(rope_theta=1.0) == L.KVMEM_E_ARG
     assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
     assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head
-    assert call(geom=_geom("f32")) == L.KVMEM_E_UNSUPPORTED  # bf16 workspaces only
+    assert call(geom=_geom("f32"), T=16) == L.KVMEM_E_UNSUPPORTED   # fp32: at most 64 rows
+    assert call(geom=_geom("f32"), T=8, scratch_bytes=L.kvmem_attend_paged_scratch_bytes(
+        _geom("f32"), 2, 8, 4) - 1) == L.KVMEM_E_WORKSPACE  # fp32 with 64 rows gets past the row check
 
 
 def test_update_index_rejects(lib):
@@ -261,7 +263,9 @@ def test_attention_mass_rejects(lib):
     assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
     assert call(scratch=None) == L.KVMEM_E_WORKSPACE
     assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head
-    assert call(geom=_geom("f32")) == L.KVMEM_E_UNSUPPORTED  # bf16 workspaces only
+    assert call(geom=_geom("f32"), T=16) == L.KVMEM_E_UNSUPPORTED   # fp32: at most 64 rows
+    assert call(geom=_geom("f32"), T=8, scratch_bytes=L.kvmem_attention_mass_scratch_bytes(
+        _geom("f32"), 2, 8, 64) - 1) == L.KVMEM_E_WORKSPACE # fp32 with 64 rows gets past the row check
     assert call(geom=_geom(d=64)) == L.KVMEM_E_UNSUPPORTED
     ws2, n2 = _ws(n_tok=(100, 64 * 32 + 1))                  # longer than the table
     assert call(ws=ws2) == L.KVMEM_E_ARG

@@ -27,6 +27,10 @@ CASES = {
                        k=40, R=4, n_planted=8, seed=102),
     "t4_g8_nine_heads": small_cfg("mass_t4", "bf16", S=1, Hq=72, Hkv=9, T=4, n_tokens=(32 * 130,),
                                   k=12, R=2, n_planted=3, seed=103),
+    # fp32 workspaces (the vector-ALU kernel)
+    "f32_t3_g4": small_cfg("mass_f32", "f32", S=2, Hq=8, Hkv=2, T=3, n_tokens=(32 * 200 + 9, 32 * 33),
+                           k=12, R=2, n_planted=4, seed=104),
+    "c1": CONFIGS["c1"],
 }
 
 
