@@ -50,8 +50,8 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
 # taken on (sha256 over block_sparse_decode_amd/csrc/*); otherwise reported null.
-COUNTER_SOURCES_SHA = "f059e361683f22ece74672e8b6f6093d231e4a6f7924a1a52509c71350746868"
-MEASURED_TRAFFIC = {"build_index": 2.216e9, "materialize_attend": 2.238e9, "materialize": 2.156e9,
+COUNTER_SOURCES_SHA = "9925d81152cbef242fa854b35033e88a27d4ba0e17f3a07444307b869884ae44"
+MEASURED_TRAFFIC = {"build_index_full": 2.216e9, "materialize_attend": 2.238e9, "materialize": 2.156e9,
                     "attend": 1.085e9, "score_select": 7.618e7}
 
 
