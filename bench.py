@@ -49,17 +49,19 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a plain 1 GiB device
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
-# taken on (sha256 over block_sparse_decode_amd/csrc/*); otherwise reported null.
+# taken on (sha256 over block_sparse_decode_amd/csrc/* and build.py); otherwise reported null.
 COUNTER_SOURCES_SHA = "9925d81152cbef242fa854b35033e88a27d4ba0e17f3a07444307b869884ae44"
 MEASURED_TRAFFIC = {"build_index_full": 2.216e9, "materialize_attend": 2.238e9, "materialize": 2.156e9,
                     "attend": 1.085e9, "score_select": 7.618e7}
 
 
 def kernel_sources_sha() -> str:
+    """sha256 over the kernel sources and the build script (its flags shape the code)."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "block_sparse_decode_amd", "csrc", "*"))):
+    for p in sorted(glob.glob(os.path.join(ROOT, "block_sparse_decode_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "block_sparse_decode_amd", "build.py")]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()

@@ -28,7 +28,7 @@ def logical_tokens(wl: Workload, pool: np.ndarray, s: int, h: int) -> np.ndarray
     n = int(wl.n_tokens[s])
     nb = -(-n // 32)
     pages = wl.block_table[s, :nb]
-    raw = pool[pages, h].reshape(nb * 32, -1)[:n]
+    raw = pool[pages, h].reshape(nb * 32, pool.shape[-1])[:n]
     if wl.cfg.dtype == "bf16":
         return (raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return raw.astype(np.float64)
