@@ -11,11 +11,11 @@
 // tile is rotated there in registers and rounded to bf16 exactly as the gather
 // would store it, and its V tile is used as stored.
 //
-// One workgroup of 8 wavefronts per (session, split of the list, group of 8
-// KV heads); wavefront w serves KV head 8 * group + w over the split's list
-// blocks.  Per block:
+// One workgroup of nw wavefronts per (session, split of the list, group of nw
+// KV heads; nw is the largest divisor of Hkv up to 8); wavefront w serves KV
+// head nw * group + w over the split's list blocks.  Per block:
 //   * the 32 x 64 RoPE (cos, sin) table of the block's view positions is
-//     shared by the 8 heads through LDS (double-buffered, one barrier per
+//     shared by the heads through LDS (double-buffered, one barrier per
 //     block).  Its angles are composed from the block's 64 base angles
 //     (evaluated by one wavefront the block before) and the 32 x 64 in-block
 //     offsets (a table formed once per workgroup), exactly as the gather
@@ -55,6 +55,8 @@ __device__ __noinline__ double2 block_angle(double pos, double inv_freq) {
   return make_double2(c, s);
 }
 
+__device__ __forceinline__ uint4 and_mask(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+
 // token of k-slot e (0..7) of lane group qq: the S^T accumulator order
 __device__ __forceinline__ int pg_token(int qq, int e) { return e < 4 ? 4 * qq + e : 16 + 4 * qq + (e - 4); }
 
@@ -82,8 +84,8 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   const int wave = tid >> 6;
   const int qq = lane >> 4;
   const int col = lane & 15;
-  const int h = blockIdx.y * kPgWaves + wave;
-  const bool head_ok = h < g.Hkv;
+  const int h = blockIdx.y * (int)(blockDim.x >> 6) + wave;   // every wavefront has a head (paged_waves)
+  const int nthr = (int)blockDim.x;
   const int V = view_tok.v[sl];
   const int m0 = split * g.bps;
   if (kBT * m0 >= V) return;                           // uniform over the workgroup
@@ -97,10 +99,10 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + col;
-    rvalid[nt] = head_ok && r < g.rows;
+    rvalid[nt] = r < g.rows;
     const int t = rvalid[nt] ? r / g.G : 0, gg = rvalid[nt] ? r % g.G : 0;
     trow[nt] = t;
-    const uint16_t *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)(head_ok ? h : 0) * g.G + gg) * kD + 8 * qq;
+    const uint16_t *src = q + (((size_t)s * g.Tq + t) * g.Hq + (size_t)h * g.G + gg) * kD + 8 * qq;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 w = *reinterpret_cast<const uint4 *>(src + 32 * c);
@@ -113,45 +115,59 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
     }
   }
 
-  // first tile of this wavefront's list run (a bad list entry or page gives a
-  // zero tile, as the gather writes zeros for it)
-  const int32_t *lst = vblocks + ((size_t)s * g.Hkv + (head_ok ? h : 0)) * g.n_list;
+  // The split's pages, resolved once (a split has at most 64 list blocks):
+  // lane l holds the page of list block m0 + l, or -1 for a bad list entry or
+  // page (flagged here; its tile is zeros, as the gather writes zeros for it).
+  // Each block then takes its page from a register with readlane instead of a
+  // list load and a table load that depend on each other: resolved per block,
+  // those two round trips, and a wait for every memory operation before them
+  // (the view stores included), stood before each tile's loads.
+  int my_page = -1;
+  if (m0 + lane < m1) {
+    const int beta = vblocks[((size_t)s * g.Hkv + h) * g.n_list + m0 + lane];
+    const bool beta_ok = beta >= 0 && beta < n_all.v[sl];
+    const int p = beta_ok ? table[(size_t)s * g.max_blocks + beta] : -1;
+    const bool okp = beta_ok && p >= 0 && p < g.n_pages;
+    if (!okp) dev_flag(dev_err, beta_ok ? 1 : 2);
+    my_page = okp ? p : -1;
+  }
   auto tile_base = [&](int m, bool &ok) -> size_t {
-    ok = false;
-    int page = 0;
-    if (head_ok) {
-      const int beta = lst[m];
-      const bool beta_ok = beta >= 0 && beta < n_all.v[sl];
-      const int p = beta_ok ? table[(size_t)s * g.max_blocks + beta] : -1;
-      ok = beta_ok && p >= 0 && p < g.n_pages;
-      if (!ok && lane == 0) dev_flag(dev_err, beta_ok ? 1 : 2);
-      page = ok ? p : 0;
-    }
-    return ((size_t)page * g.Hkv + (head_ok ? h : 0)) * (size_t)(kBT * kD);
+    const int page = __builtin_amdgcn_readlane(my_page, m - m0);
+    ok = page >= 0;
+    return ((size_t)(ok ? page : 0) * g.Hkv + h) * (size_t)(kBT * kD);
   };
   uint4 kr[2][4], vr[2][4];
   bool ok;
-  auto load_tile = [&](int m) {
-    const size_t base = tile_base(m, ok);
+  auto load_k = [&](int m) {
+    bool okm;
+    const size_t base = tile_base(m, okm);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const size_t off = base + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq;
-        kr[tt][c] = load_nt16(kpool + off);
-        vr[tt][c] = load_nt16(vpool + off);
-      }
+      for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(kpool + base + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+  };
+  auto load_v = [&](int m) {
+    bool okm;
+    const size_t base = tile_base(m, okm);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vr[tt][c] = load_nt16(vpool + base + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+  };
+  auto load_tile = [&](int m) {
+    load_k(m);
+    load_v(m);
   };
   load_tile(m0);
   __syncthreads();                                     // inv_freq
 
   {
     const int n_t = (g.rows + g.G - 1) / g.G;
-    for (int idx = tid; idx < n_t * (kD / 2); idx += 512) {
+    for (int idx = tid; idx < n_t * (kD / 2); idx += nthr) {
       const int t = idx / (kD / 2), i = idx % (kD / 2);
       rope_cos_sin((double)(V + t), inv_freq[i], cs_tab[t][i][0], cs_tab[t][i][1]);
     }
-    for (int idx = tid; idx < kBT * (kD / 2); idx += 512) {
+    for (int idx = tid; idx < kBT * (kD / 2); idx += nthr) {
       const int u = idx / (kD / 2), i = idx % (kD / 2);
       float cb, sb;
       rope_offset_pair(u, inv_freq[i], cb, sb);
@@ -185,7 +201,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   for (int m = m0; m < m1; ++m) {
     const int buf = (m - m0) & 1;
 #pragma unroll 1
-    for (int idx = tid; idx < kBT * (kD / 2); idx += 512) {
+    for (int idx = tid; idx < kBT * (kD / 2); idx += nthr) {
       const int u = idx / (kD / 2), i = idx % (kD / 2);
       const double2 a = base_cs[buf][i];
       const float2 b = offs[u][i];
@@ -194,13 +210,23 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 
     // this wavefront's V tile, token-major, into its own LDS tile (tokens at
     // or past V are zeros, as the gather writes them; their weights are 0)
+    // (the zeroing is an AND with a lane mask, not a select: a select
+    // compiles to exec-masked branches, after which the compiler no longer
+    // knows the tile's loads have landed and waits for the view stores too)
     const int tb = kBT * m;
+    (void)tile_base(m, ok);
+    uint32_t keep[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) keep[tt] = ok && tb + 16 * tt + col < V ? 0xffffffffu : 0u;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4 *>(myv + (16 * tt + col) * kPgPitch + 32 * c + 8 * qq) =
-            ok && tb + 16 * tt + col < V ? vr[tt][c] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(myv + (16 * tt + col) * kPgPitch + 32 * c + 8 * qq) = and_mask(vr[tt][c], keep[tt]);
+    // the next V tile leaves as soon as this one is staged: it flies through
+    // the barrier, the rotation and both products (at 1M tokens 471 -> 458 us
+    // with the view written, 258 -> 225 us without)
+    if (m + 1 < m1) load_v(m + 1);
     __syncthreads();
 
     // K rotated at view positions 32m + u and rounded to bf16: A operands
@@ -211,7 +237,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
       float kv[4][8];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 r = ok && tb + u < V ? kr[tt][c] : make_uint4(0, 0, 0, 0);
+        const uint4 r = and_mask(kr[tt][c], keep[tt]);
         const uint32_t e[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -235,21 +261,22 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
         }
 #pragma unroll
       for (int c = 0; c < 4; ++c) ka[tt][c] = as_bf16x8(make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]));
-      if (WV && head_ok) {   // the view's K row of token u: dims 32c + 8qq .. + 7 from this lane
+      if (WV) {   // the view's K row of token u: dims 32c + 8qq .. + 7 from this lane
         uint16_t *row = kview + (((size_t)s * g.Hkv + h) * max_view + tb + u) * kD + 8 * qq;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           store_nt16(row + 32 * c, make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]));
       }
     }
-    // writing the view, the next tile's loads go out as soon as this tile's
-    // registers are free and fly during the products (479 against 491 us at
-    // 1M tokens; the attention alone measured no better this way)
-    if (WV && m + 1 < m1) load_tile(m + 1);
+    // the next K tile: writing the view, as soon as the rotation has freed its
+    // registers; without the view, once the score products have consumed the
+    // rotated operands (225 -> 204 us at 1M tokens).  Any order that puts
+    // this tile's K view stores behind the next loads spills ~40 registers.
+    if (WV && m + 1 < m1) load_k(m + 1);
 
+    floatx4 scs[NT][2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      floatx4 sc[2];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
@@ -258,8 +285,12 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
           a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][c], qhi[nt][c], a, 0, 0, 0);
           a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][c], qlo[nt][c], a, 0, 0, 0);
         }
-        sc[tt] = a;
+        scs[nt][tt] = a;
       }
+    if (!WV && m + 1 < m1) load_k(m + 1);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      floatx4 sc[2] = {scs[nt][0], scs[nt][1]};
       if (tb + kBT > V) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
@@ -305,7 +336,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
           w[k] = (uint32_t)myv[pg_token(qq, 2 * k) * kPgPitch + dim] |
                  ((uint32_t)myv[pg_token(qq, 2 * k + 1) * kPgPitch + dim] << 16);
         const bf16x8 va = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-        if (WV && nt == 0 && head_ok)   // the lane's 8 tokens of dim are slots 8qq .. 8qq + 7 of the view's V
+        if (WV && nt == 0)   // the lane's 8 tokens of dim are slots 8qq .. 8qq + 7 of the view's V
           store_nt16(vview + ((((size_t)s * g.Hkv + h) * (max_view / kBT) + m) * kD + dim) * kBT + 8 * qq,
                      make_uint4(w[0], w[1], w[2], w[3]));
         o[nt][dt] *= alpha;
@@ -317,12 +348,8 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
     // from (every wavefront passed this block's barrier, so it is read out;
     // block m + 1's barrier orders the write before block m + 2 reads it)
     if (tid < kD / 2 && m + 2 < m1) base_cs[buf][tid] = block_angle((double)(kBT * (m + 2)), inv_freq[tid]);
-    // one tile in flight per wavefront: the next tile's loads follow the
-    // products (eight wavefronts per CU move 128 KiB per step between them)
-    if (!WV && m + 1 < m1) load_tile(m + 1);
   }
 
-  if (!head_ok) return;
   // the wavefront alone holds its head's rows: partials (or the output)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -514,9 +541,18 @@ __global__ __launch_bounds__(256) void k_attend_paged_f32(
 
 }  // namespace
 
+// Wavefronts (KV heads) per workgroup of the bf16 kernel: the largest divisor
+// of Hkv up to 8, so that every wavefront has a head and no store or load in
+// the block loop is guarded by one.
+int paged_waves(int Hkv) {
+  for (int w = kPgWaves; w > 1; --w)
+    if (Hkv % w == 0) return w;
+  return 1;
+}
+
 int paged_blocks_per_split(int n_sessions, int Hkv, int n_list) {
   // aim for >= 256 workgroups of 8 wavefronts; 1 .. 64 list blocks per split
-  const long groups = (Hkv + kPgWaves - 1) / kPgWaves;
+  const long groups = Hkv / paged_waves(Hkv);
   long b = ((long)n_list * groups * n_sessions + 255) / 256;
   if (b < 1) b = 1;
   if (b > 64) b = 64;
@@ -544,9 +580,10 @@ hipError_t launch_attend_paged(int bf16, const void *q, const float *qw, float e
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (splits > 0) {
-    dim3 grid((unsigned)splits, (unsigned)((g.Hkv + kPgWaves - 1) / kPgWaves), (unsigned)n_sess);
+    const int nw = paged_waves(g.Hkv);
+    dim3 grid((unsigned)splits, (unsigned)(g.Hkv / nw), (unsigned)n_sess);
 #define KVMEM_PAGED(NT, WV)                                                                                     \
-  hipLaunchKernelGGL((k_attend_paged_bf16<NT, WV>), grid, dim3(512), 0, st, (const uint16_t *)q, qw, eps,          \
+  hipLaunchKernelGGL((k_attend_paged_bf16<NT, WV>), grid, dim3(64 * nw), 0, st, (const uint16_t *)q, qw, eps,          \
                      (const uint16_t *)k_pool, (const uint16_t *)v_pool, table, view_blocks, part_o, part_ml, out, \
                      dev_err, view_tok, n_all, s0, g, theta, (uint16_t *)k_view, (uint16_t *)v_view, max_view)
     const bool wv = k_view != nullptr;
