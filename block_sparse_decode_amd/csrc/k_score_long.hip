@@ -9,21 +9,25 @@
 // computed twice on the matrix cores:
 //
 //   k_long_qprep : q~ * log2(e)/sqrt(d) of every row as bf16 hi + lo B-operand
-//                  fragments (16 rows per operand set).
+//                  fragments (16 rows per operand set), and each row's |q~|.
 //   k_long_pass  : one workgroup per (session, KV head, group of 256 blocks);
 //                  each of its 4 wavefronts holds one 64-block index tile as
 //                  A operands in registers for the whole kernel, and the rows
 //                  stream through LDS in chunks of 64 (double-buffered).
-//                  STATS: per-row (max, sum of 2^(s - max)) over the group's
+//                  STATS: per-row (M, sum of 2^(s - M)) over the group's
 //                  blocks -> part[row][group].  AGG: 2^(s - lse[row]) summed
 //                  over all rows into per-lane block sums, reduced across the
 //                  16 lanes of each block at the end -> A[b].
 //   k_long_lse   : lse[row] = log2 of the row's normaliser from its partials.
 //
 // Scores are in log2 units throughout (the constant is folded into the query),
-// so every exponential is a single exp2.  The two passes make identical
-// products, so each row's probabilities are normalised exactly as they are
-// summed.  Output order is fixed everywhere (deterministic).
+// so every exponential is a single exp2.  Each exponential's shift enters the
+// products as the accumulator's initial value (-lse[row] in AGG; in STATS,
+// -|q~| max|k_bar| over the tile, an upper bound of the row's scores there by
+// Cauchy-Schwarz that stands for the row maximum M, with the exact maximum
+// taken only when the bound lies so far above the scores that the sum would
+// lose its terms), which leaves one exp2 and one add per score.  Output order
+// is fixed everywhere (deterministic).
 #include "kvmem_internal.h"
 
 namespace kvmem {
@@ -42,8 +46,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast
 // dims 32k + 8qq .. + 7 of row 16cs + col, q~ * log2(e)/sqrt(d), bf16 hi (hl=0)
 // or lo (hl=1).  Rows past T * G are zero.  One wavefront per (s, h, cs).
 __global__ __launch_bounds__(64) void k_long_qprep(const uint16_t *__restrict__ q, const float *__restrict__ qw,
-                                                   float eps, uint4 *__restrict__ qf, int s0, ScoreGeom g,
-                                                   int n_sets) {
+                                                   float eps, uint4 *__restrict__ qf, float *__restrict__ qn, int s0,
+                                                   ScoreGeom g, int n_sets) {
   const int lane = threadIdx.x;
   const int qq = lane >> 4, col = lane & 15;
   const int cs = blockIdx.x % n_sets;
@@ -72,20 +76,27 @@ __global__ __launch_bounds__(64) void k_long_qprep(const uint16_t *__restrict__ 
   ss = sum_xor32(ss);
   const float rs = valid ? (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * kLog2eRsqrtD : 0.f;
   uint4 *dst = qf + (((size_t)s * g.Hkv + h) * n_sets + cs) * 8 * 64 + lane;
+  float nn = 0.f;                                       // |q~|^2 of the row (this lane's 32 dims)
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
       uint32_t h0, l0, h1, l1;
-      split_hi_lo(x[k][j] * rs * qw[32 * k + 8 * qq + j], h0, l0);
-      split_hi_lo(x[k][j + 1] * rs * qw[32 * k + 8 * qq + j + 1], h1, l1);
+      const float v0 = x[k][j] * rs * qw[32 * k + 8 * qq + j];
+      const float v1 = x[k][j + 1] * rs * qw[32 * k + 8 * qq + j + 1];
+      nn += v0 * v0 + v1 * v1;
+      split_hi_lo(v0, h0, l0);
+      split_hi_lo(v1, h1, l1);
       hw[j / 2] = h0 | (h1 << 16);
       lw[j / 2] = l0 | (l1 << 16);
     }
     dst[(2 * k) * 64] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     dst[(2 * k + 1) * 64] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
+  nn = sum_xor16(nn);
+  nn = sum_xor32(nn);
+  if (qq == 0) qn[((size_t)s * g.Hkv + h) * (16 * n_sets) + r] = sqrtf(nn);
 }
 
 struct LongGeom {
@@ -136,6 +147,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i) vmask |= (live && tile * kIdxTile + 16 * m + 4 * qq + i < nb) ? 1 << (4 * m + i) : 0;
 
+  // STATS: the largest |index row| of the wavefront's valid blocks.  A row's
+  // scores over the tile are at most |q~| kmax (Cauchy-Schwarz), which shifts
+  // its exponentials in place of the row maximum.
+  float kmax = 0.f;
+  if (!AGG) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float nn = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t e[4] = {a[4 * m + k].x, a[4 * m + k].y, a[4 * m + k].z, a[4 * m + k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = bf16_lo(e[j]), hi = bf16_hi(e[j]);
+          nn += lo * lo + hi * hi;
+        }
+      }
+      nn = sum_xor16(nn);
+      nn = sum_xor32(nn);                               // block 16m + col, in all 4 lanes of the column
+      if (live && tile * kIdxTile + 16 * m + col < nb) kmax = fmaxf(kmax, nn);
+    }
+    kmax = sqrtf(wave_max_dpp(kmax));
+  }
+
   float acc[16];                                        // AGG: sum over rows of 2^(s - lse) per own block
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -157,16 +192,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       const int i = j * 256 + tid;                                                    \
       pre[j] = reinterpret_cast<const u32x4 *>(qsrc)[(size_t)fset0 * 8 * 64 + (i < fn ? i : 0)]; \
     }                                                                                 \
-    if (AGG && tid < kLongChunkRows) {                                                \
+    if (tid < kLongChunkRows) {                                                       \
       const int r = fset0 * 16 + tid;                                                 \
-      pre_lse = r < L.rows_pad ? lse[sh * L.rows_pad + r] : INFINITY;                 \
+      pre_lse = r < L.rows_pad ? lse[sh * L.rows_pad + r] : (AGG ? INFINITY : 0.f);   \
     }                                                                                 \
   }
 #define KVMEM_LONG_STORE(BUF)                                                          \
   {                                                                                   \
     _Pragma("unroll") for (int j = 0; j < kPer; ++j)                                 \
         reinterpret_cast<u32x4 *>(sb[(BUF)])[j * 256 + tid] = pre[j];                 \
-    if (AGG && tid < kLongChunkRows) slse[(BUF)][tid] = pre_lse;                      \
+    if (tid < kLongChunkRows) slse[(BUF)][tid] = pre_lse;                             \
   }
 
   KVMEM_LONG_FETCH(0)
@@ -185,10 +220,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         b[k][0] = as_bf16x8(sb[buf][(cs * 8 + 2 * k) * 64 + lane]);
         b[k][1] = as_bf16x8(sb[buf][(cs * 8 + 2 * k + 1) * 64 + lane]);
       }
+      // the shift of this lane's row enters as the accumulator's initial value,
+      // so the products come out as s - shift: STATS, the bound |q~| kmax of a
+      // full tile (0 otherwise); AGG, the row's lse (+inf for padding rows)
+      const float shift = AGG ? slse[buf][cs * 16 + col] : (full ? slse[buf][cs * 16 + col] * kmax : 0.f);
       floatx4 d[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        d[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        d[m] = floatx4{-shift, -shift, -shift, -shift};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[4 * m + k]), b[k][0], d[m], 0, 0, 0);
@@ -197,22 +236,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       }
       const int row = (set0 + cs) * 16 + col;          // this lane's query row
       if (!AGG) {
-        // the row's max and sum of 2^(s - max) over the wavefront's blocks
-        // (v_exp_f32: results below 2^-126 flush to zero, which no sum here
-        // can notice)
-        float mx = -INFINITY, sum = 0.f;
+        // the row's (max, sum of 2^(s - max)) over the wavefront's blocks, with
+        // the bound standing for the max (v_exp_f32: results below 2^-126
+        // flush to zero; a bound so far above a row's scores that its sum
+        // falls below 2^-60 sends the set down the exact path)
+        float mx = shift, sum = 0.f;
+        bool exact = !full;
         if (full) {
 #pragma unroll
           for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, d[m][i]);
-          mx = max_xor16(mx);
-          mx = max_xor32(mx);
+            for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(d[m][i]);
+          sum = sum_xor16(sum);
+          sum = sum_xor32(sum);
+          if (__ballot(!(sum >= 0x1p-60f)) != 0) {       // rare: the products again, unshifted
+            exact = true;
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m) {
+              d[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(d[m][i] - mx);
-        } else {
+              for (int k = 0; k < 4; ++k) {
+                d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[4 * m + k]), b[k][0], d[m], 0, 0, 0);
+                d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[4 * m + k]), b[k][1], d[m], 0, 0, 0);
+              }
+            }
+          }
+        }
+        if (exact) {
+          mx = -INFINITY;
+          sum = 0.f;
 #pragma unroll
           for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -225,9 +277,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
               for (int i = 0; i < 4; ++i) sum += (vmask >> (4 * m + i)) & 1 ? __builtin_amdgcn_exp2f(d[m][i] - mx) : 0.f;
           }
+          sum = sum_xor16(sum);
+          sum = sum_xor32(sum);
         }
-        sum = sum_xor16(sum);
-        sum = sum_xor32(sum);
         if (qq == 0) sst[wave][cs * 16 + col] = make_float2(mx, sum);
         if (scores != nullptr && row < L.n_rows) {
           // optional score output, natural-log units: scores[s][t][query head][block]
@@ -237,14 +289,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
           for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if ((vmask >> (4 * m + i)) & 1) dst[tile * kIdxTile + 16 * m + 4 * qq + i] = d[m][i] * kLn2;
+              if ((vmask >> (4 * m + i)) & 1) dst[tile * kIdxTile + 16 * m + 4 * qq + i] = (d[m][i] + (exact ? 0.f : shift)) * kLn2;
         }
       } else {
-        const float lr = slse[buf][cs * 16 + col];      // +inf for padding rows: contributes 0
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[4 * m + i] += __builtin_amdgcn_exp2f(d[m][i] - lr);
+          for (int i = 0; i < 4; ++i) acc[4 * m + i] += __builtin_amdgcn_exp2f(d[m][i]);
       }
     }
     if (more) KVMEM_LONG_STORE(buf ^ 1)
@@ -356,11 +407,13 @@ hipError_t launch_score_long(const void *index, const void *q, const float *qw, 
   for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
   if (max_nb == 0) return hipSuccess;
   const LongGeom L = long_geom(g);
+  // the rows' |q~| go into the lse array, which the statistics pass reads
+  // and k_long_lse then overwrites
   hipLaunchKernelGGL(k_long_qprep, dim3((unsigned)(g.Hkv * L.n_sets), (unsigned)n_sess), dim3(64), 0, st,
-                     (const uint16_t *)q, qw, eps, qf, s0, g, L.n_sets);
+                     (const uint16_t *)q, qw, eps, qf, lse, s0, g, L.n_sets);
   const dim3 grid((unsigned)((max_nb + kLongBlocks - 1) / kLongBlocks), (unsigned)g.Hkv, (unsigned)n_sess);
   hipLaunchKernelGGL(k_long_pass<false>, grid, dim3(256), 0, st, (const uint16_t *)index, (const uint4 *)qf, part,
-                     (const float *)nullptr, (float *)nullptr, scores_opt, n_blocks, s0, g, L);
+                     (const float *)lse, (float *)nullptr, scores_opt, n_blocks, s0, g, L);
   const long rows = (long)n_sess * g.Hkv * L.rows_pad;
   hipLaunchKernelGGL(k_long_lse, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, (const float2 *)part, lse,
                      n_blocks, s0, n_sess, g, L);

@@ -295,6 +295,40 @@ def test_long_chunk_parity(name):
     _full_check(wl, attend=False)
 
 
+def _bound_far_workload():
+    """Long chunk whose queries have no component in dims 64..127 while the
+    keys of four blocks (two 64-block tiles) are large there: those blocks'
+    index rows have a large norm and no effect on any score, so the
+    statistics pass's Cauchy-Schwarz shift |q~| max|k_bar| lies far above the
+    rows' scores in those tiles (its exact-maximum path) and close to them in
+    the rest."""
+    cfg = small_cfg("long_bound_far", "bf16", S=1, Hq=16, Hkv=2, T=8, n_tokens=(32 * 600 + 7,), k=40, R=3,
+                    n_planted=8, seed=54)
+    wl = make_workload(cfg)
+    wl.q[..., 64:] = 0
+    wl.k_pool[wl.block_table[0, [70, 80, 200, 210]], :, :, 64:] = 0x41C0   # bf16 24.0
+    certify(wl)
+    return wl
+
+
+def test_long_chunk_shift_far_above_scores():
+    _need_gpu()
+    wl = _bound_far_workload()
+    cfg = wl.cfg
+    ws = oracle_ws(wl)
+    G, d = cfg.group, cfg.head_dim
+    c = np.log2(np.e) / np.sqrt(d)
+    qn = O.q_rmsnorm(O.decode(wl.q[0], cfg.dtype), wl.q_norm_w, cfg.eps)
+    for h in range(cfg.n_kv_heads):                       # the case is what it claims to be
+        idx = O.mean_k_index(ws, 0, h)
+        qg = qn[:, h * G:(h + 1) * G].reshape(-1, d)
+        s, kn, qnorm = qg @ idx.T * c, np.linalg.norm(idx, axis=1), np.linalg.norm(qg, axis=1) * c
+        for t in range(len(idx) // 64):
+            gap = qnorm * kn[64 * t:64 * t + 64].max() - s[:, 64 * t:64 * t + 64].max(axis=1)
+            assert (gap.min() > 100) if t in (1, 3) else (gap.max() < 50), (h, t, gap.min(), gap.max())
+    _full_check(wl, attend=False)
+
+
 def test_c1_parity():
     _need_gpu()
     wl = make_workload(CONFIGS["c1"])
