@@ -141,12 +141,14 @@ def _oracle_stages(wl, heads, threads=None) -> dict:
     return t
 
 
-def cpu_baseline(wl, heads=(0, 1, 2, 3), small=("c1", "c2")) -> dict:
+def cpu_baseline(wl, heads=None, small=("c1", "c2")) -> dict:
     """The oracle as it stands, timed stage by stage on a sample: the whole
-    path for a few of the KV heads of session 0, with all BLAS threads and
-    with one, scaled to the full workload; the same for the small workloads
-    (all heads of c1, two of c2)."""
+    path for every KV head of session 0 (by default), with all BLAS threads
+    and with one, scaled to the full workload; the same for the small
+    workloads (two heads of c1 and of c2, scaled)."""
     from workloads import CONFIGS, make_workload
+    if heads is None:
+        heads = tuple(range(wl.cfg.n_kv_heads))
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])

@@ -34,6 +34,14 @@ CASES.update({n: SMALL[n] for n in ("f32_ragged", "f32_t3_g4")})
 CASES["c1"] = CONFIGS["c1"]
 CASES["nine_heads"] = small_cfg("paged_nine_heads", "bf16", S=2, Hq=18, Hkv=9, n_tokens=(32 * 210 + 3, 32 * 90),
                                 k=30, R=3, n_planted=4, seed=111)
+# workgroups hold the largest divisor of Hkv up to 8 wavefronts: one (Hkv = 1),
+# five (a prime), and two groups of six (Hkv = 12)
+CASES["one_head"] = small_cfg("paged_one_head", "bf16", S=2, Hq=8, Hkv=1, n_tokens=(32 * 150 + 9, 32 * 40),
+                              k=20, R=2, n_planted=4, seed=112)
+CASES["five_heads"] = small_cfg("paged_five_heads", "bf16", S=2, Hq=10, Hkv=5, n_tokens=(32 * 95 + 30, 32 * 61),
+                                k=14, R=3, n_planted=3, seed=113)
+CASES["twelve_heads"] = small_cfg("paged_twelve_heads", "bf16", S=1, Hq=48, Hkv=12, n_tokens=(32 * 120 + 1,),
+                                  k=16, R=2, n_planted=3, seed=114)
 
 
 def _run(wl, heads=None):
