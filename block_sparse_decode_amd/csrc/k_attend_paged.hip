@@ -146,13 +146,14 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 #pragma unroll
       for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(kpool + base + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
   };
+  // V goes through LDS, so its loads take whole rows: instruction j, lane l
+  // reads token 4j + l / 16, dims 8 (l % 16) .. + 7 (full 128-byte lines)
   auto load_v = [&](int m) {
     bool okm;
     const size_t base = tile_base(m, okm);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) vr[tt][c] = load_nt16(vpool + base + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+    for (int j = 0; j < 8; ++j)
+      vr[j >> 2][j & 3] = load_nt16(vpool + base + (size_t)(4 * j + (lane >> 4)) * kD + 8 * (lane & 15));
   };
   auto load_tile = [&](int m) {
     load_k(m);
@@ -219,10 +220,11 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) keep[tt] = ok && tb + 16 * tt + col < V ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4 *>(myv + (16 * tt + col) * kPgPitch + 32 * c + 8 * qq) = and_mask(vr[tt][c], keep[tt]);
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 4 * j + (lane >> 4);
+      *reinterpret_cast<uint4 *>(myv + tok * kPgPitch + 8 * (lane & 15)) =
+          and_mask(vr[j >> 2][j & 3], ok && tb + tok < V ? 0xffffffffu : 0u);
+    }
     // the next V tile leaves as soon as this one is staged: it flies through
     // the barrier, the rotation and both products (at 1M tokens 471 -> 458 us
     // with the view written, 258 -> 225 us without)
