@@ -10,9 +10,11 @@
 //
 // k_aggregate: A[b] = sum_rows exp(s[row][b] - M_row) / Z_row for every
 //   complete block (1024 blocks per workgroup), and the candidates counted by
-//   the top digit of A's bits into the (session, head)'s selection histogram.
-// k_topk_tile: the selection when every session has at most 32768 candidates
-//   and the histogram is there (described with the kernel).
+//   the top digit of A's bits into the (session, head)'s selection histogram;
+//   each chunk's keys are also written grouped by that digit.
+// k_topk_chunk: the selection when every session has at most 32768
+//   candidates and the histogram is there, one workgroup per aggregation
+//   chunk (described with the kernel).
 // k_topk: the selection otherwise, one workgroup per (session, head),
 //   starting from that histogram when there is one.
 //
@@ -266,34 +268,40 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Selection of up to one tile of candidates from the aggregation histogram.
-// Wavefront w reads keys w*2048 + j*64 + lane (j < 32) as plain dword loads,
-// so every load instruction covers 256 contiguous bytes and the 128 KiB of a
-// head arrive in a few hundred cache-line requests; index order is (w, j,
-// lane).  The key is A's bit pattern without the sign bit, the same 31 bits
-// the aggregation counted, so the histogram, the refinement and the
-// compaction agree on every key.
-//  1. The bin of the k-th largest key from the histogram (a prefix sum over
-//     the bins in descending order).
-//  2. The keys of that bin are copied into an LDS list (one LDS atomic per
-//     wavefront reserves its run).
+// Selection spread over the aggregation chunks: one workgroup per (session,
+// KV head, chunk of kAggChunk candidates), thread t owning block
+// chunk * kAggChunk + t, when a session has at most kTile candidates.  The
+// aggregation left the head's histogram by top digit (bits 30..20 of the key,
+// the key being A's bit pattern without the sign bit) and, per chunk, the
+// chunk's keys grouped by digit (highest first) with its counts of keys at or
+// above every digit.  Every workgroup of a head finds the same exact
+// threshold independently, reading only the keys of the boundary digit:
+//  1. The boundary bin b0 of the k-th largest key from the histogram (a
+//     prefix sum over the bins in descending order).
+//  2. Per chunk j: the keys above b0 and in b0 (two counts), and the run of
+//     b0's keys in j's grouped keys, copied into an LDS list in chunk order.
 //  3. Two histogram passes over the list fix bits 19..9 and 8..0: the exact
 //     threshold key and how many keys equal to it are taken (ties to the
-//     lower block index).
-//  4. Ordered compaction: per load instruction, the kept lanes' positions
-//     are their rank in the wavefront's ballot plus the kept keys before
-//     them; the block ids go straight to the list in memory.
+//     lower block index, so to the lower chunk first).
+//  4. This chunk's first list position: the keys above b0 in earlier chunks
+//     plus their boundary keys taken (counted over the list's earlier
+//     chunks).  Its own keys, read from A in block order, are placed by one
+//     workgroup scan (two when only some keys equal to the threshold are
+//     taken).
+// The first chunk's workgroup also writes the recent blocks and the padding.
 // ---------------------------------------------------------------------------
-constexpr int kTkKeys = kTile / kTopkThreads;     // 32 keys per thread
-constexpr uint32_t kTkNone = 0x80000000u;          // no candidate: below every key as a signed int
-constexpr int kTkWaveKeys = kTile / kTopkWaves;   // 2048 keys per wavefront
+constexpr int kMaxSelChunks = kTile / kAggChunk;   // 32
+constexpr int kCopyBatch = 8;                      // boundary keys fetched per thread at a time
+constexpr uint32_t kKeyMask = 0x7fffffffu;
 
-struct TileSmem {
-  uint32_t hist[kBins];
+struct ChunkSmem {
+  uint32_t hist[kBins];              // bits 19..9 of the boundary keys
+  uint32_t hist2[kBins];             // bits 8..0 of those sharing the threshold's bits 19..9
   uint32_t wsum[kTopkWaves];
-  uint32_t wgt[kTopkWaves];
-  uint32_t weq[kTopkWaves];
-  uint32_t digit, above, n_list;
+  uint32_t digit, above, before_above;
+  uint32_t cab[kMaxSelChunks];       // per chunk: keys in bins above b0
+  uint32_t cin[kMaxSelChunks];       // per chunk: keys in b0
+  uint32_t coff[kMaxSelChunks + 1];  // per chunk: first list position of its b0 keys
   uint32_t list[kTile];
 };
 
@@ -310,29 +318,35 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// Makes the keys opaque to the compiler, so that the comparisons of a later
-// loop are recomputed instead of keeping 32 lane masks of an earlier one alive
-// in scalar registers.
-__device__ __forceinline__ void launder(uint32_t (&key)[kTkKeys]) {
-#pragma unroll
-  for (int j = 0; j < kTkKeys; ++j) asm volatile("" : "+v"(key[j]));
-}
-
 __device__ __forceinline__ uint32_t wave_total(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
+}
+
+// Exclusive prefix sum of one value per thread over a 1024-thread workgroup
+// (thread order); *total gets the sum.  wsum: kTopkWaves words of LDS.
+__device__ __forceinline__ uint32_t wg_excl_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - v, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t c = wsum[w];
+    before += (w < wave) ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before;
 }
 
 // Bin of the krem-th largest key from counts in descending bin order (thread
 // t owns bins kBins-1-2t and kBins-2-2t); sets sm.digit and sm.above (keys in
 // the bins above it).  The counts must total at least krem.
-__device__ __forceinline__ void find_bin_dpp(uint32_t c0, uint32_t c1, uint32_t krem, TileSmem &sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(c0 + c1);
-  if (lane == 63) sm.wsum[wave] = incl;
-  __syncthreads();
-  uint32_t before = incl - (c0 + c1);
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) before += (w < wave) ? sm.wsum[w] : 0u;
+__device__ __forceinline__ void find_bin_dpp(uint32_t c0, uint32_t c1, uint32_t krem, ChunkSmem &sm) {
+  uint32_t total;
+  const uint32_t before = wg_excl_scan(c0 + c1, sm.wsum, total);
   if (before < krem && krem <= before + c0) {
     sm.digit = kBins - 1 - 2 * threadIdx.x;
     sm.above = before;
@@ -343,150 +357,167 @@ __device__ __forceinline__ void find_bin_dpp(uint32_t c0, uint32_t c1, uint32_t 
   __syncthreads();
 }
 
-__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-__global__ __launch_bounds__(kTopkThreads) void k_topk_tile(const float *__restrict__ A,
-                                                            const uint32_t *__restrict__ hist,
-                                                            int32_t *__restrict__ view_blocks, TopkMeta meta, int s0,
-                                                            int Hkv, int max_blocks, int n_list) {
-  __shared__ TileSmem sm;
-  const int sl = blockIdx.y;
+__global__ __launch_bounds__(kTopkThreads) void k_topk_chunk(const float *__restrict__ A,
+                                                             const uint32_t *__restrict__ hist,
+                                                             const uint32_t *__restrict__ skey,
+                                                             const uint16_t *__restrict__ sincl,
+                                                             int32_t *__restrict__ view_blocks, TopkMeta meta,
+                                                             int s0, int Hkv, int max_blocks, int n_chunks,
+                                                             int n_list) {
+  __shared__ ChunkSmem sm;
+  const int sl = blockIdx.z;
   const int s = s0 + sl;
-  const int h = blockIdx.x;
+  const int h = blockIdx.y;
+  const int ci = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = meta.n_cand.v[sl], k = meta.k_eff.v[sl];
-  int32_t *out = view_blocks + ((size_t)s * Hkv + h) * n_list;
+  const size_t hk = (size_t)s * Hkv + h;
+  int32_t *out = view_blocks + hk * n_list;
 
-  if (k > 0) {
-    const bool take_all = k >= nc;
-    const uint32_t *hc = hist + ((size_t)s * Hkv + h) * kSelBins;
-    const float *a = A + ((size_t)s * Hkv + h) * max_blocks;
-    // the counts first: the bin search needs only them and overlaps the keys
-    const uint32_t c0 = hc[kBins - 1 - 2 * tid];
-    const uint32_t c1 = hc[kBins - 2 - 2 * tid];
-    const int base = wave * kTkWaveKeys + lane;
-    uint32_t key[kTkKeys];
-#pragma unroll
-    for (int j = 0; j < kTkKeys; ++j) key[j] = __float_as_uint(a[min(base + 64 * j, nc - 1)]);
+  if (ci == 0) {
+    const int r0 = meta.r_start.v[sl], n_rec = meta.n_all.v[sl] - r0;
+    for (int j = tid; j < n_list - k; j += kTopkThreads) out[k + j] = (j < n_rec) ? r0 + j : -1;
+  }
+  if (k == 0 || ci * kAggChunk >= nc) return;          // (uniform over the workgroup)
+  const int b = ci * kAggChunk + tid;
+  const bool valid = b < nc;
+  if (k >= nc) {                                       // every candidate is taken
+    if (valid) out[b] = b;
+    return;
+  }
 
-    // taking every candidate: a threshold below every key (and no ties)
-    uint32_t thr = take_all ? 0xffffffffu : 0u, krem = 0, n_eq = 0;
-    // (unconditional, so the counts' loads stay ahead of the keys'; with
-    // every candidate taken it looks for no key and finds no bin)
-    if (tid == 0) sm.n_list = 0;
-    find_bin_dpp(c0, c1, take_all ? 0u : (uint32_t)k, sm);
-    const uint32_t b0 = sm.digit;
-    if (!take_all) krem = (uint32_t)k - sm.above;
+  // the histogram's counts and this thread's key
+  const uint32_t *hc = hist + hk * kSelBins;
+  const uint32_t c0 = hc[kBins - 1 - 2 * tid];
+  const uint32_t c1 = hc[kBins - 2 - 2 * tid];
+  const uint32_t key = valid ? __float_as_uint(A[hk * max_blocks + b]) & kKeyMask : 0u;
+  // the refinement histograms are cleared here, ordered before their use by
+  // the barriers below
+  for (int i = tid; i < kBins; i += kTopkThreads) {
+    sm.hist[i] = 0u;
+    sm.hist2[i] = 0u;
+  }
+  find_bin_dpp(c0, c1, (uint32_t)k, sm);
+  const uint32_t b0 = sm.digit;
+  uint32_t krem = (uint32_t)k - sm.above;
+
+  // per chunk: keys above b0 and in b0
+  const int nch = (nc + kAggChunk - 1) / kAggChunk;
+  if (tid < nch) {
+    const uint16_t *inc = sincl + (hk * n_chunks + tid) * kSelBins;
+    const uint32_t ab = b0 + 1 < (uint32_t)kBins ? inc[b0 + 1] : 0u;
+    sm.cab[tid] = ab;
+    sm.cin[tid] = inc[b0] - ab;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t vin = lane < nch ? sm.cin[lane] : 0u;
+    const uint32_t vab = lane < ci ? sm.cab[lane] : 0u;
+    const uint32_t incl = wave_incl_scan(vin);
+    if (lane < nch) sm.coff[lane] = incl - vin;
+    if (lane == 63) sm.coff[nch] = incl;               // keys of b0 over the head
+    const uint32_t ab_total = wave_total(vab);
+    if (lane == 0) sm.before_above = ab_total;
+  }
+  __syncthreads();
+  // b0's keys of every chunk, in chunk order: thread t fetches list
+  // positions t + 1024 u.  Up to kCopyBatch * 1024 keys (one batch) stay in
+  // registers for the passes below; a longer list is read back from LDS.
+  const int nl = (int)sm.coff[nch];
+  const bool in_regs = nl <= kCopyBatch * kTopkThreads;
+  uint32_t v[kCopyBatch];
+  for (int p0 = 0; p0 < nl; p0 += kCopyBatch * kTopkThreads) {
+    // every position's chunk first (the last j with coff[j] <= p, coff
+    // ascending), then all loads back to back; positions past the list
+    // read its last key
+    uint32_t src[kCopyBatch];
 #pragma unroll
-    for (int j = 0; j < kTkKeys; ++j) key[j] = base + 64 * j < nc ? key[j] & 0x7fffffffu : kTkNone;
-    // per wavefront: keys above the threshold (cgt) and equal to it (ceq)
-    uint32_t cgt, ceq = 0;
-    if (take_all) {
-      cgt = (uint32_t)min(max(nc - wave * kTkWaveKeys, 0), kTkWaveKeys);
-    } else {
-      // keys of the bins above the boundary bin are kept whatever the
-      // refinement finds; the boundary bin's keys go into the list
-      const int above_key = (int)((b0 + 1) << kSelShift);
-      uint32_t c_in = 0, c_above = 0;
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int p = min(p0 + u * kTopkThreads + tid, nl - 1);
+      int j = 0;
 #pragma unroll
-      for (int j = 0; j < kTkKeys; ++j) {
-        c_in += (key[j] >> kSelShift) == b0 ? 1u : 0u;
-        c_above += (int)key[j] >= above_key ? 1u : 0u;
+      for (int step = kMaxSelChunks / 2; step >= 1; step >>= 1) {
+        const int jj = min(j + step, nch);               // coff[nch] = nl > p
+        j = (int)sm.coff[jj] <= p ? jj : j;
       }
-      const uint32_t both = wave_total((c_above << 16) | c_in);   // each at most 2048
-      const uint32_t cnt = both & 0xffffu;
-      cgt = both >> 16;
-      launder(key);
-      uint32_t run0 = 0;
-      if (lane == 0 && cnt) run0 = atomicAdd(&sm.n_list, cnt);
-      run0 = __builtin_amdgcn_readfirstlane(run0);
-      uint32_t run = run0;
-#pragma unroll
-      for (int j = 0; j < kTkKeys; ++j) {
-        const bool m = (key[j] >> kSelShift) == b0;
-        const uint64_t bm = __ballot(m);
-        if (m) sm.list[run + lane_rank(bm)] = key[j];
-        run += __popcll(bm);
-      }
-      for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0u;
-      __syncthreads();
-      const int nl = (int)sm.n_list;
-      // bits 19..9 of the listed keys
-      for (int i = tid; i < nl; i += kTopkThreads) atomicAdd(&sm.hist[(sm.list[i] >> 9) & (kBins - 1)], 1u);
-      __syncthreads();
-      find_bin_dpp(sm.hist[kBins - 1 - 2 * tid], sm.hist[kBins - 2 - 2 * tid], krem, sm);
-      const uint32_t b1 = sm.digit;
-      krem -= sm.above;
-      for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0u;
-      __syncthreads();
-      // bits 8..0 of the listed keys that share bits 19..9
-      for (int i = tid; i < nl; i += kTopkThreads) {
-        const uint32_t u = sm.list[i];
-        if (((u >> 9) & (kBins - 1)) == b1) atomicAdd(&sm.hist[u & 511u], 1u);
-      }
-      __syncthreads();
-      find_bin_dpp(sm.hist[kBins - 1 - 2 * tid], sm.hist[kBins - 2 - 2 * tid], krem, sm);
-      const uint32_t b2 = sm.digit;
-      krem -= sm.above;
-      thr = (b0 << kSelShift) | (b1 << 9) | b2;
-      n_eq = sm.hist[b2];
-      // this wavefront's listed keys above and equal to the threshold
-      uint32_t g = 0, e = 0;
-      for (uint32_t i = lane; i < cnt; i += 64) {
-        const uint32_t u = sm.list[run0 + i];
-        g += u > thr ? 1u : 0u;
-        e += u == thr ? 1u : 0u;
-      }
-      const uint32_t ge = wave_total((e << 16) | g);
-      cgt += ge & 0xffffu;
-      ceq = ge >> 16;
+      src[u] = (uint32_t)j * kAggChunk + sm.cab[j] + (uint32_t)p - sm.coff[j];
     }
-    if (lane == 0) {
-      sm.wgt[wave] = cgt;
-      sm.weq[wave] = ceq;
-    }
-    __syncthreads();
-    uint32_t gt_before = 0, eq_before = 0;
+    const uint32_t *hs = skey + hk * n_chunks * kAggChunk;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-      gt_before += (w < wave) ? sm.wgt[w] : 0u;
-      eq_before += (w < wave) ? sm.weq[w] : 0u;
-    }
-    launder(key);
-    uint32_t pos = gt_before + min(eq_before, krem);
-    char *outb = reinterpret_cast<char *>(out);
-    if (krem == n_eq) {
-      // every key equal to the threshold is kept: the keys at or above it
-      // (with every candidate taken, the threshold is -1 as a signed int)
+    for (int u = 0; u < kCopyBatch; ++u) v[u] = hs[src[u]];
+    if (!in_regs) {
 #pragma unroll
-      for (int j = 0; j < kTkKeys; ++j) {
-        const bool sel = (int)key[j] >= (int)thr;
-        const uint64_t ms = __ballot(sel);
-        const uint32_t p = pos + lane_rank(ms);
-        if (sel && p < (uint32_t)k) *reinterpret_cast<int32_t *>(outb + p * 4u) = base + 64 * j;
-        pos += __popcll(ms);
-      }
-    } else {
-      // only the first krem keys equal to the threshold, in block order
-      uint32_t eq_run = eq_before;
-#pragma unroll
-      for (int j = 0; j < kTkKeys; ++j) {
-        const bool gt = (int)key[j] > (int)thr;
-        const bool eq = key[j] == thr;
-        const uint64_t em = __ballot(eq);
-        const bool sel = gt || (eq && eq_run + lane_rank(em) < krem);
-        eq_run += __popcll(em);
-        const uint64_t ms = __ballot(sel);
-        const uint32_t p = pos + lane_rank(ms);
-        if (sel && p < (uint32_t)k) *reinterpret_cast<int32_t *>(outb + p * 4u) = base + 64 * j;
-        pos += __popcll(ms);
+      for (int u = 0; u < kCopyBatch; ++u) {
+        const int p = p0 + u * kTopkThreads + tid;
+        if (p < nl) sm.list[p] = v[u];
       }
     }
   }
-  const int r0 = meta.r_start.v[sl], n_rec = meta.n_all.v[sl] - r0;
-  for (int j = tid; j < n_list - k; j += kTopkThreads) out[k + j] = (j < n_rec) ? r0 + j : -1;
+  // visits every listed key once: f(key, list position)
+  auto for_each_listed = [&](auto f) {
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kCopyBatch; ++u) {
+        const int p = u * kTopkThreads + tid;
+        if (p < nl) f(v[u], p);
+      }
+    } else {
+      for (int p = tid; p < nl; p += kTopkThreads) f(sm.list[p], p);
+    }
+  };
+  if (!in_regs) __syncthreads();                       // the list in LDS
+  // bits 19..9 of the listed keys
+  for_each_listed([&](uint32_t u, int) { atomicAdd(&sm.hist[(u >> 9) & (kBins - 1)], 1u); });
+  __syncthreads();
+  find_bin_dpp(sm.hist[kBins - 1 - 2 * tid], sm.hist[kBins - 2 - 2 * tid], krem, sm);
+  const uint32_t b1 = sm.digit;
+  krem -= sm.above;
+  // bits 8..0 of the listed keys that share bits 19..9
+  for_each_listed([&](uint32_t u, int) {
+    if (((u >> 9) & (kBins - 1)) == b1) atomicAdd(&sm.hist2[u & 511u], 1u);
+  });
+  __syncthreads();
+  find_bin_dpp(sm.hist2[kBins - 1 - 2 * tid], sm.hist2[kBins - 2 - 2 * tid], krem, sm);
+  const uint32_t b2 = sm.digit;
+  krem -= sm.above;                                    // keys equal to the threshold that are taken
+  const uint32_t thr = (b0 << kSelShift) | (b1 << 9) | b2;
+  const uint32_t n_eq = sm.hist2[b2];
+
+  // This chunk's kept blocks in block order.  Its first list position is
+  // the keys above b0 in earlier chunks plus their boundary keys that are
+  // kept (the listed keys before position coff[ci]).
+  const int lim = (int)sm.coff[ci];
+  uint32_t p;
+  bool sel;
+  if (krem == n_eq) {
+    // every key equal to the threshold is kept: one scan, whose low half
+    // places this chunk's kept keys and whose high half's total counts the
+    // earlier chunks' kept boundary keys (each at most kTile)
+    uint32_t c = 0;
+    for_each_listed([&](uint32_t u, int q) { c += (q < lim && u >= thr) ? 1u : 0u; });
+    sel = valid && key >= thr;
+    uint32_t tot;
+    const uint32_t ex = wg_excl_scan((c << 16) | (sel ? 1u : 0u), sm.wsum, tot);
+    p = sm.before_above + (tot >> 16) + (ex & 0xffffu);
+  } else {
+    // only the first krem keys equal to the threshold, in block order
+    uint32_t g = 0, e = 0;
+    for_each_listed([&](uint32_t u, int q) {
+      if (q < lim) {
+        g += u > thr ? 1u : 0u;
+        e += u == thr ? 1u : 0u;
+      }
+    });
+    uint32_t ge;
+    wg_excl_scan((e << 16) | g, sm.wsum, ge);          // each count at most kTile / 2 per half
+    const uint32_t gt_before = ge & 0xffffu, eq_before = ge >> 16;
+    const bool eq = valid && key == thr;
+    uint32_t n_eq_chunk, n_sel;
+    const uint32_t eq_rank = eq_before + wg_excl_scan(eq ? 1u : 0u, sm.wsum, n_eq_chunk);
+    sel = (valid && key > thr) || (eq && eq_rank < krem);
+    p = sm.before_above + gt_before + min(eq_before, krem) + wg_excl_scan(sel ? 1u : 0u, sm.wsum, n_sel);
+  }
+  if (sel && p < (uint32_t)k) out[p] = b;
 }
 
 __device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
@@ -506,12 +537,18 @@ constexpr int kAggRowsPerPass = 8;    // rows whose scores a thread holds at onc
 // rows per pass measured slower at 32 query rows per KV head.)  The candidates' A are
 // counted by top digit in LDS and the non-empty bins added to the selection
 // histogram with one global atomic each (the histogram was cleared by the
-// scorer earlier in the same call).
+// scorer earlier in the same call).  A scan of the chunk's counts in
+// descending digit order gives its counts at or above every digit and each
+// digit's first position; the keys are then grouped by digit in LDS (in any
+// order inside a digit) and written out as one run.
 __global__ __launch_bounds__(kAggChunk) void k_aggregate(const float *__restrict__ scores,
                                                          const float2 *__restrict__ part, float *__restrict__ A,
-                                                         uint32_t *__restrict__ hist, SessI32 n_blocks,
+                                                         uint32_t *__restrict__ hist, uint32_t *__restrict__ skey,
+                                                         uint16_t *__restrict__ sincl, SessI32 n_blocks,
                                                          SessI32 n_cand, int s0, ScoreGeom g, ScoreSplit sp) {
   __shared__ uint32_t shist[kBins];
+  __shared__ uint32_t swsum[kTopkWaves];
+  __shared__ uint32_t sgrouped[kAggChunk];
   __shared__ float sM[kAggRowsPerPass];
   __shared__ float sInvZ[kAggRowsPerPass];
   const int sl = blockIdx.z;
@@ -567,38 +604,60 @@ __global__ __launch_bounds__(kAggChunk) void k_aggregate(const float *__restrict
   }
 
   if (valid) A[((size_t)s * g.Hkv + h) * g.max_blocks + b] = acc;
-  if (b < nc) atomicAdd(&shist[(__float_as_uint(acc) >> kSelShift) & (kBins - 1)], 1u);
+  const uint32_t key = __float_as_uint(acc) & kKeyMask;
+  const uint32_t digit = key >> kSelShift;
+  if (b < nc) atomicAdd(&shist[digit], 1u);
   __syncthreads();
   for (int i = tid; i < kBins; i += kAggChunk) {
     const uint32_t c = shist[i];
     if (c) atomicAdd(&gh[i], c);
   }
+  // thread t: digits kBins-1-2t and kBins-2-2t
+  const uint32_t c0 = shist[kBins - 1 - 2 * tid], c1 = shist[kBins - 2 - 2 * tid];
+  uint32_t n_in;
+  const uint32_t above = wg_excl_scan(c0 + c1, swsum, n_in);   // (its barriers order the reads above)
+  const size_t chunk = ((size_t)s * g.Hkv + h) * sel_chunks(g.max_blocks) + blockIdx.x;
+  // counts at or above digits kBins-2-2t (low half) and kBins-1-2t (high half)
+  reinterpret_cast<uint32_t *>(sincl + chunk * kSelBins)[(kBins - 2) / 2 - tid] =
+      (above + c0 + c1) | ((above + c0) << 16);
+  shist[kBins - 1 - 2 * tid] = above;
+  shist[kBins - 2 - 2 * tid] = above + c0;
+  __syncthreads();
+  if (b < nc) sgrouped[atomicAdd(&shist[digit], 1u)] = key;
+  __syncthreads();
+  if (tid < (int)n_in) skey[chunk * kAggChunk + tid] = sgrouped[tid];
 }
 
 }  // namespace
 
-hipError_t launch_topk(const float *A, const uint32_t *hist, int32_t *view_blocks, const TopkMeta &meta, int s0,
-                       int n_sess, int Hkv, int max_blocks, int n_list, hipStream_t st) {
-  dim3 grid((unsigned)Hkv, (unsigned)n_sess);
+hipError_t launch_topk(const float *A, const uint32_t *hist, const uint32_t *skey, const uint16_t *sincl,
+                       int32_t *view_blocks, const TopkMeta &meta, int s0, int n_sess, int Hkv, int max_blocks,
+                       int n_list, hipStream_t st) {
   int max_nc = 0;
   for (int i = 0; i < n_sess; ++i) max_nc = meta.n_cand.v[i] > max_nc ? meta.n_cand.v[i] : max_nc;
-  if (hist != nullptr && max_nc <= kTile)
-    hipLaunchKernelGGL(k_topk_tile, grid, dim3(kTopkThreads), 0, st, A, hist, view_blocks, meta, s0, Hkv, max_blocks,
-                       n_list);
-  else
+  if (hist != nullptr && max_nc <= kTile) {
+    // the first chunk's workgroup always runs (it writes the recent blocks)
+    const int nch = max_nc > 0 ? (max_nc + kAggChunk - 1) / kAggChunk : 1;
+    dim3 grid((unsigned)nch, (unsigned)Hkv, (unsigned)n_sess);
+    hipLaunchKernelGGL(k_topk_chunk, grid, dim3(kTopkThreads), 0, st, A, hist, skey, sincl, view_blocks, meta, s0,
+                       Hkv, max_blocks, sel_chunks(max_blocks), n_list);
+  } else {
+    dim3 grid((unsigned)Hkv, (unsigned)n_sess);
     hipLaunchKernelGGL(k_topk, grid, dim3(kTopkThreads), 0, st, A, hist, view_blocks, meta, s0, Hkv, max_blocks,
                        n_list);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, uint32_t *hist,
-                            const SessI32 &n_blocks, const SessI32 &n_cand, int s0, int n_sess, const ScoreGeom &g,
-                            const ScoreSplit &split, hipStream_t st) {
+hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, uint32_t *hist, uint32_t *skey,
+                            uint16_t *sincl, const SessI32 &n_blocks, const SessI32 &n_cand, int s0, int n_sess,
+                            const ScoreGeom &g, const ScoreSplit &split, hipStream_t st) {
   int max_nb = 0;
   for (int i = 0; i < n_sess; ++i) max_nb = n_blocks.v[i] > max_nb ? n_blocks.v[i] : max_nb;
   if (max_nb == 0) return hipSuccess;
   dim3 grid((unsigned)((max_nb + kAggChunk - 1) / kAggChunk), (unsigned)g.Hkv, (unsigned)n_sess);
-  hipLaunchKernelGGL(k_aggregate, grid, dim3(kAggChunk), 0, st, scores, part, A, hist, n_blocks, n_cand, s0, g, split);
+  hipLaunchKernelGGL(k_aggregate, grid, dim3(kAggChunk), 0, st, scores, part, A, hist, skey, sincl, n_blocks, n_cand,
+                     s0, g, split);
   return hipGetLastError();
 }
 

@@ -82,7 +82,7 @@ bool long_chunk(const kvmem_geom *g, int T) {
 // softmax statistics, A.  Long chunks: query operands, per-(row, block group)
 // statistics, per-row log-sum-exp, A.
 struct ScoreScratch {
-  size_t scores, part, agg, qf, lse, hist, total;
+  size_t scores, part, agg, qf, lse, hist, skey, sincl, total;
 };
 ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   ScoreScratch r;
@@ -94,7 +94,7 @@ ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
     r.qf = align_up(L.part_bytes);
     r.lse = r.qf + align_up(L.qf_bytes);
     r.agg = r.lse + align_up(L.lse_bytes);
-    r.hist = 0;
+    r.hist = r.skey = r.sincl = 0;
     r.total = r.agg + a_bytes;
     return r;
   }
@@ -105,7 +105,11 @@ ScoreScratch score_scratch(const kvmem_geom *g, int S, int max_blocks, int T) {
   r.agg = r.part + align_up(rows * n_slots * sizeof(float2));
   r.qf = r.lse = r.agg;
   r.hist = r.agg + a_bytes;
-  r.total = r.hist + align_up((size_t)S * g->n_kv_heads * kSelBins * sizeof(uint32_t));
+  // each aggregation chunk's keys grouped by top digit, and its counts per digit
+  const size_t chunks = (size_t)S * g->n_kv_heads * sel_chunks(max_blocks);
+  r.skey = r.hist + align_up((size_t)S * g->n_kv_heads * kSelBins * sizeof(uint32_t));
+  r.sincl = r.skey + align_up(chunks * kAggChunk * sizeof(uint32_t));
+  r.total = r.sincl + align_up(chunks * kSelBins * sizeof(uint16_t));
   return r;
 }
 
@@ -310,12 +314,14 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
                                              (float *)(base + sc.lse), A, scores_opt, nb, s0, n, g, hs))) != KVMEM_OK)
         return st;
       if (n_list > 0 &&
-          (st = hip_status(launch_topk(A, nullptr, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
+          (st = hip_status(launch_topk(A, nullptr, nullptr, nullptr, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks,
+                                       n_list, hs))) != KVMEM_OK)
         return st;
     } else if (max_nb == 0) {
       // nothing to score: the lists hold the recent (partial) blocks only
       if (n_list > 0 &&
-          (st = hip_status(launch_topk(A, nullptr, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) != KVMEM_OK)
+          (st = hip_status(launch_topk(A, nullptr, nullptr, nullptr, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks,
+                                       n_list, hs))) != KVMEM_OK)
         return st;
     } else {
       // the scorer clears this launch's selection histograms, the aggregation
@@ -332,11 +338,13 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
               ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs)
               : launch_score_r8(index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs);
       if ((st = hip_status(e)) != KVMEM_OK) return st;
-      if ((st = hip_status(launch_aggregate(scores, part, A, hist, nb, tm.n_cand, s0, n, g, split, hs))) != KVMEM_OK)
+      uint32_t *skey = (uint32_t *)(base + sc.skey);
+      uint16_t *sincl = (uint16_t *)(base + sc.sincl);
+      if ((st = hip_status(launch_aggregate(scores, part, A, hist, skey, sincl, nb, tm.n_cand, s0, n, g, split, hs))) !=
+          KVMEM_OK)
         return st;
-      if (n_list > 0 &&
-          (st = hip_status(launch_topk(A, hist, view_blocks, tm, s0, n, g.Hkv, ws->max_blocks, n_list, hs))) !=
-              KVMEM_OK)
+      if (n_list > 0 && (st = hip_status(launch_topk(A, hist, skey, sincl, view_blocks, tm, s0, n, g.Hkv,
+                                                     ws->max_blocks, n_list, hs))) != KVMEM_OK)
         return st;
     }
   }

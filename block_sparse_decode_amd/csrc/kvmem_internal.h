@@ -105,14 +105,22 @@ struct TopkMeta {
 
 // A for every complete block of the scored sessions, and the candidates
 // (blocks below n_cand) counted into hist[(s * Hkv + h) * kSelBins + digit]
-// (cleared by the scorer of the same call).
-hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, uint32_t *hist,
-                            const SessI32 &n_blocks, const SessI32 &n_cand, int s0, int n_sess, const ScoreGeom &g,
-                            const ScoreSplit &split, hipStream_t st);
+// (cleared by the scorer of the same call).  Per chunk c of kAggChunk blocks
+// of a (session, KV head), c < sel_chunks(max_blocks), the chunk's candidate
+// keys (A's bits without the sign bit) are also written grouped by digit,
+// highest digit first, to skey[((s * Hkv + h) * n_chunks + c) * kAggChunk
+// ...], and the number of its candidates whose digit is >= b to
+// sincl[((s * Hkv + h) * n_chunks + c) * kSelBins + b].
+hipError_t launch_aggregate(const float *scores, const float2 *part, float *A, uint32_t *hist, uint32_t *skey,
+                            uint16_t *sincl, const SessI32 &n_blocks, const SessI32 &n_cand, int s0, int n_sess,
+                            const ScoreGeom &g, const ScoreSplit &split, hipStream_t st);
+__host__ __device__ constexpr int sel_chunks(int max_blocks) { return (max_blocks + kAggChunk - 1) / kAggChunk; }
 
-// Selection from A; hist: the candidates' selection histograms, or null.
-hipError_t launch_topk(const float *A, const uint32_t *hist, int32_t *view_blocks, const TopkMeta &meta, int s0,
-                       int n_sess, int Hkv, int max_blocks, int n_list, hipStream_t st);
+// Selection from A; hist, skey, sincl: the aggregation's selection histograms
+// and grouped keys, or all null.
+hipError_t launch_topk(const float *A, const uint32_t *hist, const uint32_t *skey, const uint16_t *sincl,
+                       int32_t *view_blocks, const TopkMeta &meta, int s0, int n_sess, int Hkv, int max_blocks,
+                       int n_list, hipStream_t st);
 
 // --- materialise ------------------------------------------------------------------
 hipError_t launch_materialize(int bf16, const void *k_pool, const void *v_pool, const int32_t *table,
