@@ -263,11 +263,31 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
         }
 #pragma unroll
       for (int c = 0; c < 4; ++c) ka[tt][c] = as_bf16x8(make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]));
-      if (WV) {   // the view's K row of token u: dims 32c + 8qq .. + 7 from this lane
-        uint16_t *row = kview + (((size_t)s * g.Hkv + h) * max_view + tb + u) * kD + 8 * qq;
+      if (WV) {
+        // The view's K rows 16tt .. 16tt + 15: this lane holds dims 32c + 8qq
+        // .. + 7 of row u (16 bytes at byte 64c + 16qq).  Whole 128-byte lines
+        // per store: half hf of a row (bytes 128hf ..) is pieces c = 2hf and
+        // 2hf + 1 of its four qq lanes.  Lanes col and col ^ 8 swap their
+        // pieces 2hf + 1 (DPP row_ror:8), then one store writes half hf of
+        // rows 0..7 (col < 8: own piece 2hf; col >= 8: the partner's piece
+        // 2hf + 1 of row col - 8) and the other half hf of rows 8..15.
+        // (Written as 64-byte runs per store the K stream cost ~15 us more at
+        // 1M tokens.)
+        uint16_t *blk = kview + (((size_t)s * g.Hkv + h) * max_view + tb + 16 * tt) * kD + 8 * qq;
+        const bool lo = col < 8;
+        const int r_own = col, r_rcv = col ^ 8;          // rows of the own and the received piece
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          store_nt16(row + 32 * c, make_uint4(w[c][0], w[c][1], w[c][2], w[c][3]));
+        for (int hf = 0; hf < 2; ++hf) {
+          uint32_t x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[2 * hf + 1][e], kDppRor8, 0xf, 0xf, false);
+          const uint4 own = make_uint4(w[2 * hf][0], w[2 * hf][1], w[2 * hf][2], w[2 * hf][3]);
+          const uint4 rcv = make_uint4(x[0], x[1], x[2], x[3]);
+          // rows 0..7, then rows 8..15
+          store_nt16(blk + (lo ? r_own : r_rcv) * kD + 32 * (lo ? 2 * hf : 2 * hf + 1), lo ? own : rcv);
+          store_nt16(blk + (lo ? r_rcv : r_own) * kD + 32 * (lo ? 2 * hf + 1 : 2 * hf), lo ? rcv : own);
+        }
       }
     }
     // the next K tile: writing the view, as soon as the rotation has freed its
