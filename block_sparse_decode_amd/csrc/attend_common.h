@@ -13,6 +13,42 @@ constexpr int kQprepMaxT = 32;                          // query tokens per step
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// K tiles read as whole 128-byte lines.  The matrix-core A operand of a
+// 16-token K tile (256-byte rows) puts 16-byte piece c (dims 32c + 8qq .. +
+// 7) of row col in lane (qq, col); loaded that way, each instruction reads
+// 64-byte halves of 16 rows.  Here the two instructions of half hf of the row
+// (pieces 2hf, 2hf + 1) each read 8 whole rows: lanes col < 8 and col + 8
+// (same qq) take the two pieces of one line.
+//   r[2hf]     : piece 2hf of row col (col < 8), piece 2hf + 1 of row col - 8
+//   r[2hf + 1] : piece 2hf + 1 of row col + 8 (col < 8), piece 2hf of row col
+// rows: the tile's first row.
+__device__ __forceinline__ void load_k_lines(uint4 (&r)[4], const uint16_t *rows, int qq, int col) {
+  const bool lo = col < 8;
+  const int ra = lo ? col : col - 8, rb = lo ? col + 8 : col;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    r[2 * hf] = load_nt16(rows + (size_t)ra * kD + 32 * (lo ? 2 * hf : 2 * hf + 1) + 8 * qq);
+    r[2 * hf + 1] = load_nt16(rows + (size_t)rb * kD + 32 * (lo ? 2 * hf + 1 : 2 * hf) + 8 * qq);
+  }
+}
+
+// The A operand of row col from load_k_lines' registers: the own piece 2hf
+// stays, piece 2hf + 1 comes from lane col ^ 8 (DPP row_ror:8), which holds
+// it for this lane.
+__device__ __forceinline__ void k_lines_operand(const uint4 (&r)[4], uint4 (&a)[4], int col) {
+  const bool lo = col < 8;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const uint4 own = lo ? r[2 * hf] : r[2 * hf + 1];
+    const uint4 send = lo ? r[2 * hf + 1] : r[2 * hf];
+    a[2 * hf] = own;
+    a[2 * hf + 1] = make_uint4((uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.x, kDppRor8, 0xf, 0xf, false),
+                               (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.y, kDppRor8, 0xf, 0xf, false),
+                               (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.z, kDppRor8, 0xf, 0xf, false),
+                               (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.w, kDppRor8, 0xf, 0xf, false));
+  }
+}
+
 
 // Query operands of the matrix-core products for the 16 rows of operand set nt:
 // q~ (RMSNorm, weight), RoPE at V + t, scaled by log2(e)/sqrt(d), split into

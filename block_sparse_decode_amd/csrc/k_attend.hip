@@ -31,17 +31,14 @@ namespace kvmem {
 namespace {
 
 struct KVTile {
-  uint4 k[2][4];
+  uint4 k[2][4];     // as load_k_lines leaves them (whole 128-byte lines per load)
   uint4 v[8];
 };
 
 __device__ __forceinline__ void load_kv_tile(KVTile &t, const uint16_t *kbase, const uint16_t *vbase, int tb,
                                              int qq, int col) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      t.k[tt][c] = load_nt16(kbase + (size_t)(tb + 16 * tt + col) * kD + 32 * c + 8 * qq);
+  for (int tt = 0; tt < 2; ++tt) load_k_lines(t.k[tt], kbase + (size_t)(tb + 16 * tt) * kD, qq, col);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) t.v[dt] = load_nt16(vbase + ((size_t)(tb >> 5) * kD + 16 * dt + col) * kBT + 8 * qq);
 }
@@ -50,20 +47,23 @@ __device__ __forceinline__ void load_kv_tile(KVTile &t, const uint16_t *kbase, c
 template <int NT>
 __device__ __forceinline__ void attend_tile(const KVTile &t, const bf16x8 (&qhi)[NT][4], const bf16x8 (&qlo)[NT][4],
                                             floatx4 (&o)[NT][8], float (&mrun)[NT], float (&lrun)[NT], int tb, int V,
-                                            int qq) {
+                                            int qq, int col) {
   floatx4 sc[2][NT];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < 2; ++tt) {
+    uint4 ka[4];
+    k_lines_operand(t.k[tt], ka, col);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       floatx4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[tt][c]), qhi[nt][c], a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[tt][c]), qlo[nt][c], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[c]), qhi[nt][c], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[c]), qlo[nt][c], a, 0, 0, 0);
       }
       sc[tt][nt] = a;
     }
+  }
   if (tb + kBT > V) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void k_attend_bf16(
   // slower on this part: the stream runs best with each wavefront walking its
   // run one tile deep.)
   for (int tb = tok0; tb < tok1; tb += kBT) {
-    attend_tile<NT>(tile, qhi, qlo, o, mrun, lrun, tb, V, qq);
+    attend_tile<NT>(tile, qhi, qlo, o, mrun, lrun, tb, V, qq, col);
     if (tb + kBT < tok1) {
       load_kv_tile(tile, kbase, vbase, tb + kBT, qq, col);
       // keep all 16 K and V loads of the tile together (the scheduler would

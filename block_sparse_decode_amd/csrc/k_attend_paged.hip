@@ -138,13 +138,24 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   };
   uint4 kr[2][4], vr[2][4];
   bool ok;
+  constexpr bool kKOperandLoads = WV || NT > 1;          // K loaded in the A-operand layout
   auto load_k = [&](int m) {
     bool okm;
     const size_t base = tile_base(m, okm);
+    // Without the view and with one row tile: whole 128-byte lines
+    // (load_k_lines; k_lines_operand before use), 190 -> 186 us per call at
+    // 1M tokens.  Writing the view, or with two row tiles, the operand layout
+    // directly: there the exchange's registers made the kernel spill more
+    // (one-pass call 447 -> 456 us at 1M tokens).
+    if (kKOperandLoads) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(kpool + base + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+        for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(kpool + base + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) load_k_lines(kr[tt], kpool + base + (size_t)(16 * tt) * kD, qq, col);
+    }
   };
   // V goes through LDS, so its loads take whole rows: instruction j, lane l
   // reads token 4j + l / 16, dims 8 (l % 16) .. + 7 (full 128-byte lines)
@@ -236,10 +247,17 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int u = 16 * tt + col;
+      uint4 kop[4];
+      if (kKOperandLoads) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kop[c] = kr[tt][c];
+      } else {
+        k_lines_operand(kr[tt], kop, col);
+      }
       float kv[4][8];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint4 r = and_mask(kr[tt][c], keep[tt]);
+        const uint4 r = and_mask(kop[c], keep[tt]);
         const uint32_t e[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
