@@ -503,10 +503,9 @@ __global__ __launch_bounds__(512) void k_mass_bf16(const uint16_t *__restrict__ 
   uint4 kr[2][4];
   bool ok_cur;
   const uint16_t *src = tile_src(b0, ok_cur);
+  // (whole 128-byte lines: load_k_lines, then k_lines_operand)
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(src + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+  for (int tt = 0; tt < 2; ++tt) load_k_lines(kr[tt], src + (size_t)(16 * tt) * kD, qq, col);
 
   // RoPE table of the current block's positions, shared by the 8 heads: each
   // thread owns 4 of its 32 x 64 entries, exact at the chunk's first block
@@ -540,15 +539,11 @@ __global__ __launch_bounds__(512) void k_mass_bf16(const uint16_t *__restrict__ 
     if (!ok && head_ok && lane == 0) dev_flag(dev_err, 1);
     uint4 cur[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) cur[tt][c] = kr[tt][c];
+    for (int tt = 0; tt < 2; ++tt) k_lines_operand(kr[tt], cur[tt], col);
     if (beta + 1 < b1) {
       src = tile_src(beta + 1, ok_cur);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kr[tt][c] = load_nt16(src + (size_t)(16 * tt + col) * kD + 32 * c + 8 * qq);
+      for (int tt = 0; tt < 2; ++tt) load_k_lines(kr[tt], src + (size_t)(16 * tt) * kD, qq, col);
     }
     if (!ok) continue;                                 // per wavefront: no barrier below
     // rotate K at its own positions and round to bf16: A operands
