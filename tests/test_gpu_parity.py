@@ -187,6 +187,13 @@ SMALL = {
                             k=1, R=3, n_planted=1, seed=67),
     "select_all_but_one": small_cfg("select_all_but_one", "bf16", S=1, Hq=16, Hkv=2, n_tokens=(32 * 60 + 3,),
                                     k=58, R=2, n_planted=4, seed=68),
+    # chunk edges of the chunk-parallel selection (1024 candidates per chunk):
+    # one candidate in the last chunk, and whole chunks only
+    "select_chunk_plus_one": small_cfg("select_chunk_plus_one", "bf16", S=1, Hq=16, Hkv=2,
+                                       n_tokens=(32 * 1029 + 5,), k=300, R=5, n_planted=40, seed=71),
+    "select_three_chunks": small_cfg("select_three_chunks", "bf16", S=2, Hq=16, Hkv=2,
+                                     n_tokens=(32 * (3072 + 2), 32 * 2048 + 31), k=1500, R=2, n_planted=40,
+                                     seed=72),
     # exactly one full 32768-key selection tile (no padding keys), and one key
     # more (the multi-tile selection kernel)
     "full_select_tile": small_cfg("full_select_tile", "bf16", S=1, Hq=4, Hkv=1, n_tokens=(32 * (32768 + 4),),
