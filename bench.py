@@ -50,9 +50,9 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
 # taken on (sha256 over block_sparse_decode_amd/csrc/* and build.py); otherwise reported null.
-COUNTER_SOURCES_SHA = "a6bb8b2ca48e6860701ba2fc66efc20bd90d1956a3843f2b8184635b91ec6a25"
-MEASURED_TRAFFIC = {"build_index_full": 2.216e9, "materialize_attend": 2.173e9, "materialize": 2.156e9,
-                    "attend": 1.083e9, "score_select": 9.215e7}
+COUNTER_SOURCES_SHA = "654aeff5920c99fadcefd7ff8e79a00b492f543aac3e01db19760d919cc1b5a9"
+MEASURED_TRAFFIC = {"build_index_full": 2.216e+09, "materialize_attend": 2.173e+09, "materialize": 2.156e+09,
+                    "attend": 1.083e+09, "score_select": 9.208e+07}
 
 
 def kernel_sources_sha() -> str:

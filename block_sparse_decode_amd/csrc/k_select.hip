@@ -527,7 +527,6 @@ __device__ __forceinline__ float2 merge_ml(float2 a, float2 b) {
 }
 
 constexpr int kAggRowsPerPass = 8;    // rows whose scores a thread holds at once
-constexpr int kAggSlotBatch = 4;      // statistics slots a lane requests at once
 
 // One workgroup per (session, KV head, kAggChunk blocks); thread t owns block
 // b0 + t.  Rows are taken eight at a time: every thread first requests its
@@ -568,52 +567,29 @@ __global__ __launch_bounds__(kAggChunk) void k_aggregate(const float *__restrict
   for (int i = tid; i < kBins; i += kAggChunk) shist[i] = 0u;
   float acc = 0.f;
 
-  static_assert(kAggRowsPerPass <= kAggChunk / 64, "one row per wavefront and pass");
-  const int bl = min(b, nb - 1);                       // past the history: a valid block, unused
   for (int rb = 0; rb < n_rows; rb += kAggRowsPerPass) {
     const int nr = min(kAggRowsPerPass, n_rows - rb);
-    // wavefront w < nr merges row rb + w: the statistics slots of the
-    // scoring wavefronts that met the row's key, in order.  Its first
-    // kAggSlotBatch slots per lane are requested before the scores, so the
-    // two round trips overlap (past the last slot: the last again).
-    const bool has_row = wave < nr;
-    const int rw = rb + (has_row ? wave : 0);
-    const size_t wrow = ((size_t)s * g.Tq + rw / g.G) * g.Hq + (size_t)h * g.G + rw % g.G;
-    const int n_slots = score_n_slots((sl * sp.n_rg + rw / sp.rpg) * g.Hkv + h, sp);
-    const float2 *ps = part + wrow * g.slot_stride;
-    float2 v[kAggSlotBatch];
-    if (has_row) {
-#pragma unroll
-      for (int u = 0; u < kAggSlotBatch; ++u) v[u] = ps[min(u * 64 + lane, n_slots - 1)];
-    }
-    // (all kAggRowsPerPass requested, rows past the pass's last repeating
-    // it, so that the waits for the slots above count exactly)
     float sv[kAggRowsPerPass];
 #pragma unroll
     for (int rr = 0; rr < kAggRowsPerPass; ++rr) {
-      const int r = rb + min(rr, nr - 1);
+      if (rr >= nr) break;
+      const int r = rb + rr;
       const size_t row_id = ((size_t)s * g.Tq + r / g.G) * g.Hq + (size_t)h * g.G + r % g.G;
-      sv[rr] = scores[row_id * g.max_blocks + bl];
+      sv[rr] = valid ? scores[row_id * g.max_blocks + b] : 0.f;
     }
-    if (has_row) {
-      // each lane folds slots lane, lane + 64, ... in order; a repeated slot
-      // folds as the empty pair (-inf, 0), which leaves the fold's bits
-      // unchanged (and every load is consumed, so none is left in flight)
-      const float2 none = make_float2(-INFINITY, 0.f);
-      float2 ml = none;
-#pragma unroll
-      for (int u = 0; u < kAggSlotBatch; ++u) ml = merge_ml(ml, u * 64 + lane < n_slots ? v[u] : none);
-      for (int c0 = kAggSlotBatch * 64; c0 < n_slots; c0 += kAggSlotBatch * 64) {
-#pragma unroll
-        for (int u = 0; u < kAggSlotBatch; ++u) v[u] = ps[min(c0 + u * 64 + lane, n_slots - 1)];
-#pragma unroll
-        for (int u = 0; u < kAggSlotBatch; ++u) ml = merge_ml(ml, c0 + u * 64 + lane < n_slots ? v[u] : none);
-      }
+    for (int rw = wave; rw < nr; rw += kAggChunk / 64) {
+      const int r = rb + rw;
+      const size_t row_id = ((size_t)s * g.Tq + r / g.G) * g.Hq + (size_t)h * g.G + r % g.G;
+      // the scoring wavefronts that met this row's key, in order
+      const int key = (sl * sp.n_rg + r / sp.rpg) * g.Hkv + h;
+      const int n_slots = score_n_slots(key, sp);
+      float2 ml = make_float2(-INFINITY, 0.f);
+      for (int c = lane; c < n_slots; c += 64) ml = merge_ml(ml, part[row_id * g.slot_stride + c]);
       const float M = wave_max_dpp(ml.x);
       const float Z = wave_sum_dpp(ml.x == -INFINITY ? 0.f : ml.y * expf(ml.x - M));
       if (lane == 0) {
-        sM[wave] = M;
-        sInvZ[wave] = 1.0f / Z;
+        sM[rw] = M;
+        sInvZ[rw] = 1.0f / Z;
       }
     }
     __syncthreads();
@@ -626,27 +602,25 @@ __global__ __launch_bounds__(kAggChunk) void k_aggregate(const float *__restrict
     }
     __syncthreads();
   }
-  if (!valid) acc = 0.f;
 
+  if (valid) A[((size_t)s * g.Hkv + h) * g.max_blocks + b] = acc;
   const uint32_t key = __float_as_uint(acc) & kKeyMask;
   const uint32_t digit = key >> kSelShift;
   if (b < nc) atomicAdd(&shist[digit], 1u);
   __syncthreads();
-  // thread t: digits kBins-1-2t and kBins-2-2t, into the (session, head)'s
-  // histogram.  The global writes go out here, as early as possible so that
-  // they drain while the grouping below runs, but after the first barrier:
-  // ahead of it, the compiler made every wavefront wait there for them.
+  for (int i = tid; i < kBins; i += kAggChunk) {
+    const uint32_t c = shist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+  // thread t: digits kBins-1-2t and kBins-2-2t
   const uint32_t c0 = shist[kBins - 1 - 2 * tid], c1 = shist[kBins - 2 - 2 * tid];
-  if (valid) A[((size_t)s * g.Hkv + h) * g.max_blocks + b] = acc;
-  if (c0) atomicAdd(&gh[kBins - 1 - 2 * tid], c0);
-  if (c1) atomicAdd(&gh[kBins - 2 - 2 * tid], c1);
   uint32_t n_in;
   const uint32_t above = wg_excl_scan(c0 + c1, swsum, n_in);   // (its barriers order the reads above)
   const size_t chunk = ((size_t)s * g.Hkv + h) * sel_chunks(g.max_blocks) + blockIdx.x;
   // counts at or above digits kBins-2-2t (low half) and kBins-1-2t (high half)
   reinterpret_cast<uint32_t *>(sincl + chunk * kSelBins)[(kBins - 2) / 2 - tid] =
       (above + c0 + c1) | ((above + c0) << 16);
-  shist[kBins - 1 - 2 * tid] = above;                  // each digit's first position
+  shist[kBins - 1 - 2 * tid] = above;
   shist[kBins - 2 - 2 * tid] = above + c0;
   __syncthreads();
   if (b < nc) sgrouped[atomicAdd(&shist[digit], 1u)] = key;
