@@ -250,6 +250,32 @@ def test_selection_exact_ties(name):
     _full_check(wl, check_scores=False)
 
 
+# Ties by selection chunk: every block of 1024-block chunk c carries the keys
+# of the chunk's first block, so a head's A takes one value per chunk (the
+# four well apart) and the budget cuts through one chunk's tied class, whose
+# kept blocks are its lowest ones.  For the seed used, head 0 ranks the chunks
+# 1 > 0 > 2 > 3 and head 1 ranks them 1 > 0 > 3 > 2, so k = 1500 cuts inside
+# chunk 0 with the later chunk 1 taken whole, and k = 2500 and 3500 cut inside
+# later chunks after two and three whole ones.
+@pytest.mark.parametrize("k", [1500, 2500, 3500])
+def test_selection_ties_by_chunk(k):
+    _need_gpu()
+    cfg = small_cfg(f"ties_by_chunk_{k}", "bf16", S=1, Hq=16, Hkv=2, n_tokens=(32 * (4096 + 3),), k=k, R=3,
+                    seed=73)
+    wl = make_workload(cfg)
+    tmpl = [wl.block_table[0, 1024 * c] for c in range(4)]
+    for b in range(4096):
+        if b % 1024:
+            wl.k_pool[wl.block_table[0, b]] = wl.k_pool[tmpl[b // 1024]]
+    ws = oracle_ws(wl)
+    index = [O.mean_k_index(ws, 0, h) for h in range(cfg.n_kv_heads)]
+    _, A_all, _ = O.session_scores(ws, 0, wl.q[0], wl.q_norm_w, cfg.eps, index, keep_scores=False)
+    for h in range(cfg.n_kv_heads):
+        v = np.sort([A_all[h][1024 * c] for c in range(4)])
+        assert np.all(np.diff(v) > 1e-3 * v[1:]), (k, h, v)
+    _full_check(wl, check_scores=False)
+
+
 # Every block's keys identical: all candidates tie, all of them fall into the
 # selection's boundary bin (the tile kernel's LDS list holds all 32768), and the
 # kept blocks are the lowest block indices.
