@@ -44,10 +44,6 @@ __device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
     x[2 * k + 1] = bf16_hi(e[k]);
   }
 }
-__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
-  const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
 
 // The 16 A-operand words of a 64-block index tile: a.w[4m + c] is word
 // 4c + qq of block 16m + col (dims 32c + 8qq .. + 7), i.e. A rows = blocks
@@ -65,16 +61,33 @@ __device__ __forceinline__ void load_tile_a(TileA &a, const uint16_t *tile, int 
       a.w[4 * m + c] = load_nt16(tile + ((4 * c + qq) * kIdxTile + 16 * m + col) * 8);
 }
 
+// The same 16 words through a buffer resource over the one tile: the tile's
+// address stays in scalar registers (each lane adds only its own offset), and
+// a resource of no records (`valid` false) answers zeros without a memory
+// access, which keeps a look-ahead past the last tile free.
+__device__ __forceinline__ void load_tile_a_buf(TileA &a, const uint16_t *tile, bool valid, int lane) {
+  const int qq = lane >> 4, col = lane & 15;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void *)tile, (short)0, valid ? kIdxTile * kD * 2 : 0, 0x00020000);
+  const int v = (qq * kIdxTile + col) * 16;              // bytes: word qq of block col
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)                          // + word 4c (c * 4096 bytes) of block 16m + col
+      a.w[4 * m + c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v + m * 256, c * 4096, 2));
+}
+
 // Scores of the T * G query rows of a row group against every index row, on
 // the matrix cores.  Work items and statistics slots are those of the
 // vector-ALU scorer (ScoreSplit, rows per group = 32).  Per item the wavefront
 // computes D[cs][m] = A(blocks 16m..) * B(rows 16cs..): lane (qq, col) holds
 // the scores of blocks 16m + 4qq + i, i < 4, for row 16cs + col.  Running
 // per-lane softmax statistics of its row are merged over the four lanes of a
-// row at the end of each key.  The next tile is requested before the current
-// one is multiplied (two register buffers).
-template <typename TQ>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_score_mfma(const uint16_t *__restrict__ index, const TQ *__restrict__ q,
+// row at the end of each key.  A key's query words and norm weights are
+// requested before its first tile (vector loads return in order, so the
+// operands are built while that tile is in flight), and the next tile is
+// requested before the current one is multiplied (two register buffers).
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_score_mfma(const uint16_t *__restrict__ index, const uint16_t *__restrict__ q,
                                                    const float *__restrict__ qw, float eps,
                                                    float *__restrict__ scores, float2 *__restrict__ part,
                                                    uint32_t *__restrict__ zero, int n_zero,
@@ -86,12 +99,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const int total = sp.n_sess * g.Hkv * sp.n_rg * sp.ntl;
   const int i0 = blockIdx.x * sp.per;                   // < total (grid = ceil(total / per))
   const int i1 = min(total, i0 + sp.per);
+  const bool vec = (g.max_blocks & 3) == 0 && (((uintptr_t)scores) & 15) == 0;
 
   int key, key_r0;
   bf16x8 b[2][4][2];                                    // [cs][c][hi, lo]
   size_t row_id[2];
   bool row_ok[2];
   float m[2], l[2];
+  uint4 qraw[2][4];                                     // the key's query words: row 16cs + col, dims 32k + 8qq ..
+  float4 wraw[4][2];                                    // the norm weights of the same dims
 
   auto tile_of = [&](int item) {
     const ScoreItem it = decode_score_item(item, sp, g.Hkv, n_blocks);
@@ -111,11 +127,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
   };
 
-  // B operands of a key: lane (qq, col) holds dims 32k + 8qq .. + 7 of query
-  // row r0 + 16cs + col, as q~/sqrt(d) split into bf16 hi and lo (rows past
-  // T * G are zero).  The row's mean square is summed over the four lanes
-  // that share it.
-  auto start_key = [&](const ScoreItem &c) {
+  // A key's rows (rows past T * G read row 0 and get zero operands) and the
+  // loads of their words and weights.
+  auto load_key = [&](const ScoreItem &c) {
     key = c.key;
     key_r0 = c.r0;
     const int s = s0 + c.sl;
@@ -127,33 +141,50 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       row_id[cs] = ((size_t)s * g.Tq + rr / g.G) * g.Hq + (size_t)c.h * g.G + rr % g.G;
       m[cs] = -INFINITY;
       l[cs] = 0.f;
-      // two passes over the lane's 32 dims keep few registers live: the
-      // mean square, then the weighted, scaled, split values
-      const TQ *src = q + row_id[cs] * kD + 8 * qq;
+      const uint16_t *src = q + row_id[cs] * kD + 8 * qq;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qraw[cs][k] = *reinterpret_cast<const uint4 *>(src + 32 * k);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      wraw[k][0] = reinterpret_cast<const float4 *>(qw + 32 * k + 8 * qq)[0];
+      wraw[k][1] = reinterpret_cast<const float4 *>(qw + 32 * k + 8 * qq)[1];
+    }
+  };
+
+  // B operands of a key: lane (qq, col) holds dims 32k + 8qq .. + 7 of query
+  // row r0 + 16cs + col, as q~/sqrt(d) split into bf16 hi and lo.  The row's
+  // mean square is summed over the four lanes that share it.
+  auto build_key = [&]() {
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
       float ss = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float x[8];
-        load8(src + 32 * k, x);
+        const uint32_t e[4] = {qraw[cs][k].x, qraw[cs][k].y, qraw[cs][k].z, qraw[cs][k].w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = bf16_lo(e[j]), x1 = bf16_hi(e[j]);
+          ss += x0 * x0;
+          ss += x1 * x1;
+        }
       }
       ss += shfl_xor_f(ss, 16);
       ss += shfl_xor_f(ss, 32);
       const float rs = row_ok[cs] ? (1.0f / sqrtf(ss * (1.0f / kD) + eps)) * 0.08838834764831845f : 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float x[8], w[8];
-        load8(src + 32 * k, x);
-        load8(qw + 32 * k + 8 * qq, w);
+        const uint32_t e[4] = {qraw[cs][k].x, qraw[cs][k].y, qraw[cs][k].z, qraw[cs][k].w};
+        const float w[8] = {wraw[k][0].x, wraw[k][0].y, wraw[k][0].z, wraw[k][0].w,
+                            wraw[k][1].x, wraw[k][1].y, wraw[k][1].z, wraw[k][1].w};
         uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
+        for (int j = 0; j < 4; ++j) {
           uint32_t h0, l0, h1, l1;
-          split_hi_lo(x[j] * rs * w[j], h0, l0);
-          split_hi_lo(x[j + 1] * rs * w[j + 1], h1, l1);
-          hw[j / 2] = h0 | (h1 << 16);
-          lw[j / 2] = l0 | (l1 << 16);
+          split_hi_lo(bf16_lo(e[j]) * rs * w[2 * j], h0, l0);
+          split_hi_lo(bf16_hi(e[j]) * rs * w[2 * j + 1], h1, l1);
+          hw[j] = h0 | (h1 << 16);
+          lw[j] = l0 | (l1 << 16);
         }
         b[cs][k][0] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
         b[cs][k][1] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
@@ -178,8 +209,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         if (row_ok[cs]) {
           const int bb = c.t * kIdxTile + 16 * mm + 4 * qq;
           float *dst = scores + row_id[cs] * g.max_blocks + bb;
-          if (bb + 3 < c.nb && (g.max_blocks & 3) == 0) {
-            *reinterpret_cast<float4 *>(dst) = make_float4(d[0], d[1], d[2], d[3]);   // 16-byte aligned
+          if (vec && bb + 3 < c.nb) {
+            *reinterpret_cast<floatx4 *>(dst) = d;     // 16-byte aligned
           } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -199,22 +230,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
   };
 
-  // One segment per key in the range: the first tile's loads go out, then the
-  // key's query operands are built while they are in flight, then the tiles
-  // stream with one tile of look-ahead.  After the last item the look-ahead
-  // reads the index's first tile (shared by every wavefront, so cached): the
-  // loads stay unconditional without costing HBM traffic.
+  // One segment per key in the range: the key's query words, then the first
+  // tile's loads go out, the key's operands are built while the tile is in
+  // flight, and the tiles stream with one tile of look-ahead.  After the last
+  // item the look-ahead loads from an empty resource: the loads stay
+  // unconditional (so every wait counts exactly) without touching memory.
   for (int it = i0; it < i1;) {
     const ScoreItem c0 = decode_score_item(it, sp, g.Hkv, n_blocks);
     const int end = min(i1, (c0.key + 1) * sp.ntl);
     TileA ta, tb;
-    load_tile_a(ta, tile_of(it), lane);
-    start_key(c0);
+    load_key(c0);
+    load_tile_a_buf(ta, tile_of(it), true, lane);
+    __builtin_amdgcn_sched_barrier(0);                  // every load out before the first wait
+    build_key();
     while (true) {
-      load_tile_a(tb, it + 1 < end ? tile_of(it + 1) : index, lane);
+      load_tile_a_buf(tb, tile_of(min(it + 1, end - 1)), it + 1 < end, lane);
       compute(ta, it);
       if (++it >= end) break;
-      load_tile_a(ta, it + 1 < end ? tile_of(it + 1) : index, lane);
+      load_tile_a_buf(ta, tile_of(min(it + 1, end - 1)), it + 1 < end, lane);
       compute(tb, it);
       if (++it >= end) break;
     }
@@ -381,7 +414,7 @@ hipError_t launch_score_r8(const void *index, const void *q, const float *qw, fl
   return hipGetLastError();
 }
 
-hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
+hipError_t launch_score_mfma(const void *index, const void *q, const float *qw, float eps, float *scores,
                              float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
                              const ScoreGeom &g, ScoreSplit *split, hipStream_t st) {
   int max_nb = 0;
@@ -407,12 +440,8 @@ hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const
   sp.per = (int)((total + target - 1) / target);
   const int grid = (int)((total + sp.per - 1) / sp.per);
   *split = sp;
-  if (bf16_q)
-    hipLaunchKernelGGL(k_score_mfma<uint16_t>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index,
-                       (const uint16_t *)q, qw, eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
-  else
-    hipLaunchKernelGGL(k_score_mfma<float>, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const float *)q,
-                       qw, eps, scores, part, zero, n_zero, n_blocks, s0, g, sp);
+  hipLaunchKernelGGL(k_score_mfma, dim3(grid), dim3(64), 0, st, (const uint16_t *)index, (const uint16_t *)q, qw, eps,
+                     scores, part, zero, n_zero, n_blocks, s0, g, sp);
   return hipGetLastError();
 }
 

@@ -335,7 +335,7 @@ kvmem_status kvmem_score_select(const kvmem_geom *geom, const kvmem_workspace *w
       const hipError_t e =
           !bf16 ? launch_score_gemv(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs)
           : T * g.G > kGemvMaxRows
-              ? launch_score_mfma(bf16, index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs)
+              ? launch_score_mfma(index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs)
               : launch_score_r8(index, q, q_norm_w, eps, scores, part, zero, n_zero, nb, s0, n, g, &split, hs);
       if ((st = hip_status(e)) != KVMEM_OK) return st;
       uint32_t *skey = (uint32_t *)(base + sc.skey);

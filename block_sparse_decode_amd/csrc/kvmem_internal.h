@@ -82,7 +82,7 @@ constexpr int kGemvMaxRows = 8;
 hipError_t launch_score_r8(const void *index, const void *q, const float *qw, float eps, float *scores, float2 *part,
                           uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess, const ScoreGeom &g,
                           ScoreSplit *split, hipStream_t st);
-hipError_t launch_score_mfma(int bf16_q, const void *index, const void *q, const float *qw, float eps, float *scores,
+hipError_t launch_score_mfma(const void *index, const void *q, const float *qw, float eps, float *scores,
                              float2 *part, uint32_t *zero, int n_zero, const SessI32 &n_blocks, int s0, int n_sess,
                              const ScoreGeom &g, ScoreSplit *split, hipStream_t st);
 
