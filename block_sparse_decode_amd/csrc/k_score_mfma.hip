@@ -83,10 +83,11 @@ __device__ __forceinline__ void load_tile_a_buf(TileA &a, const uint16_t *tile, 
 // computes D[cs][m] = A(blocks 16m..) * B(rows 16cs..): lane (qq, col) holds
 // the scores of blocks 16m + 4qq + i, i < 4, for row 16cs + col.  Running
 // per-lane softmax statistics of its row are merged over the four lanes of a
-// row at the end of each key.  A key's query words and norm weights are
-// requested before its first tile (vector loads return in order, so the
-// operands are built while that tile is in flight), and the next tile is
-// requested before the current one is multiplied (two register buffers).
+// row at the end of each key.  A key's operands are built from its query
+// words before any of its tiles is requested (the words arrive quickly while
+// the memory system is idle, and the registers they held are free again),
+// then its first two tiles go out together, and each tile's registers take
+// the tile after next as soon as its products are done (two tiles in flight).
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_score_mfma(const uint16_t *__restrict__ index, const uint16_t *__restrict__ q,
                                                    const float *__restrict__ qw, float eps,
                                                    float *__restrict__ scores, float2 *__restrict__ part,
@@ -230,26 +231,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
   };
 
-  // One segment per key in the range: the key's query words, then the first
-  // tile's loads go out, the key's operands are built while the tile is in
-  // flight, and the tiles stream with one tile of look-ahead.  After the last
-  // item the look-ahead loads from an empty resource: the loads stay
-  // unconditional (so every wait counts exactly) without touching memory.
+  // One segment per key in the range: the key's operands, then its tiles
+  // with two in flight.  Past the last item the look-ahead loads from an
+  // empty resource: the loads stay unconditional (so every wait counts
+  // exactly) without touching memory.
   for (int it = i0; it < i1;) {
     const ScoreItem c0 = decode_score_item(it, sp, g.Hkv, n_blocks);
     const int end = min(i1, (c0.key + 1) * sp.ntl);
     TileA ta, tb;
     load_key(c0);
-    load_tile_a_buf(ta, tile_of(it), true, lane);
-    __builtin_amdgcn_sched_barrier(0);                  // every load out before the first wait
     build_key();
+    load_tile_a_buf(ta, tile_of(it), true, lane);
+    load_tile_a_buf(tb, tile_of(min(it + 1, end - 1)), it + 1 < end, lane);
     while (true) {
-      load_tile_a_buf(tb, tile_of(min(it + 1, end - 1)), it + 1 < end, lane);
       compute(ta, it);
       if (++it >= end) break;
       load_tile_a_buf(ta, tile_of(min(it + 1, end - 1)), it + 1 < end, lane);
       compute(tb, it);
       if (++it >= end) break;
+      load_tile_a_buf(tb, tile_of(min(it + 1, end - 1)), it + 1 < end, lane);
     }
     flush();
   }
