@@ -362,6 +362,29 @@ def test_long_chunk_shift_far_above_scores():
     _full_check(wl, attend=False)
 
 
+def test_scorer_wavefront_spans_keys():
+    """The matrix-core scorer (9-32 query rows per KV head) with more items
+    than it has wavefronts: 9 sessions x 8 KV heads x 33 index tiles (the
+    longest history is 2,100 blocks) is 2,376 (session, head, tile) items for
+    2,048 wavefronts, two items each, so a wavefront's two items often belong
+    to different (session, head) keys: it builds the operands of a second key,
+    flushes one statistics slot per key, and its look-ahead past a key's last
+    tile reads the empty resource.  Ragged lengths, partial last blocks and
+    partial last tiles; T = 2 (16 rows)."""
+    _need_gpu()
+    lens = (32 * 2100 - 5, 32 * 2050 + 17, 32 * 2003, 32 * 1999 + 1, 32 * 1500, 32 * 2100, 32 * 1800 + 31,
+            32 * 2088, 32 * 2011 + 8)
+    cfg = small_cfg("scorer_spans_keys", "bf16", S=9, Hq=64, Hkv=8, T=2, n_tokens=lens, k=24, R=4, n_planted=6,
+                    seed=81)
+    wl = make_workload(cfg)
+    ntl = -(-max(n // 32 for n in lens) // 64)
+    items = cfg.n_sessions * cfg.n_kv_heads * ntl
+    print(f"[gpu] {items} scorer items over {ntl} tiles per key", flush=True)
+    assert ntl == 33 and items > 2048
+    certify(wl)
+    _full_check(wl, attend=True)
+
+
 def test_c1_parity():
     _need_gpu()
     wl = make_workload(CONFIGS["c1"])
