@@ -777,12 +777,55 @@ __global__ __launch_bounds__(64) void k_mass_combine(const float4 *__restrict__ 
 // Log-sum-exp merge of the split partials of one (session, KV head, query
 // row), one workgroup per quarter of the row's 128 dimensions: 256 threads =
 // 32 split groups x 8 float4 slices of the quarter.  Each thread folds every
-// 32nd split with an online rescale (no separate max and sum passes, four
-// splits in flight), then the 32 groups are folded in a fixed order, so the
-// result is deterministic.
+// 32nd split with an online rescale (no separate max and sum passes, eight
+// splits in flight), then the 32 groups are merged by a fixed tree (three
+// lane exchanges inside each wavefront, then its four wavefronts in LDS), so
+// the result is deterministic.  (Folding the 32 groups in sequence in eight
+// threads took ~5 us longer per call at 1M tokens.)
 // ---------------------------------------------------------------------------
 constexpr int kCombGroups = 32;
 constexpr int kCombQuarters = 4;
+
+// A partial softmax state (running max m, sum l, weighted values a) and the
+// merge of two: symmetric in its operands (both products are formed, then one
+// commutative add), so the two lanes of an exchange get the same bits.
+struct CombState {
+  float m, l;
+  float4 a;
+};
+__device__ __forceinline__ CombState comb_merge(const CombState &x, const CombState &y) {
+  const float M = fmaxf(x.m, y.m);
+  if (M == -INFINITY) return CombState{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  const float fx = exp2f(x.m - M), fy = exp2f(y.m - M);   // exp2(-inf) = 0 for an empty side
+  CombState r;
+  r.m = M;
+  r.l = x.l * fx + y.l * fy;
+  r.a = make_float4(x.a.x * fx + y.a.x * fy, x.a.y * fx + y.a.y * fy, x.a.z * fx + y.a.z * fy,
+                    x.a.w * fx + y.a.w * fy);
+  return r;
+}
+// merge with the state of lane ^ 8 (DPP), ^ 16 or ^ 32 (lane permutes)
+__device__ __forceinline__ CombState comb_xor8(const CombState &v) {
+  CombState o;
+  o.m = dpp_f32<kDppRor8>(v.m);
+  o.l = dpp_f32<kDppRor8>(v.l);
+  o.a = make_float4(dpp_f32<kDppRor8>(v.a.x), dpp_f32<kDppRor8>(v.a.y), dpp_f32<kDppRor8>(v.a.z),
+                    dpp_f32<kDppRor8>(v.a.w));
+  return comb_merge(v, o);
+}
+template <bool X32>
+__device__ __forceinline__ CombState comb_xor_half(const CombState &v) {
+  float p[6] = {v.m, v.l, v.a.x, v.a.y, v.a.z, v.a.w}, q[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const auto r = X32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(p[i]), __float_as_uint(p[i]), false, false)
+                       : __builtin_amdgcn_permlane16_swap(__float_as_uint(p[i]), __float_as_uint(p[i]), false, false);
+    p[i] = __uint_as_float(r[0]);
+    q[i] = __uint_as_float(r[1]);
+  }
+  return comb_merge(CombState{p[0], p[1], make_float4(p[2], p[3], p[4], p[5])},
+                    CombState{q[0], q[1], make_float4(q[2], q[3], q[4], q[5])});
+}
 
 __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict__ part_o,
                                                         const float2 *__restrict__ part_ml, float *__restrict__ out,
@@ -849,27 +892,35 @@ __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict_
     const size_t pidx = base + (size_t)i * g.rows;
     fold(part_ml[pidx], reinterpret_cast<const float4 *>(part_o + pidx * kD)[slice]);
   }
-  acc_s[sg][q4] = acc;
-  if (q4 == 0) {
-    m_s[sg] = m;
-    l_s[sg] = l;
+  // the 32 groups of a slice: a fixed tree, eight groups per wavefront over
+  // the lanes (sg = 8 wave + lane / 8), then the four wavefronts in LDS
+  CombState st{m, l, acc};
+  st = comb_xor8(st);
+  st = comb_xor_half<false>(st);
+  st = comb_xor_half<true>(st);
+  const int wave = tid >> 6;
+  if ((tid & 63) < 8) {
+    acc_s[wave][q4] = st.a;
+    if (q4 == 0) {
+      m_s[wave] = st.m;
+      l_s[wave] = st.l;
+    }
   }
   __syncthreads();
   if (tid < 8) {
-    m = -INFINITY;
-    l = 0.f;
-    acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < kCombGroups; ++j) fold(make_float2(m_s[j], l_s[j]), acc_s[j][tid]);
-    const float inv = 1.0f / l;
-    reinterpret_cast<float4 *>(dst)[tid] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    CombState w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = CombState{m_s[j], l_s[j], acc_s[j][tid]};
+    const CombState r = comb_merge(comb_merge(w[0], w[1]), comb_merge(w[2], w[3]));
+    const float inv = 1.0f / r.l;
+    reinterpret_cast<float4 *>(dst)[tid] = make_float4(r.a.x * inv, r.a.y * inv, r.a.z * inv, r.a.w * inv);
   }
 }
 
 // At most kCombGroups splits per row (short views, or long runs per
 // wavefront): one thread per (query row, float4 slice of the row) folds the
-// row's splits in split order, kNarrowRows rows per workgroup.  The fold
-// order and arithmetic are those of k_attend_combine, whose split groups then
-// hold one split each, so both give the same bits.
+// row's splits in split order with k_attend_combine's online rescale,
+// kNarrowRows rows per workgroup.
 constexpr int kNarrowRows = 8;
 
 __global__ __launch_bounds__(256) void k_attend_combine_narrow(const float *__restrict__ part_o,
