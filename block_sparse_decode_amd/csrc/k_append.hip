@@ -30,6 +30,9 @@ __device__ __forceinline__ void copy8(T *dst, const T *src) {
     reinterpret_cast<uint4 *>(dst)[k] = reinterpret_cast<const uint4 *>(src)[k];
 }
 
+__device__ __forceinline__ float elem_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float elem_f32(float x) { return x; }
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__restrict__ vpool,
                                                 const int32_t *__restrict__ table, const T *__restrict__ knew,
@@ -48,6 +51,19 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
   const int page = table[(size_t)s * max_blocks + beta];
   const bool page_ok = page >= 0 && page < n_pages;
   if (!page_ok && threadIdx.x == 0) dev_flag(dev_err, 1);
+
+  // this thread's first head: its new K and V are requested before the
+  // angles are formed, so the two latencies overlap
+  const int h0 = threadIdx.x >> 3;
+  T v1[8], v2[8], k1[8], k2[8];                        // raw elements (converted when used)
+  auto load_head = [&](int h) {
+    const size_t src = (((size_t)s * T_new + t) * Hkv + h) * kD;
+    Row8<T>::load_raw(vnew + src + 8 * j, v1);
+    Row8<T>::load_raw(vnew + src + 64 + 8 * j, v2);
+    Row8<T>::load_raw(knew + src + 8 * j, k1);
+    Row8<T>::load_raw(knew + src + 64 + 8 * j, k2);
+  };
+  if (h0 < Hkv) load_head(h0);
 
   // the angles of view position vpos = 32 (vpos / 32) + vpos % 32, composed
   // as the gather composes them, once per frequency for every head
@@ -70,11 +86,9 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
 
   const int m = vpos / kBT;
   const int slot = v_slot(vpos % kBT);
-  for (int h = threadIdx.x >> 3; h < Hkv; h += blockDim.x / 8) {
+  for (int h = h0; h < Hkv; h += blockDim.x / 8) {
     const size_t src = (((size_t)s * T_new + t) * Hkv + h) * kD;
-    T v1[8], v2[8];
-    Row8<T>::load_raw(vnew + src + 8 * j, v1);
-    Row8<T>::load_raw(vnew + src + 64 + 8 * j, v2);
+    if (h != h0) load_head(h);
     // history: bit copies at (page, head, token of the block), 16 bytes a time
     if (page_ok) {
       const size_t dst = (((size_t)page * Hkv + h) * kBT + hist % kBT) * kD;
@@ -84,11 +98,9 @@ __global__ __launch_bounds__(256) void k_append(T *__restrict__ kpool, T *__rest
       copy8(vpool + dst + 64 + 8 * j, vnew + src + 64 + 8 * j);
     }
     // view: K rotated at position vpos and rounded; V at its slot
-    float x1[8], x2[8], y1[8], y2[8];
-    Row8<T>::load(knew + src + 8 * j, x1);
-    Row8<T>::load(knew + src + 64 + 8 * j, x2);
+    float y1[8], y2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rope_rotate(x1[e], x2[e], cs[e], sn[e], y1[e], y2[e]);
+    for (int e = 0; e < 8; ++e) rope_rotate(elem_f32(k1[e]), elem_f32(k2[e]), cs[e], sn[e], y1[e], y2[e]);
     T *kd = kview + (((size_t)s * Hkv + h) * max_view + vpos) * kD;
     Row8<T>::store(kd + 8 * j, y1);
     Row8<T>::store(kd + 64 + 8 * j, y2);
