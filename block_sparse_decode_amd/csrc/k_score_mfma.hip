@@ -65,16 +65,18 @@ __device__ __forceinline__ void load_tile_a(TileA &a, const uint16_t *tile, int 
 // address stays in scalar registers (each lane adds only its own offset), and
 // a resource of no records (`valid` false) answers zeros without a memory
 // access, which keeps a look-ahead past the last tile free.
+constexpr int kRawBufferWord3 = 0x00020000;   // resource word 3: 32-bit data format (raw byte offsets)
+constexpr int kNtLoad = 2;                     // cache policy of the loads: non-temporal (streamed once)
 __device__ __forceinline__ void load_tile_a_buf(TileA &a, const uint16_t *tile, bool valid, int lane) {
   const int qq = lane >> 4, col = lane & 15;
   const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void *)tile, (short)0, valid ? kIdxTile * kD * 2 : 0, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void *)tile, (short)0, valid ? kIdxTile * kD * 2 : 0, kRawBufferWord3);
   const int v = (qq * kIdxTile + col) * 16;              // bytes: word qq of block col
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int c = 0; c < 4; ++c)                          // + word 4c (c * 4096 bytes) of block 16m + col
-      a.w[4 * m + c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v + m * 256, c * 4096, 2));
+      a.w[4 * m + c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v + m * 256, c * 4096, kNtLoad));
 }
 
 // Scores of the T * G query rows of a row group against every index row, on
