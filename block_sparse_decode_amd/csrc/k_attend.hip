@@ -787,8 +787,9 @@ constexpr int kCombGroups = 32;
 constexpr int kCombQuarters = 4;
 
 // A partial softmax state (running max m, sum l, weighted values a) and the
-// merge of two: symmetric in its operands (both products are formed, then one
-// commutative add), so the two lanes of an exchange get the same bits.
+// merge of two.  Both lanes of an exchange merge the pair (their results may
+// differ in the last bit with the operands' order); the output takes the
+// states of fixed lanes, so it is the same on every run.
 struct CombState {
   float m, l;
   float4 a;
