@@ -75,6 +75,10 @@ def test_decode_bf16_bits():
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F], np.uint16)
     want = [1.0, -1.0, 3.140625, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127]
     assert list(O.decode(bits, "bf16")) == want
+    # and back: every finite bf16 pattern survives decode -> bf16_bits
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (allbits & 0x7F80) != 0x7F80
+    assert np.array_equal(O.bf16_bits(O.decode(allbits[finite], "bf16")), allbits[finite])
 
 
 # ---------------------------------------------------------------------------
