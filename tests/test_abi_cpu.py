@@ -294,8 +294,8 @@ def test_attend_noalloc_rejects(lib):
     assert call(rope_theta=1.0) == L.KVMEM_E_ARG
     assert call(T=8) == L.KVMEM_E_UNSUPPORTED               # 64 query rows per KV head in bf16
     assert call(geom=_geom(bt=64)) == L.KVMEM_E_UNSUPPORTED
-    # beyond the array: eight sessions of 262,144-token views
-    S, mv = 8, 262144
+    # beyond the array: 32 sessions of 262,144-token views
+    S, mv = 32, 262144
     assert L.kvmem_attend_scratch_bytes(g, S, 1, mv) > L.NOALLOC_SCRATCH_BYTES
     big = np.full(S, mv, np.int32)
     assert call(n_sessions=S, view_tokens_host=big, max_view=mv) == L.KVMEM_E_WORKSPACE
