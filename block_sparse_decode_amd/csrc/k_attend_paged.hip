@@ -13,7 +13,8 @@
 //
 // One workgroup of nw wavefronts per (session, split of the list, group of nw
 // KV heads; nw is the largest divisor of Hkv up to 8); wavefront w serves KV
-// head nw * group + w over the split's list blocks.  Per block:
+// head nw * group + w over the split's list blocks, which are every
+// n_splits-th block of the list starting at the split's index.  Per block:
 //   * the 32 x 64 RoPE (cos, sin) table of the block's view positions is
 //     shared by the heads through LDS (double-buffered, one barrier per
 //     block).  Its angles are composed from the block's 64 base angles
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 
   const int sl = blockIdx.z;
   const int s = s0 + sl;
-  const int split = blockIdx.x;
+  int split = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -87,10 +88,20 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   const int h = blockIdx.y * (int)(blockDim.x >> 6) + wave;   // every wavefront has a head (paged_waves)
   const int nthr = (int)blockDim.x;
   const int V = view_tok.v[sl];
-  const int m0 = split * g.bps;
-  if (kBT * m0 >= V) return;                           // uniform over the workgroup
-  const int m1 = min((V + kBT - 1) / kBT, m0 + g.bps);
   const int n_splits = (V + kBT * g.bps - 1) / (kBT * g.bps);
+  if (split >= n_splits) return;                       // uniform over the workgroup
+  // Workgroups are dealt to the 8 XCDs in turn; this permutation of the splits
+  // gives each XCD's workgroups adjacent splits.
+  if ((n_splits & 7) == 0 && (int)gridDim.x == n_splits) split = (split & 7) * (n_splits >> 3) + (split >> 3);
+  // This workgroup's view blocks: split, split + n_splits, split + 2 n_splits,
+  // ... (at most bps of them), so that the workgroups, which run in step, read
+  // and write one compact window of every head's view at a time.  One-pass
+  // call at 1M tokens: 441 us with a run of bps adjacent blocks per
+  // workgroup, 426 us with the blocks strided, 422 us with the XCD
+  // permutation as well.
+  const int nblk = (V + kBT - 1) / kBT;
+  const int n_my = (nblk - split + n_splits - 1) / n_splits;
+  auto blk = [&](int i) { return split + i * n_splits; };
 
   if (tid < kD / 2) inv_freq[tid] = rope_inv_freq(tid, theta);
   float x[NT][4][8];
@@ -116,32 +127,33 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   }
 
   // The split's pages, resolved once (a split has at most 64 list blocks):
-  // lane l holds the page of list block m0 + l, or -1 for a bad list entry or
+  // lane l holds the page of list block blk(l), or -1 for a bad list entry or
   // page (flagged here; its tile is zeros, as the gather writes zeros for it).
   // Each block then takes its page from a register with readlane instead of a
   // list load and a table load that depend on each other: resolved per block,
   // those two round trips, and a wait for every memory operation before them
   // (the view stores included), stood before each tile's loads.
   int my_page = -1;
-  if (m0 + lane < m1) {
-    const int beta = vblocks[((size_t)s * g.Hkv + h) * g.n_list + m0 + lane];
+  if (lane < n_my) {
+    const int beta = vblocks[((size_t)s * g.Hkv + h) * g.n_list + blk(lane)];
     const bool beta_ok = beta >= 0 && beta < n_all.v[sl];
     const int p = beta_ok ? table[(size_t)s * g.max_blocks + beta] : -1;
     const bool okp = beta_ok && p >= 0 && p < g.n_pages;
     if (!okp) dev_flag(dev_err, beta_ok ? 1 : 2);
     my_page = okp ? p : -1;
   }
-  auto tile_base = [&](int m, bool &ok) -> size_t {
-    const int page = __builtin_amdgcn_readlane(my_page, m - m0);
+  // the tile of the workgroup's i-th block
+  auto tile_base = [&](int i, bool &ok) -> size_t {
+    const int page = __builtin_amdgcn_readlane(my_page, i);
     ok = page >= 0;
     return ((size_t)(ok ? page : 0) * g.Hkv + h) * (size_t)(kBT * kD);
   };
   uint4 kr[2][4], vr[2][4];
   bool ok;
   constexpr bool kKOperandLoads = WV || NT > 1;          // K loaded in the A-operand layout
-  auto load_k = [&](int m) {
+  auto load_k = [&](int i) {
     bool okm;
-    const size_t base = tile_base(m, okm);
+    const size_t base = tile_base(i, okm);
     // Without the view and with one row tile: whole 128-byte lines
     // (load_k_lines; k_lines_operand before use), 190 -> 186 us per call at
     // 1M tokens.  Writing the view, or with two row tiles, the operand layout
@@ -159,18 +171,18 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   };
   // V goes through LDS, so its loads take whole rows: instruction j, lane l
   // reads token 4j + l / 16, dims 8 (l % 16) .. + 7 (full 128-byte lines)
-  auto load_v = [&](int m) {
+  auto load_v = [&](int i) {
     bool okm;
-    const size_t base = tile_base(m, okm);
+    const size_t base = tile_base(i, okm);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       vr[j >> 2][j & 3] = load_nt16(vpool + base + (size_t)(4 * j + (lane >> 4)) * kD + 8 * (lane & 15));
   };
-  auto load_tile = [&](int m) {
-    load_k(m);
-    load_v(m);
+  auto load_tile = [&](int i) {
+    load_k(i);
+    load_v(i);
   };
-  load_tile(m0);
+  load_tile(0);
   __syncthreads();                                     // inv_freq
 
   {
@@ -189,7 +201,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
 #pragma unroll 1
       for (int k = 0; k < 2; ++k) {
         double c, sn;
-        rope_angle_f64((double)(kBT * (m0 + k)), inv_freq[tid], c, sn);
+        rope_angle_f64((double)(kBT * blk(k)), inv_freq[tid], c, sn);
         base_cs[k][tid] = make_double2(c, sn);
       }
     }
@@ -210,8 +222,9 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
   }
   uint16_t *myv = vt[wave];
 
-  for (int m = m0; m < m1; ++m) {
-    const int buf = (m - m0) & 1;
+  for (int i = 0; i < n_my; ++i) {
+    const int m = blk(i);
+    const int buf = i & 1;
 #pragma unroll 1
     for (int idx = tid; idx < kBT * (kD / 2); idx += nthr) {
       const int u = idx / (kD / 2), i = idx % (kD / 2);
@@ -226,7 +239,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
     // compiles to exec-masked branches, after which the compiler no longer
     // knows the tile's loads have landed and waits for the view stores too)
     const int tb = kBT * m;
-    (void)tile_base(m, ok);
+    (void)tile_base(i, ok);
     uint32_t keep[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) keep[tt] = ok && tb + 16 * tt + col < V ? 0xffffffffu : 0u;
@@ -239,7 +252,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
     // the next V tile leaves as soon as this one is staged: it flies through
     // the barrier, the rotation and both products (at 1M tokens 471 -> 458 us
     // with the view written, 258 -> 225 us without)
-    if (m + 1 < m1) load_v(m + 1);
+    if (i + 1 < n_my) load_v(i + 1);
     __syncthreads();
 
     // K rotated at view positions 32m + u and rounded to bf16: A operands
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
     // registers; without the view, once the score products have consumed the
     // rotated operands (225 -> 204 us at 1M tokens).  Any order that puts
     // this tile's K view stores behind the next loads spills ~40 registers.
-    if (WV && m + 1 < m1) load_k(m + 1);
+    if (WV && i + 1 < n_my) load_k(i + 1);
 
     floatx4 scs[NT][2];
 #pragma unroll
@@ -327,7 +340,7 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
         }
         scs[nt][tt] = a;
       }
-    if (!WV && m + 1 < m1) load_k(m + 1);
+    if (!WV && i + 1 < n_my) load_k(i + 1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       floatx4 sc[2] = {scs[nt][0], scs[nt][1]};
@@ -384,10 +397,10 @@ __global__ __launch_bounds__(512) void k_attend_paged_bf16(
         o[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, o[nt][dt], 0, 0, 0);
       }
     }
-    // the base angles of block m + 2 into the buffer this block's table came
-    // from (every wavefront passed this block's barrier, so it is read out;
-    // block m + 1's barrier orders the write before block m + 2 reads it)
-    if (tid < kD / 2 && m + 2 < m1) base_cs[buf][tid] = block_angle((double)(kBT * (m + 2)), inv_freq[tid]);
+    // the base angles of block blk(i + 2) into the buffer this block's table
+    // came from (every wavefront passed this block's barrier, so it is read
+    // out; block i + 1's barrier orders the write before block i + 2 reads it)
+    if (tid < kD / 2 && i + 2 < n_my) base_cs[buf][tid] = block_angle((double)(kBT * blk(i + 2)), inv_freq[tid]);
   }
 
   // the wavefront alone holds its head's rows: partials (or the output)
