@@ -50,9 +50,9 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
 # taken on (sha256 over block_sparse_decode_amd/csrc/* and build.py); otherwise reported null.
-COUNTER_SOURCES_SHA = "06a8aea8f805a882933c85dbb16f59cd9821c1c4bfb3379282e358a936d38e34"
-MEASURED_TRAFFIC = {"build_index_full": 2.216e+09, "materialize_attend": 2.173e+09, "materialize": 2.156e+09,
-                    "attend": 1.083e+09, "score_select": 9.208e+07}
+COUNTER_SOURCES_SHA = "171a842db895039613d65158f66a8e26e6e8c79b70971fe3fa225d63e4c46ffd"
+MEASURED_TRAFFIC = {"build_index_full": 2.216e+09, "materialize_attend": 2.172e+09, "materialize": 2.156e+09,
+                    "attend": 1.076e+09, "score_select": 9.208e+07}
 
 
 def kernel_sources_sha() -> str:
