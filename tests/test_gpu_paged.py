@@ -42,6 +42,12 @@ CASES["five_heads"] = small_cfg("paged_five_heads", "bf16", S=2, Hq=10, Hkv=5, n
                                 k=14, R=3, n_planted=3, seed=113)
 CASES["twelve_heads"] = small_cfg("paged_twelve_heads", "bf16", S=1, Hq=48, Hkv=12, n_tokens=(32 * 120 + 1,),
                                   k=16, R=2, n_planted=3, seed=114)
+# two list blocks per split, strided over the view (workgroup j: blocks j,
+# j + n_splits, ...): session 0 has 96 splits, which the kernel permutes across
+# XCDs (96 = the launch's width, a multiple of 8), session 1 has 75 (no
+# permutation) and takes every candidate (budget above its history)
+CASES["strided_splits"] = small_cfg("paged_strided", "bf16", S=2, Hq=64, Hkv=8, n_tokens=(32 * 400 + 5, 32 * 150),
+                                    k=188, R=4, n_planted=6, seed=115)
 
 
 def _run(wl, heads=None):
