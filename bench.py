@@ -195,12 +195,14 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
     decode steps of (attention of one query token over the view, append of
     that token's K/V to the history and the view, Mean-K row of each block the
     history completes).  Timed per step with HIP events on the library's
-    stream, after the view is built: the first half of the tokens with events
-    before the attention, between it and the append, and after the append
-    (the attention / append breakdown), the second half with one event per
-    step only (each recorded event leaves the GPU idle for a few µs between
-    the kernels it separates, so the step latency comes from this half: one
-    event per interval, as in the main step loop)."""
+    stream, after the view is built, in thirds: the first with events before
+    the attention, between it and the append, and after the append (the
+    attention / append breakdown); the second with the two calls and one event
+    per step; the last with kvmem_attend_append (the attention, then the
+    append on the attention's merge launch) and one event per step, the
+    reported step latency.  (Each recorded event leaves the GPU idle for a few
+    µs between the kernels it separates, so the step latencies take one event
+    per interval, as the main step loop does.)"""
     import torch
 
     from block_sparse_decode_amd.pipeline import DeviceWorkspace, to_device
@@ -222,9 +224,13 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
     ev[1].record(stream)
     dw.materialize(stream)
     ev[2].record(stream)
-    n_br = n_dec // 2 if n_dec >= 2 else n_dec        # tokens timed with the breakdown
+    # thirds: the breakdown (two calls, events between them); two calls with
+    # one event per step; the fused call (kvmem_attend_append) with one event
+    # per step
+    n_two = n_dec // 3
+    n_br = n_dec - 2 * n_two
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_br)]
-    sev = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec - n_br + 1)]
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_two + 2)]
     for t in range(n_dec):
         if t < n_br:
             evs[t][0].record(stream)
@@ -232,17 +238,23 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
             evs[t][1].record(stream)
             dw.append(*toks[t], stream=stream)
             evs[t][2].record(stream)
-        else:
+        elif t < n_br + n_two:
             sev[t - n_br].record(stream)
             dw.attend(stream)
             dw.append(*toks[t], stream=stream)
+        else:
+            if t == n_br + n_two:
+                sev[n_two].record(stream)             # end of the two-call third
+            sev[t - n_br + 1].record(stream)
+            dw.attend_append(*toks[t], stream=stream)
     sev[-1].record(stream)
     torch.cuda.synchronize()
     att = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
     app_all = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
     step_marked = att + app_all
-    step_us = np.array([sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(n_dec - n_br)]) if n_dec > n_br \
-        else step_marked
+    step_two = np.array([sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(n_two)]) if n_two else step_marked
+    step_us = np.array([sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(n_two + 1, 2 * n_two + 1)]) \
+        if n_two else step_marked
     recall = ev[0].elapsed_time(ev[2]) * 1e3
     # steps at which some session's history completes a block (index rows added)
     blocks_done = [t for t in range(n_br) if any((int(n) + t + 1) % 32 == 0 for n in wl.n_tokens)]
@@ -250,6 +262,7 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
     app = app_all
     return {"tokens": n_dec, "view_tokens_start": int(np.sum(V_start)),
             "step_us_median": round(float(np.median(step_us)), 2),
+            "step_us_median_two_calls": round(float(np.median(step_two)), 2),
             "step_us_median_three_events": round(float(np.median(step_marked)), 2),
             "attend_us_median": round(float(np.median(att)), 2),
             "append_us_median": round(float(np.median(app[plain])), 2),
@@ -257,8 +270,7 @@ def decode_loop(wl, dev, stream, n_dec: int) -> dict:
             "attend_hbm_frac": round(2 * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
                                      * int(np.sum(V_start)) / (np.median(att) * 1e-6) / HBM_PEAK, 4),
             "recall_us": round(recall, 2),
-            "tokens_per_s_view_reused": round(n_dec / ((recall + step_marked.sum() + (step_us.sum() if n_dec > n_br else 0.0))
-                                                       * 1e-6), 1),
+            "tokens_per_s_view_reused": round(n_dec / ((recall + float(np.median(step_us)) * n_dec) * 1e-6), 1),
             "tokens_per_s_reselect_each_token": round(1.0 / ((recall + float(np.median(att))) * 1e-6), 1)}
 
 

@@ -32,6 +32,7 @@ EXPORTED = [
     "kvmem_attend_noalloc",
     "kvmem_update_index",
     "kvmem_append",
+    "kvmem_attend_append",
     "kvmem_attend_paged_scratch_bytes",
     "kvmem_attend_paged",
     "kvmem_materialize_attend",
@@ -109,6 +110,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvmem_append.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                  c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p]
     lib.kvmem_append.restype = c_int32
+    lib.kvmem_attend_append.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
+                                        c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
+    lib.kvmem_attend_append.restype = c_int32
     lib.kvmem_attend_paged_scratch_bytes.argtypes = [POINTER(Geom), c_int32, c_int32, c_int32]
     lib.kvmem_attend_paged_scratch_bytes.restype = c_size_t
     lib.kvmem_attend_paged.argtypes = [POINTER(Geom), POINTER(Workspace), c_void_p, c_int32, c_void_p, c_float,
@@ -279,6 +284,22 @@ def kvmem_append(geom: Geom, ws: Workspace, k_pool, v_pool, k_new, v_new, T_new:
                              _stream(stream))
     if check:
         _check(st, "kvmem_append")
+    return st
+
+
+def kvmem_attend_append(geom: Geom, ws: Workspace, q, T: int, q_norm_w, eps: float, k_view, v_view,
+                        view_tokens_host: np.ndarray, max_view: int, rope_theta: float, out, k_pool, v_pool, k_new,
+                        v_new, T_new: int, scratch=None, scratch_bytes: int | None = None, stream=None,
+                        check: bool = True) -> int:
+    assert view_tokens_host.dtype == np.int32
+    if scratch_bytes is None:
+        scratch_bytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    st = load().kvmem_attend_append(ctypes.byref(geom), ctypes.byref(ws), _p(q), T, _p(q_norm_w), eps, _p(k_view),
+                                    _p(v_view), _p(view_tokens_host), max_view, rope_theta, _p(out), _p(k_pool),
+                                    _p(v_pool), _p(k_new), _p(v_new), T_new, _p(scratch), scratch_bytes,
+                                    _stream(stream))
+    if check:
+        _check(st, "kvmem_attend_append")
     return st
 
 

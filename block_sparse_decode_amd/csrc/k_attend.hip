@@ -26,6 +26,9 @@
 //
 // fp32 path (k_attend_f32): a plain vector-ALU kernel with the same split and
 // merge structure (logits and probabilities staged in LDS).
+#include <string.h>
+
+#include "append_common.h"
 #include "attend_common.h"
 
 namespace kvmem {
@@ -832,11 +835,30 @@ __device__ __forceinline__ CombState comb_xor_half(const CombState &v) {
                     CombState{q[0], q[1], make_float4(q[2], q[3], q[4], q[5])});
 }
 
+// One appended token of session s0 + sl, run by a workgroup of a merge launch.
+__device__ __forceinline__ void append_in_merge(const AppendArgs &ap, const SessI32 &view_tok, int s0, int sl, int t) {
+  __shared__ float2 cs_tok[kD / 2];
+  if (ap.bf16)
+    append_token<uint16_t>((uint16_t *)ap.kpool, (uint16_t *)ap.vpool, ap.table, (const uint16_t *)ap.knew,
+                           (const uint16_t *)ap.vnew, ap.T_new, (uint16_t *)ap.kview, (uint16_t *)ap.vview,
+                           ap.dev_err, ap.n_tok.v[sl], view_tok.v[sl], s0 + sl, t, ap.Hkv, ap.max_blocks, ap.n_pages,
+                           ap.max_view, ap.theta, cs_tok);
+  else
+    append_token<float>((float *)ap.kpool, (float *)ap.vpool, ap.table, (const float *)ap.knew,
+                        (const float *)ap.vnew, ap.T_new, (float *)ap.kview, (float *)ap.vview, ap.dev_err,
+                        ap.n_tok.v[sl], view_tok.v[sl], s0 + sl, t, ap.Hkv, ap.max_blocks, ap.n_pages, ap.max_view, ap.theta,
+                        cs_tok);
+}
+
 __global__ __launch_bounds__(256) void k_attend_combine(const float *__restrict__ part_o,
                                                         const float2 *__restrict__ part_ml, float *__restrict__ out,
-                                                        SessI32 view_tok, int s0, AttendGeom g) {
+                                                        SessI32 view_tok, int s0, AttendGeom g, AppendArgs ap) {
   __shared__ float4 acc_s[kCombGroups][8];
   __shared__ float m_s[kCombGroups], l_s[kCombGroups];
+  if (ap.T_new > 0 && (int)blockIdx.x >= (int)gridDim.x - ap.T_new) {
+    if (blockIdx.y == 0) append_in_merge(ap, view_tok, s0, (int)blockIdx.z, (int)blockIdx.x - ((int)gridDim.x - ap.T_new));
+    return;
+  }
   const int sl = blockIdx.z;
   const int s = s0 + sl;
   const int h = blockIdx.y;
@@ -931,7 +953,11 @@ constexpr int kNarrowRows = 8;
 __global__ __launch_bounds__(256) void k_attend_combine_narrow(const float *__restrict__ part_o,
                                                                const float2 *__restrict__ part_ml,
                                                                float *__restrict__ out, SessI32 view_tok, int s0,
-                                                               AttendGeom g) {
+                                                               AttendGeom g, AppendArgs ap) {
+  if (ap.T_new > 0 && (int)blockIdx.x >= (int)gridDim.x - ap.T_new) {
+    if (blockIdx.y == 0) append_in_merge(ap, view_tok, s0, (int)blockIdx.z, (int)blockIdx.x - ((int)gridDim.x - ap.T_new));
+    return;
+  }
   const int sl = blockIdx.z;
   const int s = s0 + sl;
   const int h = blockIdx.y;
@@ -998,7 +1024,7 @@ int attend_max_splits(int max_view, int tpw) { return (max_view + 4 * tpw - 1) /
 hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
                          const void *v_view, float *part_o, float2 *part_ml, float *out,
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
-                         hipStream_t st) {
+                         hipStream_t st, const AppendArgs *ap) {
   int max_v = 0;
   for (int i = 0; i < n_sess; ++i) max_v = view_tok.v[i] > max_v ? view_tok.v[i] : max_v;
   const int splits = max_v > 0 ? (max_v + 4 * g.tpw - 1) / (4 * g.tpw) : 0;
@@ -1019,20 +1045,24 @@ hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_attend_combine(part_o, part_ml, out, view_tok, s0, n_sess, g, st);
+  return launch_attend_combine(part_o, part_ml, out, view_tok, s0, n_sess, g, st, ap);
 }
 
 hipError_t launch_attend_combine(const float *part_o, const float2 *part_ml, float *out, const SessI32 &view_tok,
-                                 int s0, int n_sess, const AttendGeom &g, hipStream_t st) {
+                                 int s0, int n_sess, const AttendGeom &g, hipStream_t st, const AppendArgs *ap) {
+  AppendArgs none;
+  memset(&none, 0, sizeof(none));
+  const AppendArgs &a = ap != nullptr ? *ap : none;
+  const unsigned extra = a.T_new > 0 ? (unsigned)a.T_new : 0u;   // append workgroups at the end of x
   int max_v = 0;
   for (int i = 0; i < n_sess; ++i) max_v = view_tok.v[i] > max_v ? view_tok.v[i] : max_v;
   const int n_max = (max_v + 4 * g.tpw - 1) / (4 * g.tpw);
   if (n_max <= kCombGroups) {
-    dim3 cgrid((unsigned)((g.rows + kNarrowRows - 1) / kNarrowRows), (unsigned)g.Hkv, (unsigned)n_sess);
-    hipLaunchKernelGGL(k_attend_combine_narrow, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
+    dim3 cgrid((unsigned)((g.rows + kNarrowRows - 1) / kNarrowRows) + extra, (unsigned)g.Hkv, (unsigned)n_sess);
+    hipLaunchKernelGGL(k_attend_combine_narrow, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g, a);
   } else {
-    dim3 cgrid((unsigned)(g.rows * kCombQuarters), (unsigned)g.Hkv, (unsigned)n_sess);
-    hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g);
+    dim3 cgrid((unsigned)(g.rows * kCombQuarters) + extra, (unsigned)g.Hkv, (unsigned)n_sess);
+    hipLaunchKernelGGL(k_attend_combine, cgrid, dim3(256), 0, st, part_o, part_ml, out, view_tok, s0, g, a);
   }
   return hipGetLastError();
 }

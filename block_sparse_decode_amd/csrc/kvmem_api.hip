@@ -594,7 +594,8 @@ static kvmem_status attend_check(const kvmem_geom *geom, int32_t n_sessions, con
 static kvmem_status attend_launch(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,
                                   const float *q_norm_w, float eps, const void *k_view, const void *v_view,
                                   const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
-                                  const AttendScratch &sc, char *base, void *stream) {
+                                  const AttendScratch &sc, char *base, void *stream,
+                                  AppendArgs *ap = nullptr, const int32_t *n_tokens_host = nullptr) {
   const int bf16 = geom->kv_dtype == KVMEM_BF16;
   AttendGeom g;
   g.Tq = T;
@@ -610,9 +611,13 @@ static kvmem_status attend_launch(const kvmem_geom *geom, int32_t n_sessions, co
     SessI32 vt;
     memset(&vt, 0, sizeof(vt));
     for (int i = 0; i < n; ++i) vt.v[i] = view_tokens_host[s0 + i];
+    if (ap != nullptr) {
+      memset(&ap->n_tok, 0, sizeof(ap->n_tok));
+      for (int i = 0; i < n; ++i) ap->n_tok.v[i] = n_tokens_host[s0 + i];
+    }
     const kvmem_status st = hip_status(launch_attend(bf16, q, q_norm_w, eps, k_view, v_view,
                                                      (float *)(base + sc.part_o), (float2 *)(base + sc.part_ml),
-                                                     out, vt, s0, n, g, (double)rope_theta, (hipStream_t)stream));
+                                                     out, vt, s0, n, g, (double)rope_theta, (hipStream_t)stream, ap));
     if (st != KVMEM_OK) return st;
   }
   return KVMEM_OK;
@@ -629,6 +634,46 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions, const void
   if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
   return attend_launch(geom, n_sessions, q, T, q_norm_w, eps, k_view, v_view, view_tokens_host, max_view,
                        rope_theta, out, sc, (char *)scratch, stream);
+}
+
+kvmem_status kvmem_attend_append(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
+                                 const float *q_norm_w, float eps, void *k_view, void *v_view,
+                                 const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
+                                 void *k_pool, void *v_pool, const void *k_new, const void *v_new, int32_t T_new,
+                                 void *scratch, size_t scratch_bytes, void *stream) {
+  if (!ws) return KVMEM_E_ARG;
+  AttendScratch sc;
+  kvmem_status st = attend_check(geom, ws->n_sessions, q, T, q_norm_w, eps, k_view, v_view, view_tokens_host,
+                                 max_view, rope_theta, out, &sc);
+  if (st != KVMEM_OK) return st;
+  // the checks of kvmem_append
+  if ((st = check_ws(ws, true)) != KVMEM_OK) return st;
+  if (!k_pool || !v_pool || k_pool != ws->k_pool || v_pool != ws->v_pool) return KVMEM_E_ARG;
+  if (!k_new || !v_new || T_new < 0) return KVMEM_E_ARG;
+  for (int s = 0; s < ws->n_sessions; ++s) {
+    if ((long)ws->n_tokens_host[s] + T_new > (long)ws->max_blocks * kBT) return KVMEM_E_ARG;
+    if ((long)view_tokens_host[s] + T_new > max_view) return KVMEM_E_ARG;
+  }
+  if (!scratch || scratch_bytes < sc.total) return KVMEM_E_WORKSPACE;
+  AppendArgs ap;
+  memset(&ap, 0, sizeof(ap));
+  ap.kpool = k_pool;
+  ap.vpool = v_pool;
+  ap.table = ws->block_table;
+  ap.knew = k_new;
+  ap.vnew = v_new;
+  ap.kview = k_view;
+  ap.vview = v_view;
+  ap.dev_err = ws->dev_error;
+  ap.T_new = T_new;
+  ap.Hkv = geom->n_kv_heads;
+  ap.max_blocks = ws->max_blocks;
+  ap.n_pages = ws->n_pages;
+  ap.max_view = max_view;
+  ap.bf16 = geom->kv_dtype == KVMEM_BF16;
+  ap.theta = (double)rope_theta;
+  return attend_launch(geom, ws->n_sessions, q, T, q_norm_w, eps, k_view, v_view, view_tokens_host, max_view,
+                       rope_theta, out, sc, (char *)scratch, stream, &ap, ws->n_tokens_host);
 }
 
 kvmem_status kvmem_attend_noalloc(const kvmem_geom *geom, int32_t n_sessions, const void *q, int32_t T,

@@ -153,14 +153,32 @@ struct AttendGeom {
 int attend_tokens_per_wave(int n_sessions, int Hkv, int max_view, int rows);
 int attend_max_splits(int max_view, int tpw);
 
+// New tokens appended by the merge launch of an attention (kvmem_attend_append):
+// T_new extra workgroups per session, each running the append of one token
+// (the k_append routine) while the other workgroups merge the splits.  The
+// merge runs after the attention kernel on the same stream, so the tokens'
+// view slots are written after every read of the view.  T_new = 0: none.
+struct AppendArgs {
+  void *kpool, *vpool;
+  const int32_t *table;
+  const void *knew, *vnew;
+  void *kview, *vview;
+  int32_t *dev_err;
+  SessI32 n_tok;                  // history lengths before the append
+  int T_new, Hkv, max_blocks, n_pages, max_view, bf16;
+  double theta;
+};
+
 hipError_t launch_attend(int bf16, const void *q, const float *qw, float eps, const void *k_view,
                          const void *v_view, float *part_o, float2 *part_ml, float *out,
                          const SessI32 &view_tok, int s0, int n_sess, const AttendGeom &g, double theta,
-                         hipStream_t st);
+                         hipStream_t st, const AppendArgs *ap = nullptr);
 
-// Merge of split partials (layout of the view attention) into out.
+// Merge of split partials (layout of the view attention) into out; with ap,
+// also the append of ap->T_new tokens per session (view lengths view_tok).
 hipError_t launch_attend_combine(const float *part_o, const float2 *part_ml, float *out, const SessI32 &view_tok,
-                                 int s0, int n_sess, const AttendGeom &g, hipStream_t st);
+                                 int s0, int n_sess, const AttendGeom &g, hipStream_t st,
+                                 const AppendArgs *ap = nullptr);
 
 // --- attention straight from the pages ------------------------------------------
 // query rows per KV head of the fp32 kernels (attention from the pages, the

@@ -159,6 +159,20 @@ class DeviceWorkspace:
         if np.any(self.n_tokens // BLOCK > first):
             L.kvmem_update_index(self.geom, self.ws, first, self.index, stream)
 
+    def attend_append(self, k_new, v_new, stream=None):
+        """One decode token in one call: the attention over the current view
+        (into self.out), then the append of k_new / v_new as append() does
+        (the append rides on the attention's merge launch)."""
+        T_new = int(k_new.shape[1])
+        L.kvmem_attend_append(self.geom, self.ws, self.q, self.T, self.q_norm_w, self.eps, self.k_view, self.v_view,
+                              self.view_tokens, self.max_view, self.theta, self.out, self.k_pool, self.v_pool, k_new,
+                              v_new, T_new, scratch=self.attend_scratch, stream=stream)
+        first = (self.n_tokens // BLOCK).astype(np.int32)
+        self.n_tokens += T_new
+        self.view_tokens += T_new
+        if np.any(self.n_tokens // BLOCK > first):
+            L.kvmem_update_index(self.geom, self.ws, first, self.index, stream)
+
     # --- attention straight from the pages ----------------------------------
     def attend_paged(self, out=None, stream=None):
         """The attention of kvmem_attend over the current lists, read from the

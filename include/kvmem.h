@@ -428,6 +428,31 @@ kvmem_status kvmem_append(const kvmem_geom *geom, const kvmem_workspace *ws,
                           const int32_t *view_tokens_host, int32_t max_view,
                           float rope_theta, void *k_view, void *v_view, void *stream);
 
+/* -------------------------------------------------------------------------
+ * kvmem_attend_append: one decode token over a reused view in one call --
+ * kvmem_attend over the current view (lengths view_tokens_host, BEFORE the
+ * append), then kvmem_append of the step's new tokens, with exactly the
+ * results of those two calls made in that order ([REVIEW 'Scope & Claims']:
+ * the view serves every decode token of a step; [README 'Core equation']:
+ * attention over the bounded view).  The append runs as extra workgroups of
+ * the attention's split-merge launch, which follows the attention kernel on
+ * the stream, so the appended view slots are written after every read of the
+ * view and the append costs no launch of its own.
+ *
+ * n_sessions is ws->n_sessions.  q, T, q_norm_w, eps, k_view, v_view,
+ * max_view, rope_theta, out, scratch, scratch_bytes: as for kvmem_attend
+ * (scratch sized by kvmem_attend_scratch_bytes).  k_pool, v_pool, k_new,
+ * v_new, T_new: as for kvmem_append.  Every check of both calls is made
+ * before anything is enqueued.  As with kvmem_append, the caller then
+ * advances n_tokens_host[s] and view_tokens_host[s] by T_new and indexes the
+ * blocks the append completed (kvmem_update_index).
+ * ------------------------------------------------------------------------- */
+kvmem_status kvmem_attend_append(const kvmem_geom *geom, const kvmem_workspace *ws, const void *q, int32_t T,
+                                 const float *q_norm_w, float eps, void *k_view, void *v_view,
+                                 const int32_t *view_tokens_host, int32_t max_view, float rope_theta, float *out,
+                                 void *k_pool, void *v_pool, const void *k_new, const void *v_new, int32_t T_new,
+                                 void *scratch, size_t scratch_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Selection-quality diagnostic ([REVIEW 'Strengths']: a few top blocks carry
  * most of the attention mass, which motivates block selection; [README 'Local

@@ -322,3 +322,28 @@ def test_stage_view_rejects(lib):
     assert call(ws=ws_nov) == L.KVMEM_E_ARG                # V pool needed
     ws2, n2 = _ws(n_tok=(100, 64 * 32 + 1))                  # longer than the table
     assert call(ws=ws2) == L.KVMEM_E_ARG
+
+
+def test_attend_append_rejects(lib):
+    """The decode call (attention, then the append on the merge launch) makes
+    every check of kvmem_attend and of kvmem_append before enqueuing."""
+    ws, n = _ws(n_tok=(100, 1000))
+    g = _geom()
+    vt = np.array([64, 96], np.int32)
+    need = L.kvmem_attend_scratch_bytes(g, 2, 1, 128)
+    call = lambda **kw: L.kvmem_attend_append(**{**dict(
+        geom=g, ws=ws, q=0x10, T=1, q_norm_w=0x20, eps=1e-6, k_view=0x30, v_view=0x40, view_tokens_host=vt,
+        max_view=128, rope_theta=1e6, out=0x50, k_pool=0x1000, v_pool=0x2000, k_new=0x60, v_new=0x70, T_new=1,
+        scratch=0x80, scratch_bytes=need, check=False), **kw})
+    assert call(T=0) == L.KVMEM_E_ARG
+    assert call(out=None) == L.KVMEM_E_ARG
+    assert call(k_new=None) == L.KVMEM_E_ARG
+    assert call(T_new=-1) == L.KVMEM_E_ARG
+    assert call(k_pool=0x1001) == L.KVMEM_E_ARG                   # not the workspace's pool
+    assert call(T_new=33) == L.KVMEM_E_ARG                        # session 1's view would pass max_view
+    assert call(T_new=64 * 32 - 1000 + 1, max_view=2048) == L.KVMEM_E_ARG   # session 1's history would pass the table
+    assert call(T_new=64 * 32 - 1000, max_view=2048) == L.KVMEM_E_WORKSPACE  # fits; the scratch was sized for 128
+    ws_nov = L.Workspace(0x1000, None, 0x3000, n.ctypes.data, 2, 64, 70, None)
+    assert call(ws=ws_nov, v_pool=None) == L.KVMEM_E_ARG          # V pool needed
+    assert call(scratch_bytes=need - 1) == L.KVMEM_E_WORKSPACE
+    assert call(T=8) == L.KVMEM_E_UNSUPPORTED                     # 64 query rows per KV head in bf16

@@ -111,3 +111,50 @@ def test_append_parity(name):
                 assert err <= ATT_TOL[cfg.dtype], (name, step, s, h, "attend", err)
                 assert err <= reg_bar(o_ref), (name, step, s, h, "attend regression bar", err, reg_bar(o_ref))
     assert int(dw.dev_error.item()) == 0
+
+
+# kvmem_attend_append against kvmem_attend + kvmem_append: the same kernels'
+# results, so every output, pool, view and index word must match bit for bit.
+# The wide case has 51 splits, so its append rides on the merge that folds
+# split groups (the small ones on the narrow merge).
+FUSED = dict(CASES)
+FUSED["bf16_wide"] = small_cfg("dec_bf16_wide", "bf16", S=1, Hq=8, Hkv=1, n_tokens=(32 * 600 + 7,),
+                               k=200, R=4, n_planted=6, seed=83)
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_attend_append_matches_two_calls(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_decode_amd.pipeline import DeviceWorkspace, to_device
+    cfg = FUSED[name]
+    extra = sum(STEPS)
+    wl = with_decode_capacity(make_workload(cfg), extra)
+    V0 = [O.view_tokens(int(n), cfg.k_select, cfg.n_recent) for n in wl.n_tokens]
+    max_view = -(-(max(V0) + extra) // 32) * 32
+    print(f"[gpu] attend_append {name} N={list(wl.n_tokens)} V={V0} steps={STEPS}", flush=True)
+    two, one = DeviceWorkspace(wl, "cuda", max_view=max_view), DeviceWorkspace(wl, "cuda", max_view=max_view)
+    for dw in (two, one):
+        # equal starting contents everywhere the comparison looks (the views
+        # and the index are allocated uninitialised past what the calls write)
+        for buf in (dw.k_view, dw.v_view, dw.index):
+            buf.zero_()
+        dw.build_index()
+        dw.score_select()
+        dw.materialize()
+    torch.cuda.synchronize()
+    for step, T_new in enumerate(STEPS):
+        kn, vn = draw_decode_tokens(cfg, step, T_new)
+        kd, vd = to_device(kn, cfg.dtype, "cuda"), to_device(vn, cfg.dtype, "cuda")
+        two.attend()
+        two.append(kd, vd)
+        one.attend_append(kd, vd)
+        torch.cuda.synchronize()
+        assert int(one.dev_error.item()) == 0
+        assert np.array_equal(one.n_tokens, two.n_tokens) and np.array_equal(one.view_tokens, two.view_tokens)
+        for what in ("out", "k_pool", "v_pool", "k_view", "v_view", "index"):
+            a, b = getattr(one, what), getattr(two, what)
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a.view(torch.int32),
+                               b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32)), \
+                (name, step, what)
+    print(f"[gpu] attend_append {name}: outputs, pools, views and index bit-identical to attend + append", flush=True)
