@@ -320,7 +320,7 @@ kvmem_status kvmem_attend(const kvmem_geom *geom, int32_t n_sessions,
  * Its scratch is the library's own device array of
  * KVMEM_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends.  A
  * call that needs more (kvmem_attend_scratch_bytes() above the constant, e.g.
- * more than four sessions of 262,144-token views at 64 query / 8 KV heads)
+ * more than fifteen sessions of 262,144-token views at 64 query / 8 KV heads)
  * returns KVMEM_E_WORKSPACE and enqueues nothing.  The call runs on the
  * current device (stream must belong to it).  The array's device address is
  * looked up once per device, on the first call made with that device
