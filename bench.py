@@ -50,7 +50,7 @@ MFMA_BF16_PEAK = 2.5e15   # flop/s, MI355X dense bf16 matrix cores
 # copy (fetch x2.0, write x1.0); the summary and commands are in
 # profiles/c3_1m_hbm_traffic.md.  Valid only for the kernel sources they were
 # taken on (sha256 over block_sparse_decode_amd/csrc/* and build.py); otherwise reported null.
-COUNTER_SOURCES_SHA = "171a842db895039613d65158f66a8e26e6e8c79b70971fe3fa225d63e4c46ffd"
+COUNTER_SOURCES_SHA = "0e7508d320a8fd8f53c0be728ecb56e0648b56baba751384cdcf3797966dc3cd"
 MEASURED_TRAFFIC = {"build_index_full": 2.216e+09, "materialize_attend": 2.172e+09, "materialize": 2.156e+09,
                     "attend": 1.076e+09, "score_select": 9.208e+07}
 
